@@ -1,0 +1,17 @@
+"""Selected-KV paged decode attention on MI355X (gfx950): Python binding.
+
+Thin ctypes wrappers over libkap.so (include/kap.h) with the same names as the
+C entry points.  They only marshal arguments: every step of the path runs in
+the library's HIP kernels.  PyTorch supplies device memory and the current
+stream.  If libkap.so has not been built the first call raises
+KapLibraryMissing -- there is no fallback of any kind.
+
+Tensor conventions: bf16 data may be torch.bfloat16 or 16-bit integer tensors
+holding bf16 bit patterns; fp32 data are torch.float32; index tensors int32
+(slot mapping int64).  All tensors must be contiguous and on the same GPU.
+"""
+from ._lib import (  # noqa: F401
+    BF16, F32, KapError, KapLibraryMissing, attn_workspace_bytes, budget_from_ratio,
+    build_summary, compact_view, decode_attn, lib_path, load, proxy_query,
+    proxy_workspace_bytes, score_blocks, select_topk, verify_attn, version,
+)

@@ -1,0 +1,231 @@
+"""ctypes binding of libkap.so; argument marshalling only."""
+import ctypes
+import math
+import os
+
+import torch
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+_LIB = os.path.join(_HERE, "libkap.so")
+
+F32, BF16 = 0, 1
+_STATUS = {0: "ok", 1: "invalid argument", 2: "unsupported", 3: "capacity", 4: "workspace",
+           5: "HIP error"}
+
+
+class KapLibraryMissing(RuntimeError):
+    pass
+
+
+class KapError(RuntimeError):
+    def __init__(self, status, what, detail):
+        self.status = status
+        super().__init__(f"{what}: {_STATUS.get(status, status)}: {detail}")
+
+
+_P, _I32, _I64, _F, _SZ = ctypes.c_void_p, ctypes.c_int32, ctypes.c_int64, ctypes.c_float, ctypes.c_size_t
+_SIGS = {
+    "kap_status_string": ([_I32], ctypes.c_char_p),
+    "kap_last_error": ([], ctypes.c_char_p),
+    "kap_version": ([], ctypes.c_char_p),
+    "kap_score_blocks": ([_P, _I32, _P, _F, _P, _I32, _I32, _P, _I32, _P, _I32, _I32, _I32, _I32,
+                          _I32, _P, _P], _I32),
+    "kap_proxy_workspace_bytes": ([_I32, _I32, _I32], _SZ),
+    "kap_proxy_query": ([_P, _P, _I32, _I32, _I32, _P, _P, _SZ, _P], _I32),
+    "kap_select_topk": ([_P, _I32, _I32, _I32, _P, _I32, _I32, _P, _P, _P, _I32, _I32, _P, _P, _P],
+                        _I32),
+    "kap_budget_from_ratio": ([_I32, _I64, _I64, _I32, _I32], _I32),
+    "kap_compact_view": ([_P, _P, _I32, _I32, _I32, _P, _I32, _P, _I32, _P, _I32, _P, _P, _P, _P,
+                          _P], _I32),
+    "kap_attn_workspace_bytes": ([_I32, _I32, _I32, _I32, _I32], _SZ),
+    "kap_decode_attn": ([_P, _I32, _P, _F, _F, _P, _P, _I32, _I32, _I32, _I32, _I32, _P, _I32, _I32,
+                         _P, _I32, _I32, _P, _P, _P, _SZ, _P], _I32),
+    "kap_verify_attn": ([_P, _I32, _P, _I32, _F, _F, _P, _P, _I32, _I32, _I32, _I32, _I32, _P, _I32,
+                         _P, _I32, _I32, _P, _P, _P, _SZ, _P], _I32),
+    "kap_build_summary": ([_P, _I32, _I32, _I32, _I32, _I32, _P, _I32, _P, _I32, _P, _I32, _P], _I32),
+}
+_lib = None
+
+
+def lib_path() -> str:
+    return _LIB
+
+
+def load():
+    """Load libkap.so (built in-tree by __graft_entry__.build()); raise if absent."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(_LIB):
+        raise KapLibraryMissing(
+            f"{_LIB} is not built; run `python -c 'import __graft_entry__ as g; g.build()'`")
+    lib = ctypes.CDLL(_LIB)
+    for name, (args, res) in _SIGS.items():
+        fn = getattr(lib, name)
+        fn.argtypes = args
+        fn.restype = res
+    _lib = lib
+    return lib
+
+
+def version() -> str:
+    return load().kap_version().decode()
+
+
+def _check(status, what):
+    if status != 0:
+        raise KapError(status, what, load().kap_last_error().decode())
+
+
+def _dt(t: torch.Tensor) -> int:
+    if t.dtype == torch.float32:
+        return F32
+    if t.dtype in (torch.bfloat16, torch.int16, torch.uint16):
+        return BF16
+    raise TypeError(f"unsupported element type {t.dtype}")
+
+
+def _p(t):
+    if t is None:
+        return None
+    if not t.is_contiguous():
+        raise ValueError("tensors must be contiguous")
+    return ctypes.c_void_p(t.data_ptr())
+
+
+def _stream(stream):
+    if stream is None:
+        stream = torch.cuda.current_stream()
+    return ctypes.c_void_p(stream.cuda_stream)
+
+
+def attn_workspace_bytes(B, q_len, Hq, Hkv, D) -> int:
+    return int(load().kap_attn_workspace_bytes(B, q_len, Hq, Hkv, D))
+
+
+def proxy_workspace_bytes(B, d_model, n_out) -> int:
+    return int(load().kap_proxy_workspace_bytes(B, d_model, n_out))
+
+
+def budget_from_ratio(n_pages, s_num, s_den, anchor, recent) -> int:
+    return int(load().kap_budget_from_ratio(n_pages, s_num, s_den, anchor, recent))
+
+
+def score_blocks(q, positions, summary, block_table, seq_lens, Hkv, theta=1e4, scores=None,
+                 stream=None):
+    """kap_score_blocks: q [B][Hq][D] -> scores [B][Hkv][max_pages] float32."""
+    lib = load()
+    B, Hq, D = q.shape
+    max_pages = block_table.shape[1]
+    if scores is None:
+        scores = torch.empty((B, Hkv, max_pages), dtype=torch.float32, device=q.device)
+    st = lib.kap_score_blocks(_p(q), _dt(q), _p(positions), float(theta), _p(summary),
+                              _dt(summary), summary.shape[0], _p(block_table), max_pages,
+                              _p(seq_lens), B, Hq, Hkv, D, 16, _p(scores), _stream(stream))
+    _check(st, "kap_score_blocks")
+    return scores
+
+
+def proxy_query(hidden, w_q, q_out=None, workspace=None, stream=None):
+    """kap_proxy_query: hidden [B][d_model] bf16 @ w_q [d_model][n_out] bf16 -> fp32."""
+    lib = load()
+    B, dm = hidden.shape
+    n_out = w_q.shape[1]
+    if q_out is None:
+        q_out = torch.empty((B, n_out), dtype=torch.float32, device=hidden.device)
+    need = proxy_workspace_bytes(B, dm, n_out)
+    if workspace is None:
+        workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=hidden.device)
+    st = lib.kap_proxy_query(_p(hidden), _p(w_q), B, dm, n_out, _p(q_out), _p(workspace),
+                             workspace.numel(), _stream(stream))
+    _check(st, "kap_proxy_query")
+    return q_out
+
+
+def select_topk(scores, seq_lens, anchor, recent, k_mid, max_budget, capacity, per_head=False,
+                sel=None, cnt=None, stream=None):
+    """kap_select_topk -> (sel [B][G][capacity] int32, cnt [B][G] int32)."""
+    lib = load()
+    B, Hkv, max_pages = scores.shape
+    G = Hkv if per_head else 1
+    if sel is None:
+        sel = torch.empty((B, G, capacity), dtype=torch.int32, device=scores.device)
+    if cnt is None:
+        cnt = torch.empty((B, G), dtype=torch.int32, device=scores.device)
+    st = lib.kap_select_topk(_p(scores), B, Hkv, max_pages, _p(seq_lens), 16, int(bool(per_head)),
+                             _p(anchor), _p(recent), _p(k_mid), int(max_budget), int(capacity),
+                             _p(sel), _p(cnt), _stream(stream))
+    _check(st, "kap_select_topk")
+    return sel, cnt
+
+
+def compact_view(sel, cnt, block_table, seq_lens, positions, q_new, out=None, stream=None):
+    """kap_compact_view -> (compact_bt, compact_logical, compact_len, slot_mapping)."""
+    lib = load()
+    B, G, cap = sel.shape
+    dev = sel.device
+    if out is None:
+        out = (torch.empty((B, G, cap), dtype=torch.int32, device=dev),
+               torch.empty((B, G, cap), dtype=torch.int32, device=dev),
+               torch.empty((B, G), dtype=torch.int32, device=dev),
+               torch.empty((B, max(q_new, 1)), dtype=torch.int64, device=dev))
+    cbt, clog, clen, slot = out
+    st = lib.kap_compact_view(_p(sel), _p(cnt), B, G, cap, _p(block_table), block_table.shape[1],
+                              _p(seq_lens), 16, _p(positions), int(q_new), _p(cbt), _p(clog),
+                              _p(clen), _p(slot), _stream(stream))
+    _check(st, "kap_compact_view")
+    return cbt, clog, clen, slot
+
+
+def _scale(D, scale):
+    return 1.0 / math.sqrt(D) if scale is None else float(scale)
+
+
+def decode_attn(q, positions, k_pool, v_pool, table, lens, G=1, theta=1e4, scale=None, out=None,
+                lse=None, workspace=None, stream=None):
+    """kap_decode_attn: q [B][Hq][D] over a paged view table [B][G][width] with lens [B][G]."""
+    lib = load()
+    B, Hq, D = q.shape
+    num_pages, Hkv = k_pool.shape[0], k_pool.shape[1]
+    width = table.shape[-1]
+    if out is None:
+        out = torch.empty_like(q)
+    if workspace is None:
+        workspace = torch.empty(attn_workspace_bytes(B, 1, Hq, Hkv, D), dtype=torch.uint8,
+                                device=q.device)
+    st = lib.kap_decode_attn(_p(q), _dt(q), _p(positions), float(theta), _scale(D, scale),
+                             _p(k_pool), _p(v_pool), _dt(k_pool), num_pages, Hkv, D, 16, _p(table),
+                             width, int(G), _p(lens), B, Hq, _p(out), _p(lse), _p(workspace),
+                             workspace.numel(), _stream(stream))
+    _check(st, "kap_decode_attn")
+    return out
+
+
+def verify_attn(q, start_positions, k_pool, v_pool, block_table, seq_lens, theta=1e4, scale=None,
+                out=None, lse=None, workspace=None, stream=None):
+    """kap_verify_attn: q [B][q_len][Hq][D] over the full table."""
+    lib = load()
+    B, q_len, Hq, D = q.shape
+    num_pages, Hkv = k_pool.shape[0], k_pool.shape[1]
+    if out is None:
+        out = torch.empty_like(q)
+    if workspace is None:
+        workspace = torch.empty(attn_workspace_bytes(B, q_len, Hq, Hkv, D), dtype=torch.uint8,
+                                device=q.device)
+    st = lib.kap_verify_attn(_p(q), _dt(q), _p(start_positions), q_len, float(theta),
+                             _scale(D, scale), _p(k_pool), _p(v_pool), _dt(k_pool), num_pages, Hkv,
+                             D, 16, _p(block_table), block_table.shape[1], _p(seq_lens), B, Hq,
+                             _p(out), _p(lse), _p(workspace), workspace.numel(), _stream(stream))
+    _check(st, "kap_verify_attn")
+    return out
+
+
+def build_summary(k_pool, block_table, seq_lens, summary, stream=None):
+    """kap_build_summary: block-mean K of every referenced page into summary [P][Hkv][D]."""
+    lib = load()
+    num_pages, Hkv, ps, D = k_pool.shape
+    st = lib.kap_build_summary(_p(k_pool), _dt(k_pool), num_pages, Hkv, D, ps, _p(block_table),
+                               block_table.shape[1], _p(seq_lens), block_table.shape[0],
+                               _p(summary), _dt(summary), _stream(stream))
+    _check(st, "kap_build_summary")
+    return summary

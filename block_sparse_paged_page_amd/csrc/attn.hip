@@ -1,0 +1,566 @@
+// Split-K paged attention for q = 1 decode and the short verify window.
+//
+// One launch sequence serves both entry points (KAP paper: proposal steps are
+// decode-like forwards over the compact view; the verifier scores a short
+// window over the full KV with the original positions):
+//   1. prep   : rotate the queries at their logical positions (fp64 angles) and
+//               build the split-K work plan from the per-row lengths on device
+//               (no host synchronization, so the sequence is graph-capturable).
+//   2. partial: one wave per work item = (request, KV head, chunk of pages,
+//               slice of 32 query rows).  All query rows that share a KV head
+//               (the GQA group times the window) are processed together, so
+//               every K/V byte is read once per item.
+//   3. merge  : log-sum-exp combine of an item's partials in item order.
+//
+// bf16 path: QK^T and PV run on MFMA.  S^T = K Q^T with
+// v_mfma_f32_16x16x32_bf16 (A = 16 tokens x 32 dims of K straight from the
+// page, B = 32 dims x 16 query rows), which leaves each lane holding one query
+// row and 4 tokens -- exactly the B-operand layout of P^T for
+// O^T = V^T P^T on v_mfma_f32_16x16x16_bf16.  V pages are stored dim-major,
+// so the V^T operand (one dim, 4 consecutive tokens per lane) is a contiguous
+// 8-byte load and no transpose is needed anywhere.  The output accumulator
+// then holds one query row per lane, so the online-softmax rescale is local.
+// fp32 path: plain VALU loops (used for the small fp32 workloads).
+#include "kap_internal.h"
+
+namespace kap {
+
+// ------------------------------------------------------------------ workspace
+AttnWorkspace carve_attn_workspace(void* base, int32_t B, int32_t q_len, int32_t Hq,
+                                   int32_t Hkv, int32_t D) {
+  AttnWorkspace w{};
+  const int32_t grp = Hq / Hkv;
+  const int64_t R = (int64_t)grp * q_len;
+  w.max_items = kTargetItems + B * Hkv;
+  size_t off = 0;
+  char* p = (char*)base;
+  auto take = [&](size_t bytes) {
+    char* r = p ? p + off : nullptr;
+    off = align_up(off + bytes, 256);
+    return r;
+  };
+  w.n_items = (int32_t*)take(sizeof(int32_t));
+  w.row_off = (int32_t*)take(sizeof(int32_t) * ((size_t)B * Hkv + 1));
+  w.items = (int4*)take(sizeof(int4) * (size_t)w.max_items);
+  w.qrot = (void*)take(sizeof(float) * (size_t)B * q_len * Hq * D);
+  w.part_ml = (float2*)take(sizeof(float2) * (size_t)w.max_items * R);
+  w.part_o = (float*)take(sizeof(float) * (size_t)w.max_items * R * D);
+  w.bytes = off;
+  return w;
+}
+
+struct PrepArgs {
+  const void* q;
+  int32_t q_dt;
+  const int32_t* pos;
+  double log2_theta;
+  int32_t B, q_len, Hq, Hkv, D, G, width;
+  const int32_t* lens;
+  AttnWorkspace ws;
+};
+
+// ------------------------------------------------------------------ prep
+// Blocks [0, n_rope): one thread per (b, i, h, pair) rotates a pair in fp64.
+// Last block: the split-K plan.
+__global__ __launch_bounds__(256) void attn_prep_kernel(PrepArgs a) {
+  if (blockIdx.x == gridDim.x - 1) {
+    // ---- plan: rows are (b, g); pages per row from the view length
+    __shared__ long long s_total;
+    __shared__ int s_carry;
+    __shared__ int s_scan[256];
+    const int rows = a.B * a.Hkv;
+    const int tid = threadIdx.x;
+    if (tid == 0) s_total = 0;
+    __syncthreads();
+    long long local = 0;
+    for (int r = tid; r < rows; r += 256) {
+      const int b = r / a.Hkv, g = r % a.Hkv;
+      const int gr = a.G == 1 ? 0 : g;
+      int len = a.lens[b * a.G + gr];
+      len = min(max(len, 0), a.width * kPage);
+      local += (len + kPage - 1) / kPage;
+    }
+    atomicAdd((unsigned long long*)&s_total, (unsigned long long)local);
+    __syncthreads();
+    const long long total = s_total;
+    int chunk = (int)((total + kTargetItems - 1) / kTargetItems);
+    chunk = max(chunk, kMinChunk);
+    if (tid == 0) s_carry = 0;
+    __syncthreads();
+    for (int base = 0; base < rows; base += 256) {
+      const int r = base + tid;
+      int n = 0;
+      if (r < rows) {
+        const int b = r / a.Hkv, g = r % a.Hkv;
+        const int gr = a.G == 1 ? 0 : g;
+        int len = a.lens[b * a.G + gr];
+        len = min(max(len, 0), a.width * kPage);
+        const int np = (len + kPage - 1) / kPage;
+        n = (np + chunk - 1) / chunk;
+      }
+      s_scan[tid] = n;
+      __syncthreads();
+      for (int o = 1; o < 256; o <<= 1) {  // inclusive Hillis-Steele scan
+        int v = tid >= o ? s_scan[tid - o] : 0;
+        __syncthreads();
+        s_scan[tid] += v;
+        __syncthreads();
+      }
+      if (r < rows) a.ws.row_off[r] = s_carry + s_scan[tid] - n;
+      __syncthreads();
+      if (tid == 255) s_carry += s_scan[255];
+      __syncthreads();
+    }
+    const int n_items = s_carry;
+    if (tid == 0) {
+      a.ws.row_off[rows] = n_items;
+      *a.ws.n_items = n_items;
+    }
+    __syncthreads();
+    // emit items cooperatively; the owning row is found by binary search
+    for (int it = tid; it < n_items; it += 256) {
+      int lo = 0, hi = rows - 1;
+      while (lo < hi) {
+        const int mid = (lo + hi + 1) >> 1;
+        if (a.ws.row_off[mid] <= it) lo = mid; else hi = mid - 1;
+      }
+      const int r = lo;
+      const int b = r / a.Hkv, g = r % a.Hkv;
+      const int gr = a.G == 1 ? 0 : g;
+      int len = a.lens[b * a.G + gr];
+      len = min(max(len, 0), a.width * kPage);
+      const int np = (len + kPage - 1) / kPage;
+      const int j = it - a.ws.row_off[r];
+      const int p0 = j * chunk;
+      const int p1 = min(np, p0 + chunk);
+      a.ws.items[it] = make_int4(b, g, p0, p1);
+    }
+    return;
+  }
+  // ---- RoPE of every query row, rotate-half pairing, fp64 angles
+  const int half = a.D / 2;
+  const long long idx = (long long)blockIdx.x * blockDim.x + threadIdx.x;
+  const long long total = (long long)a.B * a.q_len * a.Hq * half;
+  if (idx >= total) return;
+  const int pair = (int)(idx % half);
+  const long long rowi = idx / half;  // ((b * q_len + i) * Hq + h)
+  const int i = (int)((rowi / a.Hq) % a.q_len);
+  const int b = (int)(rowi / ((long long)a.Hq * a.q_len));
+  const double position = (double)a.pos[b] + (double)i;
+  const double inv_freq = exp2(-(2.0 * pair / a.D) * a.log2_theta);
+  double s, c;
+  sincos(position * inv_freq, &s, &c);
+  const long long e0 = rowi * a.D + pair, e1 = e0 + half;
+  double x, y;
+  if (a.q_dt == KAP_BF16) {
+    x = bf16_to_f32(((const uint16_t*)a.q)[e0]);
+    y = bf16_to_f32(((const uint16_t*)a.q)[e1]);
+  } else {
+    x = ((const float*)a.q)[e0];
+    y = ((const float*)a.q)[e1];
+  }
+  const float xr = (float)(x * c - y * s);
+  const float yr = (float)(y * c + x * s);
+  if (a.q_dt == KAP_BF16) {
+    ((uint16_t*)a.ws.qrot)[e0] = f32_to_bf16(xr);
+    ((uint16_t*)a.ws.qrot)[e1] = f32_to_bf16(yr);
+  } else {
+    ((float*)a.ws.qrot)[e0] = xr;
+    ((float*)a.ws.qrot)[e1] = yr;
+  }
+}
+
+struct PartArgs {
+  const void* qrot;
+  const void* k;
+  const void* v;
+  const int32_t* table;
+  int32_t width, G;
+  const int32_t* lens;
+  const int32_t* pos;
+  const int4* items;
+  const int32_t* n_items;
+  float* part_o;
+  float2* part_ml;
+  int32_t q_len, Hq, Hkv, grp, R;
+  float scale_log2;
+};
+
+// ------------------------------------------------------------------ bf16 MFMA partial
+// NT row tiles of 16 query rows per wave (rows = GQA group x window, row r is
+// query r / grp of head g*grp + r % grp).
+template <int D, int NT>
+__global__ __launch_bounds__(64) void attn_partial_bf16(PartArgs a) {
+  const int item = blockIdx.x;
+  if (item >= *a.n_items) return;
+  const int4 it = a.items[item];
+  const int b = it.x, g = it.y, p0 = it.z, p1 = it.w;
+  const int lane = threadIdx.x;
+  const int l16 = lane & 15, q4 = lane >> 4;
+  const int row0 = blockIdx.y * 16 * NT;
+  const int gr = a.G == 1 ? 0 : g;
+  const int len = a.lens[b * a.G + gr];
+  const int32_t* trow = a.table + (int64_t)(b * a.G + gr) * a.width;
+  constexpr int KS = D / 32;  // QK k-steps
+  constexpr int NC = D / 16;  // PV dim tiles
+  const uint16_t* qrot = (const uint16_t*)a.qrot;
+  const uint16_t* kpool = (const uint16_t*)a.k;
+  const uint16_t* vpool = (const uint16_t*)a.v;
+
+  bf16x8 qf[NT][KS];
+  int qpos[NT];
+#pragma unroll
+  for (int t = 0; t < NT; ++t) {
+    const int r = row0 + 16 * t + l16;
+    qpos[t] = -1;
+    if (r < a.R) {
+      const int i = r / a.grp, hh = r % a.grp;
+      const int h = g * a.grp + hh;
+      qpos[t] = a.pos[b] + i;
+      const uint16_t* src = qrot + (((int64_t)b * a.q_len + i) * a.Hq + h) * D + 8 * q4;
+#pragma unroll
+      for (int s = 0; s < KS; ++s)
+        qf[t][s] = __builtin_bit_cast(bf16x8, *(const uint4*)(src + 32 * s));
+    } else {
+#pragma unroll
+      for (int s = 0; s < KS; ++s) qf[t][s] = __builtin_bit_cast(bf16x8, make_uint4(0, 0, 0, 0));
+    }
+  }
+
+  floatx4 o[NT][NC];
+  float m[NT], l[NT];
+#pragma unroll
+  for (int t = 0; t < NT; ++t) {
+    m[t] = -INFINITY;
+    l[t] = 0.f;
+#pragma unroll
+    for (int c = 0; c < NC; ++c) o[t][c] = floatx4{0.f, 0.f, 0.f, 0.f};
+  }
+
+  // software pipeline: fragments of page p+1 are in flight while page p is used
+  uint4 kf[KS];
+  uint2 vf[NC];
+  auto load_page = [&](int p, uint4* kd, uint2* vd) {
+    const int64_t phys = trow[p];
+    const uint16_t* kp = kpool + (phys * a.Hkv + g) * (int64_t)(kPage * D) + l16 * D + 8 * q4;
+    const uint16_t* vp = vpool + (phys * a.Hkv + g) * (int64_t)(D * kPage) + l16 * kPage + 4 * q4;
+#pragma unroll
+    for (int s = 0; s < KS; ++s) kd[s] = *(const uint4*)(kp + 32 * s);
+#pragma unroll
+    for (int c = 0; c < NC; ++c) vd[c] = *(const uint2*)(vp + 16 * kPage * c);
+  };
+  if (p0 < p1) load_page(p0, kf, vf);
+  for (int p = p0; p < p1; ++p) {
+    uint4 kc[KS];
+    uint2 vc[NC];
+#pragma unroll
+    for (int s = 0; s < KS; ++s) kc[s] = kf[s];
+#pragma unroll
+    for (int c = 0; c < NC; ++c) vc[c] = vf[c];
+    if (p + 1 < p1) load_page(p + 1, kf, vf);
+
+    const int tok0 = p * kPage + 4 * q4;
+    const int nvalid = len - p * kPage;
+    if (nvalid < kPage) {  // partial last page: invisible slots may hold anything
+#pragma unroll
+      for (int c = 0; c < NC; ++c) {
+        uint32_t lo = vc[c].x, hi = vc[c].y;
+        const int j0 = 4 * q4;
+        if (j0 + 0 >= nvalid) lo &= 0xffff0000u;
+        if (j0 + 1 >= nvalid) lo &= 0x0000ffffu;
+        if (j0 + 2 >= nvalid) hi &= 0xffff0000u;
+        if (j0 + 3 >= nvalid) hi &= 0x0000ffffu;
+        vc[c] = make_uint2(lo, hi);
+      }
+    }
+#pragma unroll
+    for (int t = 0; t < NT; ++t) {
+      floatx4 sacc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int s = 0; s < KS; ++s)
+        sacc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, kc[s]),
+                                                      qf[t][s], sacc, 0, 0, 0);
+      float z[4];
+      float mx = -INFINITY;
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        const int tok = tok0 + j;
+        const bool vis = tok < len && tok <= qpos[t];
+        z[j] = vis ? sacc[j] * a.scale_log2 : -INFINITY;
+        mx = fmaxf(mx, z[j]);
+      }
+      mx = wave_max_xor(mx, 16, 64);
+      const float mn = fmaxf(m[t], mx);
+      const float alpha = (mn == -INFINITY) ? 1.f : exp2f(m[t] - mn);
+      float pj[4];
+      float psum = 0.f;
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        pj[j] = (z[j] == -INFINITY) ? 0.f : exp2f(z[j] - mn);
+        psum += pj[j];
+      }
+      l[t] = l[t] * alpha + psum;
+      m[t] = mn;
+      const uint32_t w0 = (uint32_t)f32_to_bf16(pj[0]) | ((uint32_t)f32_to_bf16(pj[1]) << 16);
+      const uint32_t w1 = (uint32_t)f32_to_bf16(pj[2]) | ((uint32_t)f32_to_bf16(pj[3]) << 16);
+      const short4v pf = __builtin_bit_cast(short4v, make_uint2(w0, w1));
+#pragma unroll
+      for (int c = 0; c < NC; ++c) {
+        o[t][c] *= alpha;
+        o[t][c] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(__builtin_bit_cast(short4v, vc[c]),
+                                                           pf, o[t][c], 0, 0, 0);
+      }
+    }
+  }
+#pragma unroll
+  for (int t = 0; t < NT; ++t) {
+    l[t] += __shfl_xor(l[t], 16);
+    l[t] += __shfl_xor(l[t], 32);
+    const int r = row0 + 16 * t + l16;
+    if (r < a.R) {
+      float* dst = a.part_o + ((int64_t)item * a.R + r) * D + 4 * q4;
+#pragma unroll
+      for (int c = 0; c < NC; ++c) *(floatx4*)(dst + 16 * c) = o[t][c];
+      if (q4 == 0) a.part_ml[(int64_t)item * a.R + r] = make_float2(m[t], l[t]);
+    }
+  }
+}
+
+// ------------------------------------------------------------------ fp32 VALU partial
+// One wave per (item, slice of up to 32 rows).  Page tiles staged in LDS; each
+// lane owns (row, token) score pairs, then (row, dim) output pairs.
+template <int D>
+__global__ __launch_bounds__(64) void attn_partial_f32(PartArgs a) {
+  const int item = blockIdx.x;
+  if (item >= *a.n_items) return;
+  const int4 it = a.items[item];
+  const int b = it.x, g = it.y, p0 = it.z, p1 = it.w;
+  const int lane = threadIdx.x;
+  constexpr int RS = 32;                 // rows per slice
+  const int row0 = blockIdx.y * RS;
+  const int nr = min(RS, a.R - row0);
+  const int gr = a.G == 1 ? 0 : g;
+  const int len = a.lens[b * a.G + gr];
+  const int32_t* trow = a.table + (int64_t)(b * a.G + gr) * a.width;
+  const float* qrot = (const float*)a.qrot;
+  const float* kpool = (const float*)a.k;
+  const float* vpool = (const float*)a.v;
+
+  __shared__ float sq[RS][D];
+  __shared__ float sk[kPage][D + 1];
+  __shared__ float sv[D][kPage + 1];
+  __shared__ float sp[RS][kPage];
+  __shared__ float s_alpha[RS];
+  __shared__ int s_qpos[RS];
+  for (int e = lane; e < nr * D; e += 64) {
+    const int rr = e / D, d = e % D;
+    const int r = row0 + rr;
+    const int i = r / a.grp, h = g * a.grp + r % a.grp;
+    sq[rr][d] = qrot[(((int64_t)b * a.q_len + i) * a.Hq + h) * D + d];
+  }
+  if (lane < nr) s_qpos[lane] = a.pos[b] + (row0 + lane) / a.grp;
+  constexpr int DPL = (D + 63) / 64;     // dims per lane
+  float acc[RS][DPL];
+  float mrow = -INFINITY, lrow = 0.f;    // lane r < nr keeps row r's running stats
+#pragma unroll
+  for (int rr = 0; rr < RS; ++rr)
+#pragma unroll
+    for (int u = 0; u < DPL; ++u) acc[rr][u] = 0.f;
+  __syncthreads();
+  for (int p = p0; p < p1; ++p) {
+    const int64_t phys = trow[p];
+    const float* kp = kpool + (phys * a.Hkv + g) * (int64_t)(kPage * D);
+    const float* vp = vpool + (phys * a.Hkv + g) * (int64_t)(D * kPage);
+    const int nvalid = min(kPage, len - p * kPage);
+    for (int e = lane; e < kPage * D; e += 64) {
+      const int t = e / D, d = e % D;
+      sk[t][d] = kp[e];
+      const int dv = e / kPage, tv = e % kPage;
+      const float vv = vp[e];
+      sv[dv][tv] = (tv < nvalid) ? vv : 0.f;
+    }
+    __syncthreads();
+    for (int e = lane; e < nr * kPage; e += 64) {
+      const int rr = e / kPage, t = e % kPage;
+      const int tok = p * kPage + t;
+      float z = -INFINITY;
+      if (tok < len && tok <= s_qpos[rr]) {
+        float dot = 0.f;
+        for (int d = 0; d < D; ++d) dot += sq[rr][d] * sk[t][d];
+        z = dot * a.scale_log2;
+      }
+      sp[rr][t] = z;
+    }
+    __syncthreads();
+    if (lane < nr) {
+      float mx = -INFINITY;
+      for (int t = 0; t < kPage; ++t) mx = fmaxf(mx, sp[lane][t]);
+      const float mn = fmaxf(mrow, mx);
+      const float alpha = (mn == -INFINITY) ? 1.f : exp2f(mrow - mn);
+      float ps = 0.f;
+      for (int t = 0; t < kPage; ++t) {
+        const float z = sp[lane][t];
+        const float pz = (z == -INFINITY) ? 0.f : exp2f(z - mn);
+        sp[lane][t] = pz;
+        ps += pz;
+      }
+      lrow = lrow * alpha + ps;
+      mrow = mn;
+      s_alpha[lane] = alpha;
+    }
+    __syncthreads();
+#pragma unroll
+    for (int rr = 0; rr < RS; ++rr) {
+      if (rr < nr) {
+        const float al = s_alpha[rr];
+#pragma unroll
+        for (int u = 0; u < DPL; ++u) {
+          const int d = lane + 64 * u;
+          if (d < D) {
+            float s = acc[rr][u] * al;
+            for (int t = 0; t < kPage; ++t) s += sp[rr][t] * sv[d][t];
+            acc[rr][u] = s;
+          }
+        }
+      }
+    }
+    __syncthreads();
+  }
+#pragma unroll
+  for (int rr = 0; rr < RS; ++rr) {
+    if (rr < nr) {
+      const int r = row0 + rr;
+      float* dst = a.part_o + ((int64_t)item * a.R + r) * D;
+#pragma unroll
+      for (int u = 0; u < DPL; ++u) {
+        const int d = lane + 64 * u;
+        if (d < D) dst[d] = acc[rr][u];
+      }
+    }
+  }
+  if (lane < nr) a.part_ml[(int64_t)item * a.R + row0 + lane] = make_float2(mrow, lrow);
+}
+
+struct MergeArgs {
+  const int32_t* row_off;
+  const float* part_o;
+  const float2* part_ml;
+  void* out;
+  float* lse;
+  int32_t out_dt;
+  int32_t q_len, Hq, Hkv, grp, R, D;
+};
+
+// ------------------------------------------------------------------ merge
+// One block per (b, g); fixed item order, so the result is deterministic.
+__global__ __launch_bounds__(256) void attn_merge_kernel(MergeArgs a) {
+  const int bg = blockIdx.x;
+  const int b = bg / a.Hkv, g = bg % a.Hkv;
+  const int i0 = a.row_off[bg], i1 = a.row_off[bg + 1];
+  const int total = a.R * a.D;
+  for (int e = threadIdx.x; e < total; e += blockDim.x) {
+    const int r = e / a.D, d = e % a.D;
+    float M = -INFINITY;
+    for (int j = i0; j < i1; ++j) M = fmaxf(M, a.part_ml[(int64_t)j * a.R + r].x);
+    float L = 0.f, O = 0.f;
+    if (M != -INFINITY) {
+      for (int j = i0; j < i1; ++j) {
+        const float2 ml = a.part_ml[(int64_t)j * a.R + r];
+        if (ml.x == -INFINITY) continue;
+        const float w = exp2f(ml.x - M);
+        L += w * ml.y;
+        O += w * a.part_o[((int64_t)j * a.R + r) * a.D + d];
+      }
+    }
+    const float val = L > 0.f ? O / L : 0.f;
+    const int i = r / a.grp, h = g * a.grp + r % a.grp;
+    const int64_t orow = ((int64_t)b * a.q_len + i) * a.Hq + h;
+    if (a.out_dt == KAP_BF16)
+      ((uint16_t*)a.out)[orow * a.D + d] = f32_to_bf16(val);
+    else
+      ((float*)a.out)[orow * a.D + d] = val;
+    if (d == 0 && a.lse)
+      a.lse[orow] = L > 0.f ? (M + log2f(L)) * 0.69314718055994531f : -INFINITY;
+  }
+}
+
+// ------------------------------------------------------------------ launcher
+kap_status launch_attention(const AttnCall& c) {
+  const int grp = c.Hq / c.Hkv;
+  const int R = grp * c.q_len;
+  PrepArgs pa{};
+  pa.q = c.q;
+  pa.q_dt = c.dtype;
+  pa.pos = c.positions;
+  pa.log2_theta = log2((double)c.theta);
+  pa.B = c.B;
+  pa.q_len = c.q_len;
+  pa.Hq = c.Hq;
+  pa.Hkv = c.Hkv;
+  pa.D = c.D;
+  pa.G = c.G;
+  pa.width = c.width;
+  pa.lens = c.lens;
+  pa.ws = c.ws;
+  const long long pairs = (long long)c.B * c.q_len * c.Hq * (c.D / 2);
+  const int n_rope = (int)((pairs + 255) / 256);
+  hipLaunchKernelGGL(attn_prep_kernel, dim3(n_rope + 1), dim3(256), 0, c.stream, pa);
+  kap_status st = check_launch("attention prep");
+  if (st != KAP_OK) return st;
+
+  PartArgs a{};
+  a.qrot = c.ws.qrot;
+  a.k = c.k;
+  a.v = c.v;
+  a.table = c.table;
+  a.width = c.width;
+  a.G = c.G;
+  a.lens = c.lens;
+  a.pos = c.positions;
+  a.items = c.ws.items;
+  a.n_items = c.ws.n_items;
+  a.part_o = c.ws.part_o;
+  a.part_ml = c.ws.part_ml;
+  a.q_len = c.q_len;
+  a.Hq = c.Hq;
+  a.Hkv = c.Hkv;
+  a.grp = grp;
+  a.R = R;
+  a.scale_log2 = c.scale * 1.4426950408889634f;
+  if (c.dtype == KAP_BF16) {
+    const int nt = R <= 16 ? 1 : 2;
+    const int slices = (R + 16 * nt - 1) / (16 * nt);
+    dim3 grid(c.ws.max_items, slices);
+    if (c.D == 128) {
+      if (nt == 1) hipLaunchKernelGGL((attn_partial_bf16<128, 1>), grid, dim3(64), 0, c.stream, a);
+      else hipLaunchKernelGGL((attn_partial_bf16<128, 2>), grid, dim3(64), 0, c.stream, a);
+    } else {
+      if (nt == 1) hipLaunchKernelGGL((attn_partial_bf16<64, 1>), grid, dim3(64), 0, c.stream, a);
+      else hipLaunchKernelGGL((attn_partial_bf16<64, 2>), grid, dim3(64), 0, c.stream, a);
+    }
+  } else {
+    dim3 grid(c.ws.max_items, (R + 31) / 32);
+    if (c.D == 128) hipLaunchKernelGGL((attn_partial_f32<128>), grid, dim3(64), 0, c.stream, a);
+    else hipLaunchKernelGGL((attn_partial_f32<64>), grid, dim3(64), 0, c.stream, a);
+  }
+  st = check_launch("attention partial");
+  if (st != KAP_OK) return st;
+
+  MergeArgs ma{};
+  ma.row_off = c.ws.row_off;
+  ma.part_o = c.ws.part_o;
+  ma.part_ml = c.ws.part_ml;
+  ma.out = c.out;
+  ma.lse = c.lse;
+  ma.out_dt = c.dtype;
+  ma.q_len = c.q_len;
+  ma.Hq = c.Hq;
+  ma.Hkv = c.Hkv;
+  ma.grp = grp;
+  ma.R = R;
+  ma.D = c.D;
+  hipLaunchKernelGGL(attn_merge_kernel, dim3(c.B * c.Hkv), dim3(256), 0, c.stream, ma);
+  return check_launch("attention merge");
+}
+
+}  // namespace kap

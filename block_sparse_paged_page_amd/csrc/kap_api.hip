@@ -1,0 +1,265 @@
+// C ABI of libkap: host-side validation, workspace carving and launches.
+// Every check runs before any launch; nothing here allocates or synchronizes.
+#include <stdarg.h>
+#include <stdio.h>
+#include <string.h>
+
+#include "kap_internal.h"
+
+namespace kap {
+
+static thread_local char g_err[512];
+
+void set_error(const char* fmt, ...) {
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(g_err, sizeof g_err, fmt, ap);
+  va_end(ap);
+}
+
+kap_status fail(kap_status s, const char* fmt, ...) {
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(g_err, sizeof g_err, fmt, ap);
+  va_end(ap);
+  return s;
+}
+
+kap_status check_launch(const char* what) {
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return fail(KAP_ERR_HIP, "%s: %s", what, hipGetErrorString(e));
+  return KAP_OK;
+}
+
+static bool dtype_ok(int32_t d) { return d == KAP_F32 || d == KAP_BF16; }
+
+static kap_status check_heads(int32_t Hq, int32_t Hkv, int32_t D, int32_t page_size) {
+  if (Hq <= 0 || Hkv <= 0) return fail(KAP_ERR_INVALID_ARG, "Hq=%d Hkv=%d must be > 0", Hq, Hkv);
+  if (Hq % Hkv != 0) return fail(KAP_ERR_UNSUPPORTED, "Hq=%d not a multiple of Hkv=%d", Hq, Hkv);
+  if (Hq / Hkv > 16) return fail(KAP_ERR_UNSUPPORTED, "GQA group %d > 16", Hq / Hkv);
+  if (D != 64 && D != 128) return fail(KAP_ERR_UNSUPPORTED, "head_dim %d (64 or 128)", D);
+  if (page_size != kPage) return fail(KAP_ERR_UNSUPPORTED, "page_size %d (16)", page_size);
+  return KAP_OK;
+}
+
+}  // namespace kap
+
+using namespace kap;
+
+extern "C" {
+
+const char* kap_status_string(kap_status s) {
+  switch (s) {
+    case KAP_OK: return "ok";
+    case KAP_ERR_INVALID_ARG: return "invalid argument";
+    case KAP_ERR_UNSUPPORTED: return "unsupported configuration";
+    case KAP_ERR_CAPACITY: return "selection budget exceeds compact capacity";
+    case KAP_ERR_WORKSPACE: return "workspace too small";
+    case KAP_ERR_HIP: return "HIP error";
+  }
+  return "unknown status";
+}
+
+const char* kap_last_error(void) { return g_err; }
+
+const char* kap_version(void) { return "kap 0.1 gfx950"; }
+
+kap_status kap_score_blocks(const void* q, int32_t q_dtype, const int32_t* positions,
+                            float rope_theta, const void* summary, int32_t sum_dtype,
+                            int32_t num_pages, const int32_t* block_table, int32_t max_pages,
+                            const int32_t* seq_lens, int32_t B, int32_t Hq, int32_t Hkv,
+                            int32_t D, int32_t page_size, float* scores, kap_stream stream) {
+  g_err[0] = 0;
+  if (B < 0 || max_pages < 0 || num_pages < 0)
+    return fail(KAP_ERR_INVALID_ARG, "negative size (B=%d max_pages=%d num_pages=%d)", B,
+                max_pages, num_pages);
+  kap_status st = check_heads(Hq, Hkv, D, page_size);
+  if (st != KAP_OK) return st;
+  if (!dtype_ok(q_dtype) || !dtype_ok(sum_dtype))
+    return fail(KAP_ERR_UNSUPPORTED, "dtype q=%d summary=%d", q_dtype, sum_dtype);
+  if (!(rope_theta > 1.0f)) return fail(KAP_ERR_INVALID_ARG, "rope_theta %g <= 1", rope_theta);
+  if (B == 0 || max_pages == 0) return KAP_OK;
+  if (!q || !positions || !summary || !block_table || !seq_lens || !scores)
+    return fail(KAP_ERR_INVALID_ARG, "null pointer");
+  return launch_score(q, (kap_dtype)q_dtype, positions, rope_theta, summary,
+                      (kap_dtype)sum_dtype, block_table, max_pages, seq_lens, B, Hq, Hkv, D,
+                      scores, (hipStream_t)stream);
+}
+
+size_t kap_proxy_workspace_bytes(int32_t B, int32_t d_model, int32_t n_out) {
+  if (B <= 0 || d_model <= 0 || n_out <= 0) return 0;
+  return (size_t)(d_model / 512) * B * n_out * sizeof(float);
+}
+
+kap_status kap_proxy_query(const void* hidden, const void* w_q, int32_t B, int32_t d_model,
+                           int32_t n_out, float* q_out, void* workspace, size_t workspace_bytes,
+                           kap_stream stream) {
+  g_err[0] = 0;
+  if (B <= 0 || B > 16) return fail(KAP_ERR_UNSUPPORTED, "proxy batch %d (1..16)", B);
+  if (d_model <= 0 || d_model % 512 != 0)
+    return fail(KAP_ERR_UNSUPPORTED, "d_model %d (multiple of 512)", d_model);
+  if (n_out <= 0 || n_out % 64 != 0)
+    return fail(KAP_ERR_UNSUPPORTED, "n_out %d (multiple of 64)", n_out);
+  if (!hidden || !w_q || !q_out) return fail(KAP_ERR_INVALID_ARG, "null pointer");
+  const size_t need = kap_proxy_workspace_bytes(B, d_model, n_out);
+  if (!workspace || workspace_bytes < need)
+    return fail(KAP_ERR_WORKSPACE, "proxy workspace %zu < %zu bytes", workspace_bytes, need);
+  return launch_proxy((const uint16_t*)hidden, (const uint16_t*)w_q, B, d_model, n_out, q_out,
+                      (float*)workspace, d_model / 512, (hipStream_t)stream);
+}
+
+kap_status kap_select_topk(const float* scores, int32_t B, int32_t Hkv, int32_t max_pages,
+                           const int32_t* seq_lens, int32_t page_size, int32_t per_head,
+                           const int32_t* anchor, const int32_t* recent, const int32_t* k_mid,
+                           int32_t max_budget, int32_t capacity, int32_t* sel_pages,
+                           int32_t* sel_count, kap_stream stream) {
+  g_err[0] = 0;
+  if (B < 0 || Hkv <= 0 || max_pages < 0 || capacity < 0 || max_budget < 0)
+    return fail(KAP_ERR_INVALID_ARG, "bad size (B=%d Hkv=%d max_pages=%d capacity=%d budget=%d)",
+                B, Hkv, max_pages, capacity, max_budget);
+  if (page_size != kPage) return fail(KAP_ERR_UNSUPPORTED, "page_size %d (16)", page_size);
+  if (max_pages > kMaxSelectPages)
+    return fail(KAP_ERR_UNSUPPORTED, "max_pages %d > %d", max_pages, kMaxSelectPages);
+  if (per_head != 0 && per_head != 1) return fail(KAP_ERR_INVALID_ARG, "per_head %d", per_head);
+  if (max_budget > capacity)
+    return fail(KAP_ERR_CAPACITY, "budget %d pages exceeds compact capacity %d", max_budget,
+                capacity);
+  if (B == 0 || capacity == 0) return KAP_OK;
+  if (!scores || !seq_lens || !anchor || !recent || !k_mid || !sel_pages || !sel_count)
+    return fail(KAP_ERR_INVALID_ARG, "null pointer");
+  return launch_select(scores, B, Hkv, max_pages, seq_lens, per_head, anchor, recent, k_mid,
+                       capacity, sel_pages, sel_count, (hipStream_t)stream);
+}
+
+int32_t kap_budget_from_ratio(int32_t n_pages, int64_t s_num, int64_t s_den, int32_t anchor,
+                              int32_t recent) {
+  if (n_pages < 0 || s_num < 0 || s_den <= 0 || anchor < 0 || recent < 0) return -1;
+  int64_t budget = ((int64_t)n_pages * s_num + s_den - 1) / s_den;
+  if (budget < (int64_t)anchor + recent) budget = (int64_t)anchor + recent;
+  if (budget > n_pages) budget = n_pages;
+  return (int32_t)budget;
+}
+
+kap_status kap_compact_view(const int32_t* sel_pages, const int32_t* sel_count, int32_t B,
+                            int32_t G, int32_t capacity, const int32_t* block_table,
+                            int32_t max_pages, const int32_t* seq_lens, int32_t page_size,
+                            const int32_t* positions, int32_t q_new, int32_t* compact_bt,
+                            int32_t* compact_logical, int32_t* compact_len,
+                            int64_t* slot_mapping, kap_stream stream) {
+  g_err[0] = 0;
+  if (B < 0 || G <= 0 || capacity < 0 || max_pages < 0 || q_new < 0)
+    return fail(KAP_ERR_INVALID_ARG, "bad size (B=%d G=%d capacity=%d max_pages=%d q_new=%d)", B,
+                G, capacity, max_pages, q_new);
+  if (page_size != kPage) return fail(KAP_ERR_UNSUPPORTED, "page_size %d (16)", page_size);
+  if (B == 0) return KAP_OK;
+  if (!sel_pages || !sel_count || !block_table || !seq_lens || !compact_bt || !compact_logical ||
+      !compact_len)
+    return fail(KAP_ERR_INVALID_ARG, "null pointer");
+  if (q_new > 0 && (!slot_mapping || !positions))
+    return fail(KAP_ERR_INVALID_ARG, "slot mapping needs positions and an output");
+  return launch_compact(sel_pages, sel_count, B, G, capacity, block_table, max_pages, seq_lens,
+                        positions, q_new, compact_bt, compact_logical, compact_len,
+                        q_new > 0 ? slot_mapping : nullptr, (hipStream_t)stream);
+}
+
+size_t kap_attn_workspace_bytes(int32_t B, int32_t q_len, int32_t Hq, int32_t Hkv, int32_t D) {
+  if (B <= 0 || q_len <= 0 || Hq <= 0 || Hkv <= 0 || D <= 0 || Hq % Hkv) return 0;
+  return carve_attn_workspace(nullptr, B, q_len, Hq, Hkv, D).bytes;
+}
+
+static kap_status attn_common(const void* q, int32_t q_dtype, const int32_t* positions,
+                              int32_t q_len, float theta, float scale, const void* k_pool,
+                              const void* v_pool, int32_t kv_dtype, int32_t num_pages,
+                              int32_t Hkv, int32_t D, int32_t page_size, const int32_t* table,
+                              int32_t width, int32_t G, const int32_t* lens, int32_t B,
+                              int32_t Hq, void* out, float* lse, void* workspace,
+                              size_t workspace_bytes, kap_stream stream) {
+  if (B < 0 || width < 0 || num_pages < 0)
+    return fail(KAP_ERR_INVALID_ARG, "negative size (B=%d width=%d num_pages=%d)", B, width,
+                num_pages);
+  kap_status st = check_heads(Hq, Hkv, D, page_size);
+  if (st != KAP_OK) return st;
+  if (q_len < 1 || q_len > 16) return fail(KAP_ERR_UNSUPPORTED, "q_len %d (1..16)", q_len);
+  if (G != 1 && G != Hkv) return fail(KAP_ERR_INVALID_ARG, "G=%d (1 or Hkv=%d)", G, Hkv);
+  if (!dtype_ok(q_dtype) || !dtype_ok(kv_dtype))
+    return fail(KAP_ERR_UNSUPPORTED, "dtype q=%d kv=%d", q_dtype, kv_dtype);
+  if (q_dtype != kv_dtype)
+    return fail(KAP_ERR_UNSUPPORTED, "q dtype %d must equal KV dtype %d", q_dtype, kv_dtype);
+  if (!(theta > 1.0f)) return fail(KAP_ERR_INVALID_ARG, "rope_theta %g <= 1", theta);
+  if (!(scale > 0.0f)) return fail(KAP_ERR_INVALID_ARG, "scale %g <= 0", scale);
+  if (B == 0) return KAP_OK;
+  if (!q || !positions || !k_pool || !v_pool || !table || !lens || !out)
+    return fail(KAP_ERR_INVALID_ARG, "null pointer");
+  const size_t need = kap_attn_workspace_bytes(B, q_len, Hq, Hkv, D);
+  if (!workspace || workspace_bytes < need)
+    return fail(KAP_ERR_WORKSPACE, "attention workspace %zu < %zu bytes", workspace_bytes, need);
+  AttnCall c{};
+  c.q = q;
+  c.dtype = (kap_dtype)q_dtype;
+  c.positions = positions;
+  c.q_len = q_len;
+  c.theta = theta;
+  c.scale = scale;
+  c.k = k_pool;
+  c.v = v_pool;
+  c.Hkv = Hkv;
+  c.D = D;
+  c.table = table;
+  c.width = width;
+  c.G = G;
+  c.lens = lens;
+  c.B = B;
+  c.Hq = Hq;
+  c.out = out;
+  c.lse = lse;
+  c.ws = carve_attn_workspace(workspace, B, q_len, Hq, Hkv, D);
+  c.stream = (hipStream_t)stream;
+  return launch_attention(c);
+}
+
+kap_status kap_decode_attn(const void* q, int32_t q_dtype, const int32_t* positions,
+                           float rope_theta, float scale, const void* k_pool, const void* v_pool,
+                           int32_t kv_dtype, int32_t num_pages, int32_t Hkv, int32_t D,
+                           int32_t page_size, const int32_t* block_table, int32_t table_width,
+                           int32_t G, const int32_t* lens, int32_t B, int32_t Hq, void* out,
+                           float* lse, void* workspace, size_t workspace_bytes,
+                           kap_stream stream) {
+  g_err[0] = 0;
+  return attn_common(q, q_dtype, positions, 1, rope_theta, scale, k_pool, v_pool, kv_dtype,
+                     num_pages, Hkv, D, page_size, block_table, table_width, G, lens, B, Hq, out,
+                     lse, workspace, workspace_bytes, stream);
+}
+
+kap_status kap_verify_attn(const void* q, int32_t q_dtype, const int32_t* start_positions,
+                           int32_t q_len, float rope_theta, float scale, const void* k_pool,
+                           const void* v_pool, int32_t kv_dtype, int32_t num_pages, int32_t Hkv,
+                           int32_t D, int32_t page_size, const int32_t* block_table,
+                           int32_t max_pages, const int32_t* seq_lens, int32_t B, int32_t Hq,
+                           void* out, float* lse, void* workspace, size_t workspace_bytes,
+                           kap_stream stream) {
+  g_err[0] = 0;
+  return attn_common(q, q_dtype, start_positions, q_len, rope_theta, scale, k_pool, v_pool,
+                     kv_dtype, num_pages, Hkv, D, page_size, block_table, max_pages, 1, seq_lens,
+                     B, Hq, out, lse, workspace, workspace_bytes, stream);
+}
+
+kap_status kap_build_summary(const void* k_pool, int32_t kv_dtype, int32_t num_pages,
+                             int32_t Hkv, int32_t D, int32_t page_size,
+                             const int32_t* block_table, int32_t max_pages,
+                             const int32_t* seq_lens, int32_t B, void* summary,
+                             int32_t sum_dtype, kap_stream stream) {
+  g_err[0] = 0;
+  if (B < 0 || max_pages < 0 || num_pages < 0 || Hkv <= 0)
+    return fail(KAP_ERR_INVALID_ARG, "bad size");
+  if (D != 64 && D != 128) return fail(KAP_ERR_UNSUPPORTED, "head_dim %d (64 or 128)", D);
+  if (page_size != kPage) return fail(KAP_ERR_UNSUPPORTED, "page_size %d (16)", page_size);
+  if (!dtype_ok(kv_dtype) || !dtype_ok(sum_dtype))
+    return fail(KAP_ERR_UNSUPPORTED, "dtype kv=%d summary=%d", kv_dtype, sum_dtype);
+  if (B == 0 || max_pages == 0) return KAP_OK;
+  if (!k_pool || !block_table || !seq_lens || !summary)
+    return fail(KAP_ERR_INVALID_ARG, "null pointer");
+  return launch_summary(k_pool, (kap_dtype)kv_dtype, Hkv, D, block_table, max_pages, seq_lens, B,
+                        summary, (kap_dtype)sum_dtype, (hipStream_t)stream);
+}
+
+}  // extern "C"

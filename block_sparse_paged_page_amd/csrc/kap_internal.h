@@ -1,0 +1,111 @@
+// Internal declarations shared by the libkap HIP sources (gfx950 only).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "../../include/kap.h"
+
+namespace kap {
+
+// ---------------------------------------------------------------- constants
+constexpr int kPage = 16;            // tokens per KV page
+constexpr int kTargetItems = 2048;   // split-K work items aimed at per attention call
+constexpr int kMinChunk = 2;         // minimum pages per work item
+constexpr int kMaxSelectPages = 65536;
+
+// ---------------------------------------------------------------- device types
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef short short4v __attribute__((ext_vector_type(4)));
+typedef float floatx4 __attribute__((ext_vector_type(4)));
+
+__device__ __forceinline__ float bf16_to_f32(uint16_t x) {
+  return __uint_as_float(((uint32_t)x) << 16);
+}
+
+// round-to-nearest-even, NaN kept quiet
+__device__ __forceinline__ uint16_t f32_to_bf16(float f) {
+  uint32_t u = __float_as_uint(f);
+  if ((u & 0x7fffffffu) > 0x7f800000u) return (uint16_t)0x7fc0;
+  u += 0x7fffu + ((u >> 16) & 1u);
+  return (uint16_t)(u >> 16);
+}
+
+template <typename T>
+__device__ __forceinline__ float load_as_f32(const T* p, int64_t i);
+template <>
+__device__ __forceinline__ float load_as_f32<float>(const float* p, int64_t i) {
+  return p[i];
+}
+template <>
+__device__ __forceinline__ float load_as_f32<uint16_t>(const uint16_t* p, int64_t i) {
+  return bf16_to_f32(p[i]);
+}
+
+__device__ __forceinline__ float wave_max_xor(float v, int from, int to) {
+  for (int m = from; m < to; m <<= 1) v = fmaxf(v, __shfl_xor(v, m));
+  return v;
+}
+
+// ---------------------------------------------------------------- host side
+void set_error(const char* fmt, ...);
+kap_status fail(kap_status s, const char* fmt, ...);
+kap_status check_launch(const char* what);
+
+inline size_t align_up(size_t x, size_t a) { return (x + a - 1) / a * a; }
+
+// Workspace carving for the attention calls (decode and verify share it).
+struct AttnWorkspace {
+  int32_t* n_items;     // [1]
+  int32_t* row_off;     // [B*Hkv + 1]
+  int4* items;          // [max_items] (b, g, page_begin, page_end)
+  void* qrot;           // [B][q_len][Hq][D] (bf16 or f32)
+  float2* part_ml;      // [max_items][R] (running max in log2 units, sum)
+  float* part_o;        // [max_items][R][D]
+  int32_t max_items;
+  size_t bytes;
+};
+AttnWorkspace carve_attn_workspace(void* base, int32_t B, int32_t q_len, int32_t Hq,
+                                   int32_t Hkv, int32_t D);
+
+struct AttnCall {
+  const void* q;
+  kap_dtype dtype;
+  const int32_t* positions;
+  int32_t q_len;
+  float theta, scale;
+  const void* k;
+  const void* v;
+  int32_t Hkv, D;
+  const int32_t* table;
+  int32_t width, G;
+  const int32_t* lens;
+  int32_t B, Hq;
+  void* out;
+  float* lse;
+  AttnWorkspace ws;
+  hipStream_t stream;
+};
+kap_status launch_attention(const AttnCall& c);
+
+kap_status launch_score(const void* q, kap_dtype q_dt, const int32_t* pos, float theta,
+                        const void* summ, kap_dtype s_dt, const int32_t* bt, int32_t max_pages,
+                        const int32_t* seq_lens, int32_t B, int32_t Hq, int32_t Hkv, int32_t D,
+                        float* scores, hipStream_t stream);
+kap_status launch_select(const float* scores, int32_t B, int32_t Hkv, int32_t max_pages,
+                         const int32_t* seq_lens, int32_t per_head, const int32_t* anchor,
+                         const int32_t* recent, const int32_t* k_mid, int32_t capacity,
+                         int32_t* sel, int32_t* cnt, hipStream_t stream);
+kap_status launch_compact(const int32_t* sel, const int32_t* cnt, int32_t B, int32_t G,
+                          int32_t cap, const int32_t* bt, int32_t max_pages,
+                          const int32_t* seq_lens, const int32_t* pos, int32_t q_new,
+                          int32_t* cbt, int32_t* clog, int32_t* clen, int64_t* slot,
+                          hipStream_t stream);
+kap_status launch_summary(const void* k, kap_dtype kv_dt, int32_t Hkv, int32_t D,
+                          const int32_t* bt, int32_t max_pages, const int32_t* seq_lens,
+                          int32_t B, void* summ, kap_dtype s_dt, hipStream_t stream);
+kap_status launch_proxy(const uint16_t* hidden, const uint16_t* wq, int32_t B, int32_t dm,
+                        int32_t n_out, float* q_out, float* partial, int32_t splits,
+                        hipStream_t stream);
+
+}  // namespace kap

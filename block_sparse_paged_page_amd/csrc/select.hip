@@ -1,0 +1,199 @@
+// Top-K page selection under the A<a>R<r>K<k> split (KRI page, A<a>R<r>K<k>
+// tag section) with the lowest-index tie-break.
+//
+// One 1024-thread block per selection row (request, or request x KV head).
+// Thread t owns the KPT consecutive pages [t*KPT, (t+1)*KPT) and keeps their
+// keys in registers.  Keys are mapped to order-preserving uint32 (NaN lowest,
+// -0 == +0); a 4-pass 8-bit radix select finds the k-th largest middle key T
+// and how many of the keys equal to T are still needed; an index-ordered
+// block scan then admits those ties lowest index first, and a second scan
+// writes the chosen pages in ascending order.  Bit-exact: integer logic only,
+// apart from the pooled key, which is folded in fp32 with explicit
+// round-to-nearest adds in head order and one rounded division (the KRI
+// connector mean-pools over heads before the per-request top-K).
+#include "kap_internal.h"
+
+namespace kap {
+
+struct SelArgs {
+  const float* scores;
+  int32_t Hkv, max_pages;
+  const int32_t* seq_lens;
+  int32_t per_head;
+  const int32_t* anchor;
+  const int32_t* recent;
+  const int32_t* k_mid;
+  int32_t cap;
+  int32_t* sel;
+  int32_t* cnt;
+};
+
+__device__ __forceinline__ uint32_t order_key(float f) {
+  if (f != f) return 0u;          // NaN: below everything, all NaNs tie
+  if (f == 0.f) f = 0.f;          // -0 -> +0
+  const uint32_t u = __float_as_uint(f);
+  return (u & 0x80000000u) ? ~u : (u | 0x80000000u);
+}
+
+// Exclusive prefix of v over the block (1024 threads, thread order); *total gets the sum.
+__device__ __forceinline__ int block_exclusive_scan(int v, int* s_wave, int* total) {
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  int x = v;
+#pragma unroll
+  for (int o = 1; o < 64; o <<= 1) {
+    const int y = __shfl_up(x, o);
+    if (lane >= o) x += y;
+  }
+  if (lane == 63) s_wave[wave] = x;
+  __syncthreads();
+  if (tid < 64) {
+    int w = tid < 16 ? s_wave[tid] : 0;
+    int inc = w;
+#pragma unroll
+    for (int o = 1; o < 16; o <<= 1) {
+      const int y = __shfl_up(inc, o);
+      if (lane >= o) inc += y;
+    }
+    if (tid < 16) s_wave[16 + tid] = inc - w;  // exclusive wave offsets
+    if (tid == 15) s_wave[32] = inc;
+  }
+  __syncthreads();
+  const int excl = s_wave[16 + wave] + x - v;
+  *total = s_wave[32];
+  __syncthreads();
+  return excl;
+}
+
+template <int KPT>
+__global__ __launch_bounds__(1024) void select_kernel(SelArgs a) {
+  const int gr = blockIdx.x, b = blockIdx.y;
+  const int G = a.per_head ? a.Hkv : 1;
+  const int tid = threadIdx.x;
+  __shared__ int s_hist[256];
+  __shared__ int s_suf[257];
+  __shared__ int s_wave[33];
+  __shared__ uint32_t s_digit;
+  const int N = min((max(a.seq_lens[b], 0) + kPage - 1) / kPage, a.max_pages);
+  const int na = max(a.anchor[b], 0), nr = max(a.recent[b], 0), nk = a.k_mid[b];
+  int32_t* out = a.sel + ((int64_t)b * G + gr) * a.cap;
+  const bool all = (na + nr >= N);
+  const int mid_lo = na, mid_hi = N - nr;
+  const int take = all ? 0 : min(max(nk, 0), mid_hi - mid_lo);
+
+  uint32_t key[KPT];
+  uint64_t cand = 0;  // bit j: page t*KPT+j is a middle candidate
+  const int pbase = tid * KPT;
+#pragma unroll
+  for (int j = 0; j < KPT; ++j) {
+    const int p = pbase + j;
+    key[j] = 0u;
+    if (!all && p >= mid_lo && p < mid_hi) {
+      float k;
+      if (a.per_head) {
+        k = a.scores[((int64_t)b * a.Hkv + gr) * a.max_pages + p];
+      } else {
+        float acc = a.scores[((int64_t)b * a.Hkv) * a.max_pages + p];
+        for (int g = 1; g < a.Hkv; ++g)
+          acc = __fadd_rn(acc, a.scores[((int64_t)b * a.Hkv + g) * a.max_pages + p]);
+        k = __fdiv_rn(acc, (float)a.Hkv);
+      }
+      key[j] = order_key(k);
+      cand |= 1ull << j;
+    }
+  }
+
+  // ---- radix select of the take-th largest candidate key
+  uint32_t prefix = 0, pmask = 0;
+  int remaining = take;
+  if (take > 0) {
+    for (int shift = 24; shift >= 0; shift -= 8) {
+      if (tid < 256) s_hist[tid] = 0;
+      __syncthreads();
+#pragma unroll
+      for (int j = 0; j < KPT; ++j)
+        if (((cand >> j) & 1ull) && (key[j] & pmask) == prefix)
+          atomicAdd(&s_hist[(key[j] >> shift) & 255u], 1);
+      __syncthreads();
+      if (tid < 256) s_suf[tid] = s_hist[tid];
+      if (tid == 0) s_suf[256] = 0;
+      __syncthreads();
+      for (int o = 1; o < 256; o <<= 1) {  // suffix sums: s_suf[d] = sum over digits >= d
+        int v = 0;
+        if (tid < 256 && tid + o < 256) v = s_suf[tid + o];
+        __syncthreads();
+        if (tid < 256) s_suf[tid] += v;
+        __syncthreads();
+      }
+      if (tid < 256 && s_suf[tid] >= remaining && s_suf[tid + 1] < remaining) s_digit = tid;
+      __syncthreads();
+      const uint32_t d = s_digit;
+      remaining -= s_suf[d + 1];
+      prefix |= d << shift;
+      pmask |= 0xffu << shift;
+      __syncthreads();
+    }
+  }
+  const uint32_t T = prefix;
+
+  // ---- ties at T: lowest indices first
+  int n_eq = 0;
+#pragma unroll
+  for (int j = 0; j < KPT; ++j)
+    if (take > 0 && ((cand >> j) & 1ull) && key[j] == T) ++n_eq;
+  int tot;
+  int eq_rank = block_exclusive_scan(n_eq, s_wave, &tot);
+
+  uint64_t chosen = 0;
+#pragma unroll
+  for (int j = 0; j < KPT; ++j) {
+    const int p = pbase + j;
+    bool c = false;
+    if (p < N) {
+      if (all || p < mid_lo || p >= mid_hi) {
+        c = true;
+      } else if (take > 0 && ((cand >> j) & 1ull)) {
+        if (key[j] > T) c = true;
+        else if (key[j] == T) {
+          c = eq_rank < remaining;
+          ++eq_rank;
+        }
+      }
+    }
+    if (c) chosen |= 1ull << j;
+  }
+  const int n_ch = __popcll(chosen);
+  int total;
+  int pos = block_exclusive_scan(n_ch, s_wave, &total);
+#pragma unroll
+  for (int j = 0; j < KPT; ++j) {
+    if ((chosen >> j) & 1ull) {
+      if (pos < a.cap) out[pos] = pbase + j;
+      ++pos;
+    }
+  }
+  const int c = min(total, a.cap);
+  for (int j = c + tid; j < a.cap; j += 1024) out[j] = -1;
+  if (tid == 0) a.cnt[(int64_t)b * G + gr] = c;
+}
+
+kap_status launch_select(const float* scores, int32_t B, int32_t Hkv, int32_t max_pages,
+                         const int32_t* seq_lens, int32_t per_head, const int32_t* anchor,
+                         const int32_t* recent, const int32_t* k_mid, int32_t capacity,
+                         int32_t* sel, int32_t* cnt, hipStream_t stream) {
+  SelArgs a{scores, Hkv, max_pages, seq_lens, per_head, anchor, recent, k_mid, capacity, sel, cnt};
+  const int G = per_head ? Hkv : 1;
+  dim3 grid(G, B);
+  const int kpt = (max_pages + 1023) / 1024;
+#define KAP_SEL(K) hipLaunchKernelGGL((select_kernel<K>), grid, dim3(1024), 0, stream, a)
+  if (kpt <= 1) KAP_SEL(1);
+  else if (kpt <= 2) KAP_SEL(2);
+  else if (kpt <= 4) KAP_SEL(4);
+  else if (kpt <= 8) KAP_SEL(8);
+  else if (kpt <= 16) KAP_SEL(16);
+  else if (kpt <= 32) KAP_SEL(32);
+  else KAP_SEL(64);
+#undef KAP_SEL
+  return check_launch("select");
+}
+
+}  // namespace kap

@@ -1,0 +1,244 @@
+/*
+ * kap.h -- C ABI of the selected-KV paged decode attention library (libkap.so)
+ * for AMD Instinct MI355X (gfx950).
+ *
+ * The path, per request and attention layer:
+ *   1. kap_score_blocks  score every KV page: rotated query . block-mean K
+ *   2. kap_select_topk   pick pages under an anchor / recent / middle split
+ *   3. kap_compact_view  compact block table + slot mapping over the pick
+ *   4. kap_decode_attn   q = 1 GQA decode over the compact view
+ *   5. kap_verify_attn   short query window over the full paged KV
+ *
+ * Sources (web pages the method is described on):
+ *   [KAP]  "KAP: Bridging the Knowledge Selection-Runtime Consumption Gap in
+ *          LLM Systems" (arXiv 2607.24260): selected-KV view, executor,
+ *          verifier, shape stabilization and fallback paragraphs.
+ *   [KRI]  knlp.io "KRI" page: KRI-Q variant and the A<a>R<r>K<k> tag section.
+ *   [ESKV] EarlySelectKV news item, Interpretation: proxy-query routing over a
+ *          K-summary cache.
+ *
+ * Conventions shared by every entry point
+ *   - Pointers named *device* are device memory owned by the caller; the
+ *     library never frees, keeps or allocates memory.  Scalars are host values.
+ *   - Every call enqueues kernels on `stream` (a hipStream_t; NULL = default
+ *     stream) and returns without synchronizing, so a sequence of calls can be
+ *     captured in a HIP graph ([KAP] stabilizes shapes, tables and metadata so
+ *     that proposal and verify replay as graphs).
+ *   - All shape, dtype and size checks run on the host before any launch and
+ *     return a status; kap_last_error() then holds a message for the calling
+ *     thread.  Device-side data are trusted: page ids outside [0, num_pages)
+ *     or lengths beyond a table's width are undefined behaviour.
+ *   - Element types: KAP_F32 (float) and KAP_BF16 (bfloat16 stored as 16-bit).
+ *   - Page size is 16 tokens; head_dim is 64 or 128; Hq is a multiple of Hkv,
+ *     query heads map to KV heads in contiguous groups g(h) = h / (Hq/Hkv).
+ *   - Paged KV layout, per attention layer (dense, element offsets):
+ *       K pool [num_pages][Hkv][16][D]   (token-major inside a page)
+ *       V pool [num_pages][Hkv][D][16]   (dim-major inside a page: the 16
+ *                                         values of one dim are contiguous)
+ *     Summary pool [num_pages][Hkv][D].  Block table [B][max_pages] int32
+ *     maps logical page p of request b to its physical page (-1: none).
+ *   - Results are bit-identical from run to run and do not depend on where
+ *     pages sit in the pool.
+ */
+#ifndef KAP_H
+#define KAP_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define KAP_API __attribute__((visibility("default")))
+
+typedef enum {
+  KAP_OK = 0,
+  KAP_ERR_INVALID_ARG = 1, /* null pointer, negative or inconsistent size        */
+  KAP_ERR_UNSUPPORTED = 2, /* valid but not implemented (dtype, head_dim, ...)    */
+  KAP_ERR_CAPACITY = 3,    /* selection budget exceeds the compact capacity: the
+                              caller's cue to fall back to full context ([KAP]
+                              fallback when a plan exceeds the compact workspace) */
+  KAP_ERR_WORKSPACE = 4,   /* workspace missing or smaller than required          */
+  KAP_ERR_HIP = 5          /* a HIP launch or runtime call failed                 */
+} kap_status;
+
+typedef enum { KAP_F32 = 0, KAP_BF16 = 1 } kap_dtype;
+
+typedef void* kap_stream; /* hipStream_t */
+
+/* Static text for a status code. */
+KAP_API const char* kap_status_string(kap_status s);
+/* Detail of the last failing call on this thread ("" if none). */
+KAP_API const char* kap_last_error(void);
+/* Library version string. */
+KAP_API const char* kap_version(void);
+
+/*
+ * Page scores.  [KRI] KRI-Q: query-aware agreement of the query with each
+ * block's mean key; the query is first rotated at its full-sequence logical
+ * position ([KAP] executor).  For request b, KV head g and logical page p:
+ *   u_g        = sum over query heads h of group g of RoPE(q[b][h], positions[b])
+ *   scores[b][g][p] = u_g . summary[block_table[b][p]][g]   for p < ceil(seq_lens[b]/16)
+ *                   = -inf                                   for the other p < max_pages
+ * A raw dot product (no 1/sqrt(D), no softmax).  RoPE pairs element i with
+ * i + D/2 at frequency rope_theta^(-2i/D); angles are formed in fp64.
+ *   q          device [B][Hq][D], q_dtype (unrotated query)
+ *   positions  device [B] int32 logical position of the query
+ *   summary    device [num_pages][Hkv][D], sum_dtype (block-mean K per page)
+ *   block_table device [B][max_pages] int32; seq_lens device [B] int32
+ *   scores     device out [B][Hkv][max_pages] float
+ */
+KAP_API kap_status kap_score_blocks(const void* q, int32_t q_dtype, const int32_t* positions,
+                            float rope_theta, const void* summary, int32_t sum_dtype,
+                            int32_t num_pages, const int32_t* block_table, int32_t max_pages,
+                            const int32_t* seq_lens, int32_t B, int32_t Hq, int32_t Hkv,
+                            int32_t D, int32_t page_size, float* scores, kap_stream stream);
+
+/*
+ * Proxy query for early routing.  [ESKV] Interpretation: the side flow builds
+ * a proxy query from a preceding hidden state through the query projection,
+ * then scores and selects over the K-summary cache before the target layer.
+ *   q_out[b][n] = sum_c hidden[b][c] * w_q[c][n]     (bf16 inputs, fp32 accumulation,
+ *                 row splits of 512 added in split order: deterministic)
+ *   hidden device [B][d_model] bf16; w_q device [d_model][n_out] bf16 (row-major)
+ *   q_out  device out [B][n_out] float -- feed to kap_score_blocks as KAP_F32
+ *          with n_out = Hq * D.
+ *   workspace device, >= kap_proxy_workspace_bytes(B, d_model, n_out)
+ * 1 <= B <= 16; d_model a multiple of 512; n_out a multiple of 64.
+ */
+KAP_API size_t kap_proxy_workspace_bytes(int32_t B, int32_t d_model, int32_t n_out);
+KAP_API kap_status kap_proxy_query(const void* hidden, const void* w_q, int32_t B, int32_t d_model,
+                           int32_t n_out, float* q_out, void* workspace, size_t workspace_bytes,
+                           kap_stream stream);
+
+/*
+ * Top-K pages under the A<a>R<r>K<k> split ([KRI] A<a>R<r>K<k> tag section):
+ * anchors = the first a logical pages, recents = the last r, plus the best
+ * k_mid pages of the middle [a, N - r) by score (N = ceil(seq_lens[b]/16)).
+ * When a + r >= N every page is taken.  Ranking: score descending, ties to the
+ * lowest page index; -0 equals +0; NaN ranks below -inf.
+ * per_head = 0 (pooled): one selection per request on the mean over KV heads,
+ *   folded in fp32 as ((S0 + S1) + ... + S_{H-1}) / H ([KRI] the connector
+ *   mean-pools across heads before the per-request top-K).
+ * per_head = 1: an independent selection per KV head ([ESKV] per-head routing).
+ * Output lists are ascending ([KAP] selected pages are compacted in access
+ * order) and padded with -1.  G = per_head ? Hkv : 1.
+ *   scores     device [B][Hkv][max_pages] float (from kap_score_blocks)
+ *   anchor, recent, k_mid  device [B] int32
+ *   max_budget host upper bound of anchor+recent+k_mid over the batch
+ *   capacity   pages per output row; max_budget > capacity -> KAP_ERR_CAPACITY
+ *              before any launch.  If the device values still exceed it, the
+ *              row is truncated to capacity (memory stays in bounds).
+ *   sel_pages  device out [B][G][capacity] int32; sel_count device out [B][G]
+ * max_pages <= 65536.
+ */
+KAP_API kap_status kap_select_topk(const float* scores, int32_t B, int32_t Hkv, int32_t max_pages,
+                           const int32_t* seq_lens, int32_t page_size, int32_t per_head,
+                           const int32_t* anchor, const int32_t* recent, const int32_t* k_mid,
+                           int32_t max_budget, int32_t capacity, int32_t* sel_pages,
+                           int32_t* sel_count, kap_stream stream);
+
+/* Host helper: page budget for retention s = s_num/s_den over n_pages pages,
+ * ceil(n_pages * s) in integers, raised to anchor + recent, capped at n_pages.
+ * The middle count is budget - anchor - recent.  Returns -1 on bad input. */
+KAP_API int32_t kap_budget_from_ratio(int32_t n_pages, int64_t s_num, int64_t s_den, int32_t anchor,
+                              int32_t recent);
+
+/*
+ * Compact view over a selection ([KAP] selected-KV view: block tables resolve
+ * plan-visible logical blocks to compact physical pages in access order while
+ * logical positions are preserved; slot mappings place newly scheduled tokens
+ * into their physical KV slots).  For row (b, gr):
+ *   compact_bt[j]      = block_table[b][sel_pages[j]]   (j < sel_count, else -1)
+ *   compact_logical[j] = sel_pages[j]                   (j < sel_count, else -1)
+ *   compact_len        = total valid tokens of the selected pages (the last
+ *                        logical page holds seq_len - 16 (N - 1) tokens)
+ *   slot_mapping[b][i] = block_table[b][t/16]*16 + t%16 for t = positions[b] + i,
+ *                        or -1 when t/16 >= max_pages or that entry is -1.
+ * The compact table is a plain paged view: its first compact_len tokens are the
+ * selected tokens in ascending logical order, so kap_decode_attn reads it like
+ * any other table.
+ *   sel_pages device [B][G][capacity], sel_count device [B][G] (kap_select_topk)
+ *   compact_bt, compact_logical device out [B][G][capacity]; compact_len device out [B][G]
+ *   slot_mapping device out [B][q_new] int64 (may be NULL when q_new == 0)
+ */
+KAP_API kap_status kap_compact_view(const int32_t* sel_pages, const int32_t* sel_count, int32_t B,
+                            int32_t G, int32_t capacity, const int32_t* block_table,
+                            int32_t max_pages, const int32_t* seq_lens, int32_t page_size,
+                            const int32_t* positions, int32_t q_new, int32_t* compact_bt,
+                            int32_t* compact_logical, int32_t* compact_len,
+                            int64_t* slot_mapping, kap_stream stream);
+
+/*
+ * Workspace for kap_decode_attn (q_len = 1) and kap_verify_attn: rotated
+ * queries, the split-K work plan and the split partials.  Caller-owned device
+ * memory of at least this many bytes; its contents need no initialization and
+ * are overwritten by every call (so concurrent calls need separate workspaces).
+ */
+KAP_API size_t kap_attn_workspace_bytes(int32_t B, int32_t q_len, int32_t Hq, int32_t Hkv, int32_t D);
+
+/*
+ * q = 1 GQA decode attention over a paged view ([KAP] executor: each proposal
+ * step is a decode-like forward with one query token at its full-sequence
+ * logical position, over the compact block table and compact metadata).
+ * For request b and query head h (KV head g = g(h), table row gr = G == 1 ? 0 : g):
+ *   keys   = the first lens[b][gr] tokens of table row (b, gr): token t lives at
+ *            page block_table[(b*G + gr)*table_width + t/16], slot t%16
+ *   z_t    = scale * RoPE(q[b][h], positions[b]) . K(t)
+ *   out    = sum_t e^{z_t - m} V(t) / sum_t e^{z_t - m};  lse = m + ln sum_t e^{z_t - m}
+ * Work is split over page chunks (split-K) and merged with a log-sum-exp
+ * combine in fixed order.  Use (block_table, max_pages, G = 1, seq_lens) for
+ * full-context decode and (compact_bt, capacity, G, compact_len) for the
+ * selected view.  A row with no key yields out = 0 and lse = -inf.
+ *   q        device [B][Hq][D], q_dtype; out device [B][Hq][D], same dtype as q
+ *   lse      device out [B][Hq] float, natural log, or NULL
+ *   k_pool, v_pool device, kv_dtype, layouts above; q_dtype must equal kv_dtype
+ *   lens     device [B][G] int32 (lens <= 16 * table_width)
+ *   workspace device, >= kap_attn_workspace_bytes(B, 1, Hq, Hkv, D)
+ */
+KAP_API kap_status kap_decode_attn(const void* q, int32_t q_dtype, const int32_t* positions,
+                           float rope_theta, float scale, const void* k_pool, const void* v_pool,
+                           int32_t kv_dtype, int32_t num_pages, int32_t Hkv, int32_t D,
+                           int32_t page_size, const int32_t* block_table, int32_t table_width,
+                           int32_t G, const int32_t* lens, int32_t B, int32_t Hq, void* out,
+                           float* lse, void* workspace, size_t workspace_bytes,
+                           kap_stream stream);
+
+/*
+ * Full-context verification window ([KAP] verifier: a short contiguous query
+ * window scored against the full KV cache, full block table and original
+ * logical positions).  Query i of request b sits at start_positions[b] + i and
+ * is rotated there; it sees key t (logical position t, read through the full
+ * block table) iff t < seq_lens[b] and t <= start_positions[b] + i.
+ * Otherwise as kap_decode_attn.  1 <= q_len <= 16.
+ *   q   device [B][q_len][Hq][D]; out device [B][q_len][Hq][D] (q dtype)
+ *   lse device out [B][q_len][Hq] float or NULL
+ *   workspace >= kap_attn_workspace_bytes(B, q_len, Hq, Hkv, D)
+ */
+KAP_API kap_status kap_verify_attn(const void* q, int32_t q_dtype, const int32_t* start_positions,
+                           int32_t q_len, float rope_theta, float scale, const void* k_pool,
+                           const void* v_pool, int32_t kv_dtype, int32_t num_pages, int32_t Hkv,
+                           int32_t D, int32_t page_size, const int32_t* block_table,
+                           int32_t max_pages, const int32_t* seq_lens, int32_t B, int32_t Hq,
+                           void* out, float* lse, void* workspace, size_t workspace_bytes,
+                           kap_stream stream);
+
+/*
+ * Block-mean K summary maintenance ([ESKV] the K-summary cache kept beside the
+ * KV; [KRI] KRI-Q's block-mean K).  For every logical page p < N_b of every
+ * request, summary[block_table[b][p]][g][:] = mean of K over that page's valid
+ * tokens (seq_len - 16 p on the last page), fp32 accumulation, stored in
+ * sum_dtype with round-to-nearest-even.  Pages not referenced are untouched.
+ */
+KAP_API kap_status kap_build_summary(const void* k_pool, int32_t kv_dtype, int32_t num_pages,
+                             int32_t Hkv, int32_t D, int32_t page_size,
+                             const int32_t* block_table, int32_t max_pages,
+                             const int32_t* seq_lens, int32_t B, void* summary,
+                             int32_t sum_dtype, kap_stream stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* KAP_H */

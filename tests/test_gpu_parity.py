@@ -1,0 +1,348 @@
+"""GPU parity of the HIP path against the CPU oracle, through the C ABI.
+
+Inputs come from the seeded generators (workloads/); expected values come from
+the oracle on the same host arrays.  Nothing the GPU produces is fed to the
+oracle: integer stages (selection, compaction) are fed oracle-made inputs on
+both sides and must match bit for bit; the full GPU chain is then compared
+with the full oracle chain.
+"""
+import numpy as np
+import pytest
+import torch
+
+import block_sparse_paged_page_amd as kap
+import oracle
+import workloads as W
+from _gpu_util import (LSE_TOL, TOL, Case, check_scores, host, row_errors, t, workspace)
+
+pytestmark = pytest.mark.gpu
+
+CASES = {
+    # tiny fp32 case: 1 x 1024 tokens, GQA 4:1, D 64, A1R2K5
+    "tiny": lambda: W.spec("tiny"),
+    # Llama-3-8B-shaped attention, ragged and short rows (one shorter than its budget)
+    "llama": lambda: W.spec("llama8b_32k", B=3, seq_lens=[4096, 3007, 1234]),
+    # 32B-shaped, GQA 8:1 (verify rows = 32), ragged
+    "qwen": lambda: W.spec("qwen32b_128k", B=2, seq_lens=[16384, 9999]),
+    # mixed serving batch: ragged lengths, per-request retention and A/R splits
+    "mixed": lambda: W.spec("mixed_serving", B=8, len_range=(100, 20000), pool_pages=None),
+}
+_cache = {}
+
+
+def get_case(name):
+    if name not in _cache:
+        print(f"[case] building {name}", flush=True)
+        _cache[name] = Case(CASES[name](), aim_needles=True)
+    return _cache[name]
+
+
+def _oracle_chain(c, cap):
+    w, b = c.w, c.b
+    s_ref = oracle.score(b["q"], b["positions"], c.summ_l, c.btl, b["seq_lens"], w.Hkv)
+    sel, cnt = oracle.select(s_ref.astype(np.float32), b["seq_lens"], b["anchor"], b["recent"],
+                             c.k_mid_h, cap, per_head=w.per_head)
+    return s_ref, sel, cnt
+
+
+def _gpu_chain(c, cap):
+    w = c.w
+    scores = kap.score_blocks(c.q, c.pos, c.S, c.bt, c.L, w.Hkv)
+    sel, cnt = kap.select_topk(scores, c.L, c.anchor, c.recent, c.k_mid, c.budget(), cap,
+                               per_head=w.per_head)
+    return scores, sel, cnt
+
+
+@pytest.mark.parametrize("name", list(CASES))
+def test_score_parity(name):
+    c = get_case(name)
+    scores = kap.score_blocks(c.q, c.pos, c.S, c.bt, c.L, c.w.Hkv)
+    torch.cuda.synchronize()
+    check_scores(c, scores.cpu().numpy())
+
+
+@pytest.mark.parametrize("name", list(CASES))
+def test_select_bit_exact_on_oracle_scores(name):
+    c = get_case(name)
+    cap = c.budget() + 3
+    s_ref, sel_ref, cnt_ref = _oracle_chain(c, cap)
+    s32 = torch.from_numpy(s_ref.astype(np.float32)).cuda()
+    sel, cnt = kap.select_topk(s32, c.L, c.anchor, c.recent, c.k_mid, c.budget(), cap,
+                               per_head=c.w.per_head)
+    torch.cuda.synchronize()
+    np.testing.assert_array_equal(sel.cpu().numpy(), sel_ref)
+    np.testing.assert_array_equal(cnt.cpu().numpy(), cnt_ref)
+
+
+@pytest.mark.parametrize("name", list(CASES))
+def test_chain_selection_matches_oracle_chain(name):
+    c = get_case(name)
+    cap = c.budget() + 3
+    s_ref, sel_ref, cnt_ref = _oracle_chain(c, cap)
+    _, sel, cnt = _gpu_chain(c, cap)
+    torch.cuda.synchronize()
+    np.testing.assert_array_equal(cnt.cpu().numpy(), cnt_ref)
+    sel_h = sel.cpu().numpy()
+    # picks may differ only by swapping near-tied pages (scores agree to SCORE_TOL, not bits)
+    flips = 0
+    for bi in range(c.w.B):
+        for gr in range(sel_h.shape[1]):
+            n = int(cnt_ref[bi, gr])
+            a, b = set(sel_h[bi, gr, :n].tolist()), set(sel_ref[bi, gr, :n].tolist())
+            if a == b:
+                continue
+            key = s_ref[bi, gr] if c.w.per_head else s_ref[bi].mean(axis=0)
+            scale = np.abs(key[np.isfinite(key)]).max()
+            for p_ in a - b:
+                for q_ in b - a:
+                    assert abs(key[p_] - key[q_]) <= 1e-4 * scale, (bi, gr, p_, q_)
+            flips += len(a - b)
+    print(f"[{name}] near-tie flips between GPU and oracle chains: {flips}", flush=True)
+    # aimed needles are picked
+    for bi, pages in enumerate(c.b["needle_pages"]):
+        chosen = set(sel_h[bi, 0, :cnt_ref[bi, 0]].tolist())
+        k = int(c.k_mid_h[bi])
+        if k >= len(pages):
+            assert set(pages.tolist()) <= chosen
+
+
+@pytest.mark.parametrize("name", list(CASES))
+def test_compact_bit_exact(name):
+    c = get_case(name)
+    cap = c.budget() + 3
+    _, sel_ref, cnt_ref = _oracle_chain(c, cap)
+    q_new = 5
+    cbt, clog, clen, slot = kap.compact_view(t(sel_ref), t(cnt_ref), c.bt, c.L, c.pos, q_new)
+    torch.cuda.synchronize()
+    r = oracle.compact(sel_ref, cnt_ref, c.b["bt"], c.b["seq_lens"], c.b["positions"], q_new)
+    for got, want in zip((cbt, clog, clen, slot), r):
+        np.testing.assert_array_equal(got.cpu().numpy(), want)
+
+
+def _check_attn(c, out, lse, ref, lref):
+    tol = TOL[c.w.dtype]
+    o = host(out, c.bf16)
+    e = row_errors(o.reshape(ref.shape), ref)
+    assert e.max() <= tol, f"attention error {e.max():.3e} > {tol}"
+    lg = lse.cpu().numpy().reshape(lref.shape)
+    fin = np.isfinite(lref)
+    assert np.array_equal(np.isfinite(lg), fin)
+    if fin.any():
+        d = np.abs(lg[fin] - lref[fin]).max()
+        assert d <= LSE_TOL[c.w.dtype], f"lse error {d:.3e}"
+    return float(e.max())
+
+
+@pytest.mark.parametrize("name", list(CASES))
+def test_selected_decode_parity(name):
+    c = get_case(name)
+    w = c.w
+    cap = c.budget() + 3
+    _, sel_ref, cnt_ref = _oracle_chain(c, cap)
+    cbt, clog, clen, slot = kap.compact_view(t(sel_ref), t(cnt_ref), c.bt, c.L, c.pos, 1)
+    G = w.Hkv if w.per_head else 1
+    lse = torch.empty((w.B, w.Hq), dtype=torch.float32, device="cuda")
+    out = kap.decode_attn(c.q, c.pos, c.K, c.V, cbt, clen, G=G, lse=lse)
+    torch.cuda.synchronize()
+    keys = oracle.keys_selected(sel_ref, cnt_ref, c.b["seq_lens"])
+    ref, lref = oracle.attend(c.b["q"][:, None], c.b["positions"], c.Kl, c.Vl, c.btl, keys, G, w.Hkv)
+    err = _check_attn(c, out, lse, ref[:, 0], lref[:, 0])
+    print(f"[{name}] selected decode max rel err {err:.2e}", flush=True)
+
+
+@pytest.mark.parametrize("name", list(CASES))
+def test_full_decode_parity(name):
+    c = get_case(name)
+    w = c.w
+    lse = torch.empty((w.B, w.Hq), dtype=torch.float32, device="cuda")
+    out = kap.decode_attn(c.q, c.pos, c.K, c.V, c.bt, c.L, G=1, lse=lse)
+    torch.cuda.synchronize()
+    ref, lref = oracle.attend(c.b["q"][:, None], c.b["positions"], c.Kl, c.Vl, c.btl,
+                              oracle.keys_full(c.b["seq_lens"]), 1, w.Hkv)
+    err = _check_attn(c, out, lse, ref[:, 0], lref[:, 0])
+    print(f"[{name}] full decode max rel err {err:.2e}", flush=True)
+
+
+@pytest.mark.parametrize("name", list(CASES))
+@pytest.mark.parametrize("shift", [0, -3])
+def test_verify_parity(name, shift):
+    """Window at the context end (shift 0) and overlapping it (causal masking)."""
+    c = get_case(name)
+    w = c.w
+    start = np.maximum(c.b["positions"] + shift, 0).astype(np.int32)
+    lse = torch.empty((w.B, w.q_len, w.Hq), dtype=torch.float32, device="cuda")
+    out = kap.verify_attn(c.qv, t(start), c.K, c.V, c.bt, c.L, lse=lse)
+    torch.cuda.synchronize()
+    ref, lref = oracle.attend(c.b["qv"], start, c.Kl, c.Vl, c.btl,
+                              oracle.keys_full(c.b["seq_lens"]), 1, w.Hkv)
+    err = _check_attn(c, out, lse, ref, lref)
+    print(f"[{name}] verify (shift {shift}) max rel err {err:.2e}", flush=True)
+
+
+@pytest.mark.parametrize("name", ["llama", "qwen"])
+def test_gpu_chain_end_to_end(name):
+    """score -> select -> compact -> decode, all on the GPU, against the oracle chain."""
+    c = get_case(name)
+    w = c.w
+    cap = c.budget()
+    _, sel_ref, cnt_ref = _oracle_chain(c, cap)
+    _, sel, cnt = _gpu_chain(c, cap)
+    cbt, clog, clen, slot = kap.compact_view(sel, cnt, c.bt, c.L, c.pos, 1)
+    out = kap.decode_attn(c.q, c.pos, c.K, c.V, cbt, clen, G=1)
+    torch.cuda.synchronize()
+    keys = oracle.keys_selected(sel_ref, cnt_ref, c.b["seq_lens"])
+    ref, _ = oracle.attend(c.b["q"][:, None], c.b["positions"], c.Kl, c.Vl, c.btl, keys, 1, w.Hkv)
+    e = row_errors(host(out, c.bf16), ref[:, 0])
+    assert e.max() <= TOL[w.dtype]
+
+
+def test_verify_window_k_plus_one():
+    """The KAP paper's verify window is k+1 tokens (carry + k drafts): q_len 5 on the tiny case."""
+    w = W.spec("tiny", q_len=5)
+    c = Case(w)
+    out = kap.verify_attn(c.qv, c.pos, c.K, c.V, c.bt, c.L)
+    torch.cuda.synchronize()
+    ref, _ = oracle.attend(c.b["qv"], c.b["positions"], c.Kl, c.Vl, c.btl,
+                           oracle.keys_full(c.b["seq_lens"]), 1, w.Hkv)
+    assert row_errors(host(out, False), ref).max() <= TOL["f32"]
+
+
+# ----------------------------------------------------------------------------- invariants
+def test_full_selection_is_bit_identical_to_full_decode():
+    """s = 1: the compact view is the full table, so the result is bit-identical."""
+    c = get_case("llama")
+    w = c.w
+    N = w.n_pages
+    kall = t(N.astype(np.int32))
+    cap = int(N.max())
+    sel, cnt = kap.select_topk(kap.score_blocks(c.q, c.pos, c.S, c.bt, c.L, w.Hkv), c.L, c.anchor,
+                               c.recent, kall, cap, cap)
+    cbt, clog, clen, _ = kap.compact_view(sel, cnt, c.bt, c.L, c.pos, 1)
+    o_sel = kap.decode_attn(c.q, c.pos, c.K, c.V, cbt, clen)
+    o_full = kap.decode_attn(c.q, c.pos, c.K, c.V, c.bt, c.L)
+    torch.cuda.synchronize()
+    assert np.array_equal(clen.cpu().numpy()[:, 0], c.b["seq_lens"])
+    assert torch.equal(o_sel, o_full)
+
+
+def test_placement_invariance_and_determinism():
+    """Moving pages in the pool (table moved with them) and re-running change no bit."""
+    c = get_case("qwen")
+    pool = c.K.shape[0]
+    g = torch.Generator().manual_seed(7)
+    perm = torch.randperm(pool, generator=g).cuda()
+    inv = torch.argsort(perm)
+    K2, V2 = c.K[perm].contiguous(), c.V[perm].contiguous()
+    bt2 = torch.where(c.bt >= 0, inv[c.bt.clamp(min=0).long()].int(), c.bt).contiguous()
+    o1 = kap.verify_attn(c.qv, c.pos, c.K, c.V, c.bt, c.L)
+    o2 = kap.verify_attn(c.qv, c.pos, K2, V2, bt2, c.L)
+    o3 = kap.verify_attn(c.qv, c.pos, c.K, c.V, c.bt, c.L)
+    d1 = kap.decode_attn(c.q, c.pos, c.K, c.V, c.bt, c.L)
+    d2 = kap.decode_attn(c.q, c.pos, K2, V2, bt2, c.L)
+    torch.cuda.synchronize()
+    assert torch.equal(o1, o2) and torch.equal(o1, o3) and torch.equal(d1, d2)
+
+
+# ----------------------------------------------------------------------------- edge cases
+def test_adversarial_selection_keys():
+    """Ties, +-0, +-inf and NaN keys: GPU top-K equals the oracle's bit for bit."""
+    rng = np.random.default_rng(21)
+    palette = np.array([0.0, -0.0, 1.0, -1.0, 2.5, np.inf, -np.inf, np.nan, 1.0, 0.5], np.float32)
+    B, H, P = 6, 4, 3000
+    S = palette[rng.integers(0, len(palette), size=(B, H, P))]
+    L = np.array([16 * 3000, 16 * 2999 + 1, 100, 16 * 5, 1, 0], np.int32)
+    a = np.array([1, 4, 0, 2, 0, 1], np.int32)
+    r = np.array([2, 4, 3, 3, 0, 0], np.int32)
+    k = np.array([110, 1000, 2, 0, 5, 3], np.int32)
+    cap = 2000
+    for per_head in (False, True):
+        sel, cnt = kap.select_topk(t(S), t(L), t(a), t(r), t(k), int((a + r + k).max()), cap,
+                                   per_head=per_head)
+        torch.cuda.synchronize()
+        sref, cref = oracle.select(S, L, a, r, k, cap, per_head=per_head)
+        np.testing.assert_array_equal(sel.cpu().numpy(), sref)
+        np.testing.assert_array_equal(cnt.cpu().numpy(), cref)
+
+
+def test_empty_and_single_token_rows():
+    w = W.spec("llama8b_32k", B=3, seq_lens=[0, 1, 17], needles=0)
+    c = Case(w)
+    lse = torch.empty((w.B, w.Hq), dtype=torch.float32, device="cuda")
+    out = kap.decode_attn(c.q, c.pos, c.K, c.V, c.bt, c.L, lse=lse)
+    vlse = torch.empty((w.B, w.q_len, w.Hq), dtype=torch.float32, device="cuda")
+    vout = kap.verify_attn(c.qv, c.pos, c.K, c.V, c.bt, c.L, lse=vlse)
+    scores = kap.score_blocks(c.q, c.pos, c.S, c.bt, c.L, w.Hkv)
+    sel, cnt = kap.select_topk(scores, c.L, c.anchor, c.recent, c.k_mid, c.budget(), c.budget())
+    torch.cuda.synchronize()
+    o = host(out, True)
+    assert np.all(o[0] == 0) and np.all(np.isneginf(lse.cpu().numpy()[0]))
+    ref, lref = oracle.attend(c.b["q"][:, None], c.b["positions"], c.Kl, c.Vl, c.btl,
+                              oracle.keys_full(c.b["seq_lens"]), 1, w.Hkv)
+    assert row_errors(o[1:], ref[1:, 0]).max() <= TOL["bf16"]
+    vref, _ = oracle.attend(c.b["qv"], c.b["positions"], c.Kl, c.Vl, c.btl,
+                            oracle.keys_full(c.b["seq_lens"]), 1, w.Hkv)
+    assert row_errors(host(vout, True), vref).max() <= TOL["bf16"]
+    assert cnt.cpu().numpy().ravel().tolist() == [0, 1, 2]
+    assert np.all(np.isneginf(scores.cpu().numpy()[0]))
+
+
+def test_capacity_error_is_the_fallback_cue():
+    c = get_case("tiny")
+    s = kap.score_blocks(c.q, c.pos, c.S, c.bt, c.L, c.w.Hkv)
+    with pytest.raises(kap.KapError) as ei:
+        kap.select_topk(s, c.L, c.anchor, c.recent, c.k_mid, max_budget=8, capacity=7)
+    assert ei.value.status == 3
+
+
+def test_summary_builder_matches_oracle():
+    c = get_case("mixed")
+    S2 = torch.zeros_like(c.S)
+    kap.build_summary(c.K, c.bt, c.L, S2)
+    torch.cuda.synchronize()
+    got = oracle.widen(S2.cpu().numpy().view(np.uint16))[c.b["phys"]]
+    ref = oracle.summary(c.Kl, c.btl, c.b["seq_lens"])
+    used = np.zeros(len(c.b["phys"]), bool)
+    for bi in range(c.w.B):
+        used[c.btl[bi, :int(c.w.n_pages[bi])]] = True
+    # one bf16 rounding of a value that differs from the fp64 mean by fp32 summation error
+    d = np.abs(got[used] - ref[used])
+    assert np.all(d <= np.abs(ref[used]) * 2.0 ** -8 + 1e-6)
+
+
+def test_proxy_query_and_per_head_routing():
+    """Early routing: proxy query GEMV -> per-head scores -> per-head top-8 -> decode."""
+    w = W.spec("early_route_40k", B=2, seq_lens=[40000, 23456])
+    c = Case(w)
+    hid, wq = t(c.b["hidden"]), t(c.b["wq"])
+    qp = kap.proxy_query(hid, wq)
+    torch.cuda.synchronize()
+    qref = oracle.proxy_query(c.b["hidden"], c.b["wq"])
+    e = np.abs(qp.cpu().numpy() - qref).max(axis=1) / np.linalg.norm(qref, axis=1)
+    assert e.max() <= 1e-5
+    # per-head routing on the proxy query (oracle chain from the oracle's own proxy query)
+    Hq, D = w.Hq, w.D
+    q32 = qp.view(w.B, Hq, D).contiguous()
+    scores = kap.score_blocks(q32, c.pos, c.S, c.bt, c.L, w.Hkv)
+    qref32 = qref.astype(np.float32).reshape(w.B, Hq, D)
+    s_ref = oracle.score(qref32, c.b["positions"], c.summ_l, c.btl, c.b["seq_lens"], w.Hkv)
+    torch.cuda.synchronize()
+    s_gpu = scores.cpu().numpy()
+    N = w.n_pages
+    for bi in range(w.B):
+        n = int(N[bi])
+        scale = np.abs(s_ref[bi, :, :n]).max()
+        assert np.abs(s_gpu[bi, :, :n] - s_ref[bi, :, :n]).max() <= 1e-4 * scale
+    cap = 8
+    sel_ref, cnt_ref = oracle.select(s_ref.astype(np.float32), c.b["seq_lens"], 0, 0, 8, cap,
+                                     per_head=True)
+    sel, cnt = kap.select_topk(t(s_ref.astype(np.float32)), c.L, c.anchor, c.recent, c.k_mid, 8,
+                               cap, per_head=True)
+    torch.cuda.synchronize()
+    np.testing.assert_array_equal(sel.cpu().numpy(), sel_ref)
+    cbt, clog, clen, _ = kap.compact_view(sel, cnt, c.bt, c.L, c.pos, 1)
+    out = kap.decode_attn(c.q, c.pos, c.K, c.V, cbt, clen, G=w.Hkv)
+    torch.cuda.synchronize()
+    keys = oracle.keys_selected(sel_ref, cnt_ref, c.b["seq_lens"])
+    ref, _ = oracle.attend(c.b["q"][:, None], c.b["positions"], c.Kl, c.Vl, c.btl, keys, w.Hkv,
+                           w.Hkv)
+    assert row_errors(host(out, True), ref[:, 0]).max() <= TOL["bf16"]
