@@ -64,76 +64,71 @@ struct PrepArgs {
 // Last block: the split-K plan.
 __global__ __launch_bounds__(256) void attn_prep_kernel(PrepArgs a) {
   if (blockIdx.x == gridDim.x - 1) {
-    // ---- plan: rows are (b, g); pages per row from the view length
-    __shared__ long long s_total;
-    __shared__ int s_carry;
-    __shared__ int s_scan[256];
+    // ---- plan: rows are (b, g); pages per row from the view length.  Row
+    // offsets live in LDS so that item emission (binary search) is cheap.
+    __shared__ int s_off[kMaxPlanRows + 1];
+    __shared__ long long s_red[4];
+    __shared__ int s_wsum[4];
     const int rows = a.B * a.Hkv;
-    const int tid = threadIdx.x;
-    if (tid == 0) s_total = 0;
-    __syncthreads();
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     long long local = 0;
     for (int r = tid; r < rows; r += 256) {
       const int b = r / a.Hkv, g = r % a.Hkv;
       const int gr = a.G == 1 ? 0 : g;
-      int len = a.lens[b * a.G + gr];
-      len = min(max(len, 0), a.width * kPage);
-      local += (len + kPage - 1) / kPage;
+      const int len = min(max(a.lens[b * a.G + gr], 0), a.width * kPage);
+      const int np = (len + kPage - 1) / kPage;
+      s_off[r] = np;
+      local += np;
     }
-    atomicAdd((unsigned long long*)&s_total, (unsigned long long)local);
+    for (int o = 32; o > 0; o >>= 1) local += __shfl_xor(local, o);
+    if (lane == 0) s_red[wave] = local;
     __syncthreads();
-    const long long total = s_total;
-    int chunk = (int)((total + kTargetItems - 1) / kTargetItems);
-    chunk = max(chunk, kMinChunk);
-    if (tid == 0) s_carry = 0;
-    __syncthreads();
-    for (int base = 0; base < rows; base += 256) {
-      const int r = base + tid;
-      int n = 0;
-      if (r < rows) {
-        const int b = r / a.Hkv, g = r % a.Hkv;
-        const int gr = a.G == 1 ? 0 : g;
-        int len = a.lens[b * a.G + gr];
-        len = min(max(len, 0), a.width * kPage);
-        const int np = (len + kPage - 1) / kPage;
-        n = (np + chunk - 1) / chunk;
-      }
-      s_scan[tid] = n;
-      __syncthreads();
-      for (int o = 1; o < 256; o <<= 1) {  // inclusive Hillis-Steele scan
-        int v = tid >= o ? s_scan[tid - o] : 0;
-        __syncthreads();
-        s_scan[tid] += v;
-        __syncthreads();
-      }
-      if (r < rows) a.ws.row_off[r] = s_carry + s_scan[tid] - n;
-      __syncthreads();
-      if (tid == 255) s_carry += s_scan[255];
-      __syncthreads();
+    const long long total = s_red[0] + s_red[1] + s_red[2] + s_red[3];
+    const int chunk = max((int)((total + kTargetItems - 1) / kTargetItems), kMinChunk);
+    // items per row, then an exclusive scan: thread t owns a contiguous segment
+    const int seg = (rows + 255) / 256;
+    const int r0 = min(tid * seg, rows), r1 = min(r0 + seg, rows);
+    int mine = 0;
+    for (int r = r0; r < r1; ++r) {
+      const int n = (s_off[r] + chunk - 1) / chunk;
+      s_off[r] = n;
+      mine += n;
     }
-    const int n_items = s_carry;
+    int x = mine;
+    for (int o = 1; o < 64; o <<= 1) {
+      const int y = __shfl_up(x, o);
+      if (lane >= o) x += y;
+    }
+    if (lane == 63) s_wsum[wave] = x;
+    __syncthreads();
+    int base = x - mine;
+    for (int w = 0; w < wave; ++w) base += s_wsum[w];
+    for (int r = r0; r < r1; ++r) {
+      const int n = s_off[r];
+      s_off[r] = base;
+      a.ws.row_off[r] = base;
+      base += n;
+    }
+    const int n_items = s_wsum[0] + s_wsum[1] + s_wsum[2] + s_wsum[3];
     if (tid == 0) {
+      s_off[rows] = n_items;
       a.ws.row_off[rows] = n_items;
       *a.ws.n_items = n_items;
     }
     __syncthreads();
-    // emit items cooperatively; the owning row is found by binary search
     for (int it = tid; it < n_items; it += 256) {
       int lo = 0, hi = rows - 1;
       while (lo < hi) {
         const int mid = (lo + hi + 1) >> 1;
-        if (a.ws.row_off[mid] <= it) lo = mid; else hi = mid - 1;
+        if (s_off[mid] <= it) lo = mid; else hi = mid - 1;
       }
       const int r = lo;
       const int b = r / a.Hkv, g = r % a.Hkv;
       const int gr = a.G == 1 ? 0 : g;
-      int len = a.lens[b * a.G + gr];
-      len = min(max(len, 0), a.width * kPage);
+      const int len = min(max(a.lens[b * a.G + gr], 0), a.width * kPage);
       const int np = (len + kPage - 1) / kPage;
-      const int j = it - a.ws.row_off[r];
-      const int p0 = j * chunk;
-      const int p1 = min(np, p0 + chunk);
-      a.ws.items[it] = make_int4(b, g, p0, p1);
+      const int p0 = (it - s_off[r]) * chunk;
+      a.ws.items[it] = make_int4(b, g, p0, min(np, p0 + chunk));
     }
     return;
   }
@@ -147,9 +142,8 @@ __global__ __launch_bounds__(256) void attn_prep_kernel(PrepArgs a) {
   const int i = (int)((rowi / a.Hq) % a.q_len);
   const int b = (int)(rowi / ((long long)a.Hq * a.q_len));
   const double position = (double)a.pos[b] + (double)i;
-  const double inv_freq = exp2(-(2.0 * pair / a.D) * a.log2_theta);
   double s, c;
-  sincos(position * inv_freq, &s, &c);
+  rope_sincos(position, pair, a.D, a.log2_theta, &s, &c);
   const long long e0 = rowi * a.D + pair, e1 = e0 + half;
   double x, y;
   if (a.q_dt == KAP_BF16) {
@@ -448,40 +442,65 @@ struct MergeArgs {
   void* out;
   float* lse;
   int32_t out_dt;
-  int32_t q_len, Hq, Hkv, grp, R, D;
+  int32_t q_len, Hq, Hkv, grp, R;
 };
 
 // ------------------------------------------------------------------ merge
-// One block per (b, g); fixed item order, so the result is deterministic.
+// Block (b, g, query row r): IG item groups x D/4 threads (4 dims each).  Each
+// item group folds the items j = i0 + ig, i0 + ig + IG, ... (max, then the
+// e^(m_j - M) weighted sums); the groups are combined in group order through
+// LDS, so the result does not depend on scheduling.
+template <int D>
 __global__ __launch_bounds__(256) void attn_merge_kernel(MergeArgs a) {
-  const int bg = blockIdx.x;
+  constexpr int TPR = D / 4, IG = 256 / TPR;
+  const int bg = blockIdx.x, r = blockIdx.y;
   const int b = bg / a.Hkv, g = bg % a.Hkv;
+  const int tid = threadIdx.x, ig = tid / TPR, t4 = tid % TPR, d4 = t4 * 4;
   const int i0 = a.row_off[bg], i1 = a.row_off[bg + 1];
-  const int total = a.R * a.D;
-  for (int e = threadIdx.x; e < total; e += blockDim.x) {
-    const int r = e / a.D, d = e % a.D;
-    float M = -INFINITY;
-    for (int j = i0; j < i1; ++j) M = fmaxf(M, a.part_ml[(int64_t)j * a.R + r].x);
-    float L = 0.f, O = 0.f;
-    if (M != -INFINITY) {
-      for (int j = i0; j < i1; ++j) {
-        const float2 ml = a.part_ml[(int64_t)j * a.R + r];
-        if (ml.x == -INFINITY) continue;
-        const float w = exp2f(ml.x - M);
-        L += w * ml.y;
-        O += w * a.part_o[((int64_t)j * a.R + r) * a.D + d];
-      }
+  __shared__ float s_m[IG], s_l[IG];
+  __shared__ floatx4 s_o[IG][TPR];
+  float m = -INFINITY;
+  for (int j = i0 + ig; j < i1; j += IG) m = fmaxf(m, a.part_ml[(int64_t)j * a.R + r].x);
+  if (t4 == 0) s_m[ig] = m;
+  __syncthreads();
+  float M = -INFINITY;
+#pragma unroll
+  for (int k = 0; k < IG; ++k) M = fmaxf(M, s_m[k]);
+  float L = 0.f;
+  floatx4 O = {0.f, 0.f, 0.f, 0.f};
+  if (M != -INFINITY) {
+#pragma unroll 4
+    for (int j = i0 + ig; j < i1; j += IG) {
+      const float2 ml = a.part_ml[(int64_t)j * a.R + r];
+      const floatx4 o = *(const floatx4*)(a.part_o + ((int64_t)j * a.R + r) * D + d4);
+      const float w = exp2f(ml.x - M);  // 0 for items that saw no key (m = -inf)
+      L += w * ml.y;
+      O += w * o;
     }
-    const float val = L > 0.f ? O / L : 0.f;
-    const int i = r / a.grp, h = g * a.grp + r % a.grp;
-    const int64_t orow = ((int64_t)b * a.q_len + i) * a.Hq + h;
-    if (a.out_dt == KAP_BF16)
-      ((uint16_t*)a.out)[orow * a.D + d] = f32_to_bf16(val);
-    else
-      ((float*)a.out)[orow * a.D + d] = val;
-    if (d == 0 && a.lse)
-      a.lse[orow] = L > 0.f ? (M + log2f(L)) * 0.69314718055994531f : -INFINITY;
   }
+  if (t4 == 0) s_l[ig] = L;
+  s_o[ig][t4] = O;
+  __syncthreads();
+  if (ig != 0) return;
+  L = 0.f;
+  O = floatx4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+  for (int k = 0; k < IG; ++k) {
+    L += s_l[k];
+    O += s_o[k][t4];
+  }
+  const int i = r / a.grp, h = g * a.grp + r % a.grp;
+  const int64_t orow = ((int64_t)b * a.q_len + i) * a.Hq + h;
+  const float inv = L > 0.f ? 1.f / L : 0.f;
+  if (a.out_dt == KAP_BF16) {
+    const uint32_t w0 = (uint32_t)f32_to_bf16(O[0] * inv) | ((uint32_t)f32_to_bf16(O[1] * inv) << 16);
+    const uint32_t w1 = (uint32_t)f32_to_bf16(O[2] * inv) | ((uint32_t)f32_to_bf16(O[3] * inv) << 16);
+    *(uint2*)((uint16_t*)a.out + orow * D + d4) = make_uint2(w0, w1);
+  } else {
+    *(floatx4*)((float*)a.out + orow * D + d4) = O * inv;
+  }
+  if (d4 == 0 && a.lse)
+    a.lse[orow] = L > 0.f ? (M + log2f(L)) * 0.69314718055994531f : -INFINITY;
 }
 
 // ------------------------------------------------------------------ launcher
@@ -558,8 +577,9 @@ kap_status launch_attention(const AttnCall& c) {
   ma.Hkv = c.Hkv;
   ma.grp = grp;
   ma.R = R;
-  ma.D = c.D;
-  hipLaunchKernelGGL(attn_merge_kernel, dim3(c.B * c.Hkv), dim3(256), 0, c.stream, ma);
+  dim3 mgrid(c.B * c.Hkv, R);
+  if (c.D == 128) hipLaunchKernelGGL(attn_merge_kernel<128>, mgrid, dim3(256), 0, c.stream, ma);
+  else hipLaunchKernelGGL(attn_merge_kernel<64>, mgrid, dim3(256), 0, c.stream, ma);
   return check_launch("attention merge");
 }
 

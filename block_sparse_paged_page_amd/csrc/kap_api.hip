@@ -181,6 +181,8 @@ static kap_status attn_common(const void* q, int32_t q_dtype, const int32_t* pos
   if (st != KAP_OK) return st;
   if (q_len < 1 || q_len > 16) return fail(KAP_ERR_UNSUPPORTED, "q_len %d (1..16)", q_len);
   if (G != 1 && G != Hkv) return fail(KAP_ERR_INVALID_ARG, "G=%d (1 or Hkv=%d)", G, Hkv);
+  if ((int64_t)B * Hkv > kMaxPlanRows)
+    return fail(KAP_ERR_UNSUPPORTED, "B*Hkv=%lld > %d", (long long)B * Hkv, kMaxPlanRows);
   if (!dtype_ok(q_dtype) || !dtype_ok(kv_dtype))
     return fail(KAP_ERR_UNSUPPORTED, "dtype q=%d kv=%d", q_dtype, kv_dtype);
   if (q_dtype != kv_dtype)

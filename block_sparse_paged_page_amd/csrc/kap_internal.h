@@ -13,6 +13,7 @@ constexpr int kPage = 16;            // tokens per KV page
 constexpr int kTargetItems = 2048;   // split-K work items aimed at per attention call
 constexpr int kMinChunk = 2;         // minimum pages per work item
 constexpr int kMaxSelectPages = 65536;
+constexpr int kMaxPlanRows = 8192;      // batch x KV heads per attention call
 
 // ---------------------------------------------------------------- device types
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
@@ -40,6 +41,19 @@ __device__ __forceinline__ float load_as_f32<float>(const float* p, int64_t i) {
 template <>
 __device__ __forceinline__ float load_as_f32<uint16_t>(const uint16_t* p, int64_t i) {
   return bf16_to_f32(p[i]);
+}
+
+// sin and cos of pos * inv_freq, both fp64.  The angle reaches ~1.3e5 rad at
+// 128K context, so it is first reduced by 2*pi (split in two parts, Cody-Waite)
+// to keep the library call on its small-argument path.
+__device__ __forceinline__ void rope_sincos(double pos, int pair, int D, double log2_theta,
+                                            double* s, double* c) {
+  const double inv_freq = exp2(-(2.0 * pair / D) * log2_theta);
+  const double ang = pos * inv_freq;
+  const double k = rint(ang * 0.15915494309189535);       // 1 / (2 pi)
+  double r = fma(-k, 6.283185307179586, ang);             // 2 pi, high part
+  r = fma(-k, 2.4492935982947064e-16, r);                 // 2 pi, low part
+  sincos(r, s, c);
 }
 
 __device__ __forceinline__ float wave_max_xor(float v, int from, int to) {

@@ -37,16 +37,20 @@ __global__ __launch_bounds__(256) void score_kernel(ScoreArgs a) {
   const int b = blockIdx.z, g = blockIdx.y;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   __shared__ float su[D];
+  __shared__ float sq[16 * D];  // the group's query heads (grp <= 16)
   constexpr int half = D / 2;
+  {
+    const int64_t q0 = ((int64_t)b * a.Hq + g * a.grp) * D;  // group heads are contiguous
+    for (int e = tid; e < a.grp * D; e += 256) sq[e] = (float)widen_any<QT>(a.q, q0 + e);
+  }
+  __syncthreads();
   for (int pair = tid; pair < half; pair += 256) {
-    const double inv_freq = exp2(-(2.0 * pair / D) * a.log2_theta);
     double s, c;
-    sincos((double)a.pos[b] * inv_freq, &s, &c);
+    rope_sincos((double)a.pos[b], pair, D, a.log2_theta, &s, &c);
     double ux = 0.0, uy = 0.0;
     for (int hh = 0; hh < a.grp; ++hh) {
-      const int64_t row = ((int64_t)b * a.Hq + g * a.grp + hh) * D;
-      const double x = widen_any<QT>(a.q, row + pair);
-      const double y = widen_any<QT>(a.q, row + pair + half);
+      const double x = sq[hh * D + pair];
+      const double y = sq[hh * D + pair + half];
       ux += x * c - y * s;
       uy += y * c + x * s;
     }
@@ -58,7 +62,7 @@ __global__ __launch_bounds__(256) void score_kernel(ScoreArgs a) {
   constexpr int EPL = 16 / (int)sizeof(ST);  // elements per 16-byte load
   constexpr int LPR = D / EPL;               // lanes per summary row
   constexpr int RPL = 64 / LPR;              // rows per wave-wide load
-  constexpr int U = 4;                       // loads in flight per lane
+  constexpr int U = 8;                       // loads in flight per lane
   const int part = lane % LPR, sub = lane / LPR;
   float ur[EPL];
 #pragma unroll

@@ -69,7 +69,7 @@ __global__ __launch_bounds__(1024) void select_kernel(SelArgs a) {
   const int gr = blockIdx.x, b = blockIdx.y;
   const int G = a.per_head ? a.Hkv : 1;
   const int tid = threadIdx.x;
-  __shared__ int s_hist[256];
+  __shared__ int s_hist[16][256];  // one private histogram per wave
   __shared__ int s_suf[257];
   __shared__ int s_wave[33];
   __shared__ uint32_t s_digit;
@@ -83,23 +83,40 @@ __global__ __launch_bounds__(1024) void select_kernel(SelArgs a) {
   uint32_t key[KPT];
   uint64_t cand = 0;  // bit j: page t*KPT+j is a middle candidate
   const int pbase = tid * KPT;
+  float kv[KPT];
+  if (!all) {
+    // pooled: fold heads in ascending order, 4 heads' loads in flight at a time
+    const int nh = a.per_head ? 1 : a.Hkv;
+    const float* base = a.scores + ((int64_t)b * a.Hkv + (a.per_head ? gr : 0)) * a.max_pages;
+    for (int g0 = 0; g0 < nh; g0 += 4) {
+      float v[4][KPT];
 #pragma unroll
-  for (int j = 0; j < KPT; ++j) {
-    const int p = pbase + j;
-    key[j] = 0u;
-    if (!all && p >= mid_lo && p < mid_hi) {
-      float k;
-      if (a.per_head) {
-        k = a.scores[((int64_t)b * a.Hkv + gr) * a.max_pages + p];
-      } else {
-        float acc = a.scores[((int64_t)b * a.Hkv) * a.max_pages + p];
-        for (int g = 1; g < a.Hkv; ++g)
-          acc = __fadd_rn(acc, a.scores[((int64_t)b * a.Hkv + g) * a.max_pages + p]);
-        k = __fdiv_rn(acc, (float)a.Hkv);
-      }
-      key[j] = order_key(k);
-      cand |= 1ull << j;
+      for (int gi = 0; gi < 4; ++gi)
+#pragma unroll
+        for (int j = 0; j < KPT; ++j) {
+          const int p = pbase + j;
+          v[gi][j] = (g0 + gi < nh && p >= mid_lo && p < mid_hi)
+                         ? base[(int64_t)(g0 + gi) * a.max_pages + p] : 0.f;
+        }
+#pragma unroll
+      for (int gi = 0; gi < 4; ++gi)
+#pragma unroll
+        for (int j = 0; j < KPT; ++j)
+          if (g0 + gi < nh) kv[j] = (g0 + gi == 0) ? v[gi][j] : __fadd_rn(kv[j], v[gi][j]);
     }
+#pragma unroll
+    for (int j = 0; j < KPT; ++j) {
+      const int p = pbase + j;
+      key[j] = 0u;
+      if (p >= mid_lo && p < mid_hi) {
+        const float k = a.per_head ? kv[j] : __fdiv_rn(kv[j], (float)a.Hkv);
+        key[j] = order_key(k);
+        cand |= 1ull << j;
+      }
+    }
+  } else {
+#pragma unroll
+    for (int j = 0; j < KPT; ++j) key[j] = 0u;
   }
 
   // ---- radix select of the take-th largest candidate key
@@ -107,14 +124,20 @@ __global__ __launch_bounds__(1024) void select_kernel(SelArgs a) {
   int remaining = take;
   if (take > 0) {
     for (int shift = 24; shift >= 0; shift -= 8) {
-      if (tid < 256) s_hist[tid] = 0;
+      for (int e = tid; e < 16 * 256; e += 1024) (&s_hist[0][0])[e] = 0;
       __syncthreads();
+      const int wv = tid >> 6;
 #pragma unroll
       for (int j = 0; j < KPT; ++j)
         if (((cand >> j) & 1ull) && (key[j] & pmask) == prefix)
-          atomicAdd(&s_hist[(key[j] >> shift) & 255u], 1);
+          atomicAdd(&s_hist[wv][(key[j] >> shift) & 255u], 1);
       __syncthreads();
-      if (tid < 256) s_suf[tid] = s_hist[tid];
+      if (tid < 256) {
+        int h = 0;
+#pragma unroll
+        for (int w = 0; w < 16; ++w) h += s_hist[w][tid];
+        s_suf[tid] = h;
+      }
       if (tid == 0) s_suf[256] = 0;
       __syncthreads();
       for (int o = 1; o < 256; o <<= 1) {  // suffix sums: s_suf[d] = sum over digits >= d
@@ -189,8 +212,11 @@ kap_status launch_select(const float* scores, int32_t B, int32_t Hkv, int32_t ma
   else if (kpt <= 2) KAP_SEL(2);
   else if (kpt <= 4) KAP_SEL(4);
   else if (kpt <= 8) KAP_SEL(8);
+  else if (kpt <= 12) KAP_SEL(12);
   else if (kpt <= 16) KAP_SEL(16);
+  else if (kpt <= 24) KAP_SEL(24);
   else if (kpt <= 32) KAP_SEL(32);
+  else if (kpt <= 48) KAP_SEL(48);
   else KAP_SEL(64);
 #undef KAP_SEL
   return check_launch("select");

@@ -49,9 +49,15 @@ def _load():
     lib.kor_compact.argtypes = [_P, _P, _I, _I, _I, _P, _I, _P, _I, _P, _I, _P, _P, _P, _P]
     lib.kor_attend.argtypes = [_P, _I, _I, _P, _D, _D, _P, _P, _I, _I, _I, _I, _P, _I, _P, _P,
                                _I, _I, _I, _P, _P]
+    lib.kor_num_threads.restype = _I
     lib.kor_append_kv.argtypes = [_P, _P, _I, _P, _I, _I, _I, _I, _I, _P, _P]
     _lib = lib
     return lib
+
+
+def num_threads() -> int:
+    """OpenMP threads the oracle runs on."""
+    return int(_load().kor_num_threads())
 
 
 def _dt(a: np.ndarray) -> int:

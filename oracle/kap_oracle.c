@@ -28,11 +28,15 @@
  *   block table [B][max_pages], compact tables [B][G][cap]
  */
 #include <math.h>
+#include <omp.h>
 #include <stdint.h>
 #include <stdlib.h>
 #include <string.h>
 
 enum { KOR_F32 = 0, KOR_BF16 = 1 };
+
+/* Threads the OpenMP loops below use. */
+int kor_num_threads(void) { return omp_get_max_threads(); }
 
 /* Exact widening of one stored element to double. */
 static double widen(const void* base, int dtype, int64_t i) {

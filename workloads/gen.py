@@ -260,3 +260,64 @@ def dense_pool(batch: dict):
     K[phys] = Kp
     V[phys] = Vp
     return K, V
+
+
+def make_device(w: Workload, device, needle_dir: Optional[np.ndarray] = None) -> dict:
+    """Same recipe as make(), with the K/V pages drawn on the GPU.
+
+    Queries, needle pages, placement and budgets come from the same numpy
+    streams as make() (so they are identical); the K/V values come from
+    torch's Philox generator on `device`, seeded with (seed, b), and are
+    rounded to bf16 by torch (round-to-nearest-even).  Returns the make()
+    dictionary without K_pages/V_pages, plus device tensors K, V (full pool,
+    unallocated pages zero), and torch copies of the small arrays.
+    """
+    import torch
+
+    b = make(w, needle_dir=needle_dir, with_kv=False)
+    B, Hq, Hkv, D, ps = w.B, w.Hq, w.Hkv, w.D, w.page_size
+    grp = Hq // Hkv
+    L = b["seq_lens"]
+    NA = w.alloc_pages
+    tdt = torch.bfloat16 if w.dtype == "bf16" else torch.float32
+    pool = b["pool_pages"]
+    K = torch.zeros((pool, Hkv, ps, D), dtype=tdt, device=device)
+    V = torch.zeros((pool, Hkv, D, ps), dtype=tdt, device=device)
+    alpha = w.needle_scale * w.sigma * math.sqrt(D)
+    starts = np.concatenate([[0], np.cumsum(NA)[:-1]]).astype(np.int64)
+    for bi in range(B):
+        g = torch.Generator(device=device)
+        g.manual_seed(int(w.seed) * 1_000_003 + bi)
+        npg = int(NA[bi])
+        rows = torch.from_numpy(b["phys"][starts[bi]:starts[bi] + npg].astype(np.int64)).to(device)
+        kb = torch.randn((npg, Hkv, ps, D), generator=g, device=device, dtype=torch.float32)
+        vb = torch.randn((npg, Hkv, ps, D), generator=g, device=device, dtype=torch.float32)
+        if w.sigma != 1.0:
+            kb.mul_(w.sigma)
+            vb.mul_(w.sigma)
+        pages = b["needle_pages"][bi]
+        if len(pages):
+            if needle_dir is not None:
+                dirs = np.asarray(needle_dir[bi], dtype=np.float64)
+            else:
+                qb = b["q"][bi]
+                qf = ((qb.astype(np.uint32) << 16).view(np.float32) if qb.dtype == np.uint16
+                      else qb).astype(np.float64)
+                qsum = qf.reshape(Hkv, grp, D).sum(axis=1)
+                dirs = qsum / np.linalg.norm(qsum, axis=1, keepdims=True)
+            bump = torch.from_numpy((alpha * dirs).astype(np.float32)).to(device)
+            for p in pages:
+                nvalid = min(ps, int(L[bi]) - int(p) * ps)
+                kb[int(p), :, :nvalid, :] += bump[:, None, :]
+        first_dead = int(L[bi])
+        if first_dead < npg * ps:
+            p0 = first_dead // ps
+            for p in range(p0, npg):
+                t0 = max(0, first_dead - p * ps)
+                kb[p, :, t0:, :] = float("nan")
+                vb[p, :, t0:, :] = float("nan")
+        K[rows] = kb.to(tdt)
+        V[rows] = vb.transpose(2, 3).contiguous().to(tdt)
+        del kb, vb
+    b["K"], b["V"] = K, V
+    return b
