@@ -84,7 +84,7 @@ def algorithmic_bytes(w, b, sel_pages):
 def read_traffic(kernel_key):
     """HBM traffic per launch recorded from rocprofv3 PMC runs, if the kernel source still matches."""
     import hashlib
-    path = os.path.join(ROOT, "profiles", "traffic.md")
+    path = os.path.join(ROOT, "profiles", "attn_qwen32b_128k_b4_hbm_traffic.md")
     if not os.path.exists(path):
         return None
     src = os.path.join(ROOT, "block_sparse_paged_page_amd", "csrc", "attn.hip")
@@ -251,12 +251,29 @@ def main():
     torch.cuda.synchronize()
     full_ms = np.mean([e0[i].elapsed_time(e0[i + 1]) for i in range(args.steps)])
 
+    # measured read ceiling: 16-byte-load stream over 4 GiB (median of 10)
+    probe = torch.zeros(4 << 30, dtype=torch.uint8, device=dev)
+    sink = torch.zeros(1, dtype=torch.int32, device=dev)
+    for _ in range(2):
+        kap.diag_stream_read(probe, sink)
+    pe = [torch.cuda.Event(enable_timing=True) for _ in range(11)]
+    pe[0].record(stream)
+    for i in range(10):
+        kap.diag_stream_read(probe, sink)
+        pe[i + 1].record(stream)
+    torch.cuda.synchronize()
+    ceil_ms = sorted(pe[i].elapsed_time(pe[i + 1]) for i in range(10))[5]
+    ceiling_gbs = probe.numel() / (ceil_ms * 1e-3) / 1e9
+    del probe
+
     gbs = lambda nb, ms: nb / (ms * 1e-3) / 1e9  # noqa: E731
     ver_gbs = gbs(nbytes["verify"], ver_ms)
     traffic = read_traffic("verify")
     roofline = {"bound": "hbm", "kernel": "kap_verify_attn (prep + MFMA split-K partial + merge)",
                 "achieved": round(ver_gbs, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
                 "frac": round(ver_gbs / HBM_PEAK_GBS, 4), "traffic": traffic,
+                "measured_read_ceiling_GBps": round(ceiling_gbs, 1),
+                "frac_of_measured_ceiling": round(ver_gbs / ceiling_gbs, 4),
                 "bytes_per_launch": nbytes["verify"], "avg_launch_us": round(ver_ms * 1e3, 2)}
     s_meas = nbytes["decode_selected"] / nbytes["decode_full"]
     h = 0.952  # KAP paper Table 5 at 128K: s + (h - s) = 0.055 + 0.897

@@ -12,6 +12,6 @@ holding bf16 bit patterns; fp32 data are torch.float32; index tensors int32
 """
 from ._lib import (  # noqa: F401
     BF16, F32, KapError, KapLibraryMissing, attn_workspace_bytes, budget_from_ratio,
-    build_summary, compact_view, decode_attn, lib_path, load, proxy_query,
+    build_summary, compact_view, decode_attn, diag_stream_read, lib_path, load, proxy_query,
     proxy_workspace_bytes, score_blocks, select_topk, verify_attn, version,
 )

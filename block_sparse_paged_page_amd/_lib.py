@@ -42,6 +42,7 @@ _SIGS = {
                          _P, _I32, _I32, _P, _P, _P, _SZ, _P], _I32),
     "kap_verify_attn": ([_P, _I32, _P, _I32, _F, _F, _P, _P, _I32, _I32, _I32, _I32, _I32, _P, _I32,
                          _P, _I32, _I32, _P, _P, _P, _SZ, _P], _I32),
+    "kap_diag_stream_read": ([_P, _SZ, _P, _P], _I32),
     "kap_build_summary": ([_P, _I32, _I32, _I32, _I32, _I32, _P, _I32, _P, _I32, _P, _I32, _P], _I32),
 }
 _lib = None
@@ -218,6 +219,13 @@ def verify_attn(q, start_positions, k_pool, v_pool, block_table, seq_lens, theta
                              _p(out), _p(lse), _p(workspace), workspace.numel(), _stream(stream))
     _check(st, "kap_verify_attn")
     return out
+
+
+def diag_stream_read(buf, sink, stream=None):
+    """kap_diag_stream_read: read every byte of `buf` (diagnostic bandwidth probe)."""
+    st = load().kap_diag_stream_read(_p(buf), buf.numel() * buf.element_size(), _p(sink),
+                                     _stream(stream))
+    _check(st, "kap_diag_stream_read")
 
 
 def build_summary(k_pool, block_table, seq_lens, summary, stream=None):

@@ -67,6 +67,7 @@ __global__ __launch_bounds__(256) void attn_prep_kernel(PrepArgs a) {
     // ---- plan: rows are (b, g); pages per row from the view length.  Row
     // offsets live in LDS so that item emission (binary search) is cheap.
     __shared__ int s_off[kMaxPlanRows + 1];
+    __shared__ int s_np[kMaxPlanRows];
     __shared__ long long s_red[4];
     __shared__ int s_wsum[4];
     const int rows = a.B * a.Hkv;
@@ -78,6 +79,7 @@ __global__ __launch_bounds__(256) void attn_prep_kernel(PrepArgs a) {
       const int len = min(max(a.lens[b * a.G + gr], 0), a.width * kPage);
       const int np = (len + kPage - 1) / kPage;
       s_off[r] = np;
+      s_np[r] = np;
       local += np;
     }
     for (int o = 32; o > 0; o >>= 1) local += __shfl_xor(local, o);
@@ -123,12 +125,8 @@ __global__ __launch_bounds__(256) void attn_prep_kernel(PrepArgs a) {
         if (s_off[mid] <= it) lo = mid; else hi = mid - 1;
       }
       const int r = lo;
-      const int b = r / a.Hkv, g = r % a.Hkv;
-      const int gr = a.G == 1 ? 0 : g;
-      const int len = min(max(a.lens[b * a.G + gr], 0), a.width * kPage);
-      const int np = (len + kPage - 1) / kPage;
       const int p0 = (it - s_off[r]) * chunk;
-      a.ws.items[it] = make_int4(b, g, p0, min(np, p0 + chunk));
+      a.ws.items[it] = make_int4(r / a.Hkv, r % a.Hkv, p0, min(s_np[r], p0 + chunk));
     }
     return;
   }
@@ -183,6 +181,25 @@ struct PartArgs {
 // ------------------------------------------------------------------ bf16 MFMA partial
 // NT row tiles of 16 query rows per wave (rows = GQA group x window, row r is
 // query r / grp of head g*grp + r % grp).
+//
+// Memory pipeline: three page buffers in a ring, so two pages' K/V loads are
+// in flight while the third is consumed; the item's page-table entries are
+// fetched 64 at a time into one lane register each and broadcast with
+// readlane.  The query fragments live in LDS (re-read per page) to keep the
+// register footprint low enough for two waves per SIMD at NT = 2.
+// Online softmax with a lazy reference max: a row's reference only moves
+// when its running max exceeds it by more than 2^8 (log2 units), so the
+// O rescale is skipped wave-wide on almost every page; probabilities stay
+// below 2^8, well inside bf16/fp32 range.  The final (m, l) pair uses the
+// reference, so the merged result is the same softmax.
+constexpr float kLazyRescale = 8.0f;
+
+template <int D>
+struct PageFrag {
+  uint4 k[D / 32];
+  uint2 v[D / 16];
+};
+
 template <int D, int NT>
 __global__ __launch_bounds__(64) void attn_partial_bf16(PartArgs a) {
   const int item = blockIdx.x;
@@ -197,11 +214,40 @@ __global__ __launch_bounds__(64) void attn_partial_bf16(PartArgs a) {
   const int32_t* trow = a.table + (int64_t)(b * a.G + gr) * a.width;
   constexpr int KS = D / 32;  // QK k-steps
   constexpr int NC = D / 16;  // PV dim tiles
-  const uint16_t* qrot = (const uint16_t*)a.qrot;
   const uint16_t* kpool = (const uint16_t*)a.k;
   const uint16_t* vpool = (const uint16_t*)a.v;
+  const int64_t head_off = (int64_t)g * (kPage * D);
+  const int64_t page_stride = (int64_t)a.Hkv * (kPage * D);
+  const int k_lane = l16 * D + 8 * q4;
+  const int v_lane = l16 * kPage + 4 * q4;
 
-  bf16x8 qf[NT][KS];
+  // page-table window: lane j holds trow[wbase + j]
+  int wbase = p0;
+  int tr = (p0 + lane < p1) ? trow[p0 + lane] : 0;
+  auto phys_of = [&](int p) -> int64_t {
+    if (p - wbase >= 64) {  // wave-uniform refill
+      wbase += 64;
+      tr = (wbase + lane < p1) ? trow[wbase + lane] : 0;
+    }
+    return (int64_t)__builtin_amdgcn_readlane(tr, p - wbase);
+  };
+  auto load_page = [&](int p, PageFrag<D>& f) {
+    const int64_t base = phys_of(p) * page_stride + head_off;
+    const uint16_t* kp = kpool + base + k_lane;
+    const uint16_t* vp = vpool + base + v_lane;
+#pragma unroll
+    for (int s = 0; s < KS; ++s) f.k[s] = *(const uint4*)(kp + 32 * s);
+#pragma unroll
+    for (int c = 0; c < NC; ++c) f.v[c] = *(const uint2*)(vp + 16 * kPage * c);
+  };
+
+  PageFrag<D> buf0, buf1, buf2;
+  if (p0 < p1) load_page(p0, buf0);
+  if (p0 + 1 < p1) load_page(p0 + 1, buf1);
+  if (p0 + 2 < p1) load_page(p0 + 2, buf2);
+
+  // query fragments -> LDS (B operand of S^T = K Q^T: row l16, dims 8*q4 + 32*s)
+  __shared__ uint4 sq[NT][KS][64];
   int qpos[NT];
 #pragma unroll
   for (int t = 0; t < NT; ++t) {
@@ -211,15 +257,15 @@ __global__ __launch_bounds__(64) void attn_partial_bf16(PartArgs a) {
       const int i = r / a.grp, hh = r % a.grp;
       const int h = g * a.grp + hh;
       qpos[t] = a.pos[b] + i;
-      const uint16_t* src = qrot + (((int64_t)b * a.q_len + i) * a.Hq + h) * D + 8 * q4;
+      const uint16_t* src = (const uint16_t*)a.qrot + (((int64_t)b * a.q_len + i) * a.Hq + h) * D + 8 * q4;
 #pragma unroll
-      for (int s = 0; s < KS; ++s)
-        qf[t][s] = __builtin_bit_cast(bf16x8, *(const uint4*)(src + 32 * s));
+      for (int s = 0; s < KS; ++s) sq[t][s][lane] = *(const uint4*)(src + 32 * s);
     } else {
 #pragma unroll
-      for (int s = 0; s < KS; ++s) qf[t][s] = __builtin_bit_cast(bf16x8, make_uint4(0, 0, 0, 0));
+      for (int s = 0; s < KS; ++s) sq[t][s][lane] = make_uint4(0, 0, 0, 0);
     }
   }
+  __syncthreads();
 
   floatx4 o[NT][NC];
   float m[NT], l[NT];
@@ -231,49 +277,33 @@ __global__ __launch_bounds__(64) void attn_partial_bf16(PartArgs a) {
     for (int c = 0; c < NC; ++c) o[t][c] = floatx4{0.f, 0.f, 0.f, 0.f};
   }
 
-  // software pipeline: fragments of page p+1 are in flight while page p is used
-  uint4 kf[KS];
-  uint2 vf[NC];
-  auto load_page = [&](int p, uint4* kd, uint2* vd) {
-    const int64_t phys = trow[p];
-    const uint16_t* kp = kpool + (phys * a.Hkv + g) * (int64_t)(kPage * D) + l16 * D + 8 * q4;
-    const uint16_t* vp = vpool + (phys * a.Hkv + g) * (int64_t)(D * kPage) + l16 * kPage + 4 * q4;
-#pragma unroll
-    for (int s = 0; s < KS; ++s) kd[s] = *(const uint4*)(kp + 32 * s);
-#pragma unroll
-    for (int c = 0; c < NC; ++c) vd[c] = *(const uint2*)(vp + 16 * kPage * c);
-  };
-  if (p0 < p1) load_page(p0, kf, vf);
-  for (int p = p0; p < p1; ++p) {
-    uint4 kc[KS];
-    uint2 vc[NC];
-#pragma unroll
-    for (int s = 0; s < KS; ++s) kc[s] = kf[s];
-#pragma unroll
-    for (int c = 0; c < NC; ++c) vc[c] = vf[c];
-    if (p + 1 < p1) load_page(p + 1, kf, vf);
-
+  auto consume = [&](int p, PageFrag<D>& f) {
     const int tok0 = p * kPage + 4 * q4;
     const int nvalid = len - p * kPage;
     if (nvalid < kPage) {  // partial last page: invisible slots may hold anything
 #pragma unroll
       for (int c = 0; c < NC; ++c) {
-        uint32_t lo = vc[c].x, hi = vc[c].y;
+        uint32_t lo = f.v[c].x, hi = f.v[c].y;
         const int j0 = 4 * q4;
         if (j0 + 0 >= nvalid) lo &= 0xffff0000u;
         if (j0 + 1 >= nvalid) lo &= 0x0000ffffu;
         if (j0 + 2 >= nvalid) hi &= 0xffff0000u;
         if (j0 + 3 >= nvalid) hi &= 0x0000ffffu;
-        vc[c] = make_uint2(lo, hi);
+        f.v[c] = make_uint2(lo, hi);
       }
     }
+    // re-read the query fragments from LDS every page (an opaque index keeps
+    // the compiler from hoisting them into registers)
+    int ql = lane;
+    asm volatile("" : "+v"(ql));
 #pragma unroll
     for (int t = 0; t < NT; ++t) {
       floatx4 sacc = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
       for (int s = 0; s < KS; ++s)
-        sacc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, kc[s]),
-                                                      qf[t][s], sacc, 0, 0, 0);
+        sacc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, f.k[s]),
+                                                      __builtin_bit_cast(bf16x8, sq[t][s][ql]),
+                                                      sacc, 0, 0, 0);
       float z[4];
       float mx = -INFINITY;
 #pragma unroll
@@ -284,26 +314,43 @@ __global__ __launch_bounds__(64) void attn_partial_bf16(PartArgs a) {
         mx = fmaxf(mx, z[j]);
       }
       mx = wave_max_xor(mx, 16, 64);
-      const float mn = fmaxf(m[t], mx);
-      const float alpha = (mn == -INFINITY) ? 1.f : exp2f(m[t] - mn);
+      // move the reference only when the running max clears it by kLazyRescale
+      const bool bump = mx > m[t] + kLazyRescale || (m[t] == -INFINITY && mx != -INFINITY);
+      if (__ballot(bump)) {
+        const float mn = bump ? mx : m[t];
+        const float alpha = (m[t] == -INFINITY) ? 0.f : __builtin_amdgcn_exp2f(m[t] - mn);
+        l[t] *= alpha;
+#pragma unroll
+        for (int c = 0; c < NC; ++c) o[t][c] *= alpha;
+        m[t] = mn;
+      }
       float pj[4];
       float psum = 0.f;
 #pragma unroll
       for (int j = 0; j < 4; ++j) {
-        pj[j] = (z[j] == -INFINITY) ? 0.f : exp2f(z[j] - mn);
+        pj[j] = (z[j] == -INFINITY) ? 0.f : __builtin_amdgcn_exp2f(z[j] - m[t]);
         psum += pj[j];
       }
-      l[t] = l[t] * alpha + psum;
-      m[t] = mn;
-      const uint32_t w0 = (uint32_t)f32_to_bf16(pj[0]) | ((uint32_t)f32_to_bf16(pj[1]) << 16);
-      const uint32_t w1 = (uint32_t)f32_to_bf16(pj[2]) | ((uint32_t)f32_to_bf16(pj[3]) << 16);
-      const short4v pf = __builtin_bit_cast(short4v, make_uint2(w0, w1));
+      l[t] += psum;
+      const short4v pf = __builtin_bit_cast(
+          short4v, make_uint2(pack_bf16x2(pj[0], pj[1]), pack_bf16x2(pj[2], pj[3])));
 #pragma unroll
-      for (int c = 0; c < NC; ++c) {
-        o[t][c] *= alpha;
-        o[t][c] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(__builtin_bit_cast(short4v, vc[c]),
+      for (int c = 0; c < NC; ++c)
+        o[t][c] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(__builtin_bit_cast(short4v, f.v[c]),
                                                            pf, o[t][c], 0, 0, 0);
-      }
+    }
+  };
+
+  for (int p = p0; p < p1; p += 3) {
+    consume(p, buf0);
+    if (p + 3 < p1) load_page(p + 3, buf0);
+    if (p + 1 < p1) {
+      consume(p + 1, buf1);
+      if (p + 4 < p1) load_page(p + 4, buf1);
+    }
+    if (p + 2 < p1) {
+      consume(p + 2, buf2);
+      if (p + 5 < p1) load_page(p + 5, buf2);
     }
   }
 #pragma unroll
@@ -493,9 +540,8 @@ __global__ __launch_bounds__(256) void attn_merge_kernel(MergeArgs a) {
   const int64_t orow = ((int64_t)b * a.q_len + i) * a.Hq + h;
   const float inv = L > 0.f ? 1.f / L : 0.f;
   if (a.out_dt == KAP_BF16) {
-    const uint32_t w0 = (uint32_t)f32_to_bf16(O[0] * inv) | ((uint32_t)f32_to_bf16(O[1] * inv) << 16);
-    const uint32_t w1 = (uint32_t)f32_to_bf16(O[2] * inv) | ((uint32_t)f32_to_bf16(O[3] * inv) << 16);
-    *(uint2*)((uint16_t*)a.out + orow * D + d4) = make_uint2(w0, w1);
+    *(uint2*)((uint16_t*)a.out + orow * D + d4) =
+        make_uint2(pack_bf16x2(O[0] * inv, O[1] * inv), pack_bf16x2(O[2] * inv, O[3] * inv));
   } else {
     *(floatx4*)((float*)a.out + orow * D + d4) = O * inv;
   }

@@ -1,0 +1,26 @@
+// Diagnostic: sustained HBM read bandwidth with the load shape the attention
+// kernels use (16-byte loads per lane).  Not part of the attention path; it
+// gives the measured ceiling the attention kernels are compared against.
+#include "kap_internal.h"
+
+namespace kap {
+
+__global__ __launch_bounds__(256) void diag_stream_read_kernel(const uint4* __restrict__ p,
+                                                               size_t n16, uint32_t* sink) {
+  size_t i = (size_t)blockIdx.x * blockDim.x + threadIdx.x;
+  const size_t stride = (size_t)gridDim.x * blockDim.x;
+  uint32_t acc = 0;
+  for (; i < n16; i += stride) {
+    const uint4 v = p[i];
+    acc ^= v.x ^ v.y ^ v.z ^ v.w;
+  }
+  if (acc == 0x9e3779b9u) sink[0] = acc;  // keeps the loads live; practically never taken
+}
+
+kap_status launch_diag_read(const void* buf, size_t bytes, uint32_t* sink, hipStream_t stream) {
+  hipLaunchKernelGGL(diag_stream_read_kernel, dim3(2048), dim3(256), 0, stream,
+                     (const uint4*)buf, bytes / 16, sink);
+  return check_launch("diag read");
+}
+
+}  // namespace kap

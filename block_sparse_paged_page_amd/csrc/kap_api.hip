@@ -264,4 +264,11 @@ kap_status kap_build_summary(const void* k_pool, int32_t kv_dtype, int32_t num_p
                         summary, (kap_dtype)sum_dtype, (hipStream_t)stream);
 }
 
+kap_status kap_diag_stream_read(const void* buf, size_t bytes, uint32_t* sink, kap_stream stream) {
+  g_err[0] = 0;
+  if (!buf || !sink) return fail(KAP_ERR_INVALID_ARG, "null pointer");
+  if (bytes % 16 != 0) return fail(KAP_ERR_INVALID_ARG, "bytes %zu not a multiple of 16", bytes);
+  return launch_diag_read(buf, bytes, sink, (hipStream_t)stream);
+}
+
 }  // extern "C"

@@ -13,7 +13,7 @@ constexpr int kPage = 16;            // tokens per KV page
 constexpr int kTargetItems = 2048;   // split-K work items aimed at per attention call
 constexpr int kMinChunk = 2;         // minimum pages per work item
 constexpr int kMaxSelectPages = 65536;
-constexpr int kMaxPlanRows = 8192;      // batch x KV heads per attention call
+constexpr int kMaxPlanRows = 4096;      // batch x KV heads per attention call
 
 // ---------------------------------------------------------------- device types
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
@@ -30,6 +30,16 @@ __device__ __forceinline__ uint16_t f32_to_bf16(float f) {
   if ((u & 0x7fffffffu) > 0x7f800000u) return (uint16_t)0x7fc0;
   u += 0x7fffu + ((u >> 16) & 1u);
   return (uint16_t)(u >> 16);
+}
+
+typedef __bf16 bf16x2v __attribute__((ext_vector_type(2)));
+typedef float float2v __attribute__((ext_vector_type(2)));
+
+// Two floats -> packed bf16 pair (low half = a), one round-to-nearest-even
+// conversion instruction on gfx950.
+__device__ __forceinline__ uint32_t pack_bf16x2(float a, float b) {
+  const float2v x = {a, b};
+  return __builtin_bit_cast(uint32_t, __builtin_convertvector(x, bf16x2v));
 }
 
 template <typename T>
@@ -118,6 +128,7 @@ kap_status launch_compact(const int32_t* sel, const int32_t* cnt, int32_t B, int
 kap_status launch_summary(const void* k, kap_dtype kv_dt, int32_t Hkv, int32_t D,
                           const int32_t* bt, int32_t max_pages, const int32_t* seq_lens,
                           int32_t B, void* summ, kap_dtype s_dt, hipStream_t stream);
+kap_status launch_diag_read(const void* buf, size_t bytes, uint32_t* sink, hipStream_t stream);
 kap_status launch_proxy(const uint16_t* hidden, const uint16_t* wq, int32_t B, int32_t dm,
                         int32_t n_out, float* q_out, float* partial, int32_t splits,
                         hipStream_t stream);

@@ -237,6 +237,16 @@ KAP_API kap_status kap_build_summary(const void* k_pool, int32_t kv_dtype, int32
                              const int32_t* seq_lens, int32_t B, void* summary,
                              int32_t sum_dtype, kap_stream stream);
 
+/*
+ * Diagnostic, not part of the path: reads `bytes` (a multiple of 16) of device
+ * memory with 16-byte loads from a 2048 x 256 grid-stride kernel, the load
+ * shape of the attention kernels.  Timing it gives the sustained read
+ * bandwidth those kernels are compared against.  sink: device, one uint32
+ * (written only with probability ~2^-32).
+ */
+KAP_API kap_status kap_diag_stream_read(const void* buf, size_t bytes, uint32_t* sink,
+                                        kap_stream stream);
+
 #ifdef __cplusplus
 }
 #endif
