@@ -1,0 +1,217 @@
+"""Parity at the workloads' full sizes, in the launch configuration bench.py times.
+
+K/V are drawn on the GPU by the seeded device generator; the oracle gets host
+copies of exactly the pages and KV head it needs and computes sampled output
+rows (one KV group of one request at a time).  Routing (scores, selection,
+compaction) is checked on every page.
+"""
+import numpy as np
+import pytest
+import torch
+
+import block_sparse_paged_page_amd as kap
+import oracle
+import workloads as W
+from _gpu_util import LSE_TOL, TOL, row_errors
+
+pytestmark = pytest.mark.gpu
+
+
+def _u16(x: torch.Tensor) -> np.ndarray:
+    return x.contiguous().view(torch.int16).cpu().numpy().view(np.uint16)
+
+
+class Big:
+    def __init__(self, w):
+        self.w = w
+        dev = torch.device("cuda:0")
+        self.b = b = W.make_device(w, dev)
+        to = lambda a: torch.from_numpy(np.ascontiguousarray(a)).to(dev)  # noqa: E731
+        self.bt, self.L, self.pos = to(b["bt"]), to(b["seq_lens"]), to(b["positions"])
+        self.anchor, self.recent = to(b["anchor"]), to(b["recent"])
+        if "k_mid" in b:
+            self.k_mid_h = b["k_mid"]
+        else:
+            N = w.n_pages
+            self.k_mid_h = np.array([
+                oracle.budget_from_ratio(int(N[i]), r[0], r[1], int(b["anchor"][i]),
+                                         int(b["recent"][i])) - int(b["anchor"][i]) - int(b["recent"][i])
+                for i, r in enumerate(b["ratio"])], dtype=np.int32)
+        self.k_mid = to(self.k_mid_h)
+        self.q = to(b["q"].view(np.int16))
+        self.qv = to(b["qv"].view(np.int16))
+        self.K, self.V = b["K"], b["V"]
+        self.S = torch.zeros((b["pool_pages"], w.Hkv, w.D), dtype=torch.bfloat16, device=dev)
+        kap.build_summary(self.K, self.bt, self.L, self.S)
+        NA = w.alloc_pages
+        self.starts = np.concatenate([[0], np.cumsum(NA)[:-1]]).astype(np.int64)
+        torch.cuda.synchronize()
+
+    def budget(self):
+        return int((self.b["anchor"] + self.b["recent"] + self.k_mid_h).max())
+
+    def pages(self, bi):
+        NA = self.w.alloc_pages
+        return self.b["phys"][self.starts[bi]:self.starts[bi] + NA[bi]]
+
+    def host_group(self, bi, g):
+        """Request bi's allocated pages of KV head g, local table, oracle summary rows."""
+        ph = torch.from_numpy(self.pages(bi).astype(np.int64)).cuda()
+        Kh = _u16(self.K[ph][:, g:g + 1])
+        Vh = _u16(self.V[ph][:, g:g + 1])
+        btl = np.arange(len(ph), dtype=np.int32)[None]
+        return Kh, Vh, btl
+
+    def host_summary(self, bi):
+        """oracle summary of request bi (all heads), rounded to bf16, local page order."""
+        ph = torch.from_numpy(self.pages(bi).astype(np.int64)).cuda()
+        Kh = _u16(self.K[ph])
+        btl = np.arange(len(ph), dtype=np.int32)[None]
+        s = oracle.summary(Kh, btl, self.b["seq_lens"][bi:bi + 1])
+        return oracle.round_to_bf16(s), btl
+
+
+def _routing(big):
+    """GPU routing vs oracle routing on every page: scores within tolerance,
+    top-K bit-exact on the oracle's scores, compaction bit-exact."""
+    w, b = big.w, big.b
+    cap = big.budget()
+    # both sides score the oracle's summary rows; the GPU summary builder is
+    # checked against them separately (one bf16 rounding apart at most)
+    S_o = torch.zeros_like(big.S)
+    summs = []
+    for bi in range(w.B):
+        summ, btl = big.host_summary(bi)
+        summs.append((summ, btl))
+        ph = torch.from_numpy(big.pages(bi).astype(np.int64)).cuda()
+        n = int(w.n_pages[bi])
+        S_o[ph[:n]] = torch.from_numpy(summ[:n].view(np.int16)).cuda().view(torch.bfloat16)
+        got = oracle.widen(_u16(big.S[ph[:n]]))
+        want = oracle.widen(summ[:n])
+        assert np.all(np.abs(got - want) <= np.abs(want) * 2.0 ** -7 + 1e-30), f"summary, request {bi}"
+    scores = kap.score_blocks(big.q, big.pos, S_o, big.bt, big.L, w.Hkv)
+    torch.cuda.synchronize()
+    s_gpu = scores.cpu().numpy()
+    max_pages = b["bt"].shape[1]
+    s_ref = np.full((w.B, w.Hkv, max_pages), -np.inf)
+    grp = w.Hq // w.Hkv
+    for bi in range(w.B):
+        summ, btl = summs[bi]
+        btl_full = np.full((1, max_pages), -1, np.int32)
+        btl_full[0, :btl.shape[1]] = btl[0]
+        s_ref[bi] = oracle.score(b["q"][bi:bi + 1], b["positions"][bi:bi + 1], summ, btl_full,
+                                 b["seq_lens"][bi:bi + 1], w.Hkv)[0]
+        n = int(w.n_pages[bi])
+        qr = oracle.rope(oracle.widen(b["q"][bi]), float(b["positions"][bi]))
+        un = np.linalg.norm(qr.reshape(w.Hkv, grp, w.D).sum(axis=1), axis=1)
+        rn = np.linalg.norm(oracle.widen(summ[:n]), axis=-1)          # [n][Hkv]
+        bound = 1e-5 * un[:, None] * rn.T + 1e-30
+        assert np.all(np.abs(s_gpu[bi, :, :n] - s_ref[bi, :, :n]) <= bound), f"scores, request {bi}"
+        assert np.all(np.isneginf(s_gpu[bi, :, n:]))
+    s32 = s_ref.astype(np.float32)
+    sel_ref, cnt_ref = oracle.select(s32, b["seq_lens"], b["anchor"], b["recent"], big.k_mid_h, cap,
+                                     per_head=w.per_head)
+    sel, cnt = kap.select_topk(torch.from_numpy(s32).cuda(), big.L, big.anchor, big.recent,
+                               big.k_mid, cap, cap, per_head=w.per_head)
+    torch.cuda.synchronize()
+    np.testing.assert_array_equal(sel.cpu().numpy(), sel_ref)
+    np.testing.assert_array_equal(cnt.cpu().numpy(), cnt_ref)
+    cv = kap.compact_view(sel, cnt, big.bt, big.L, big.pos, 1)
+    torch.cuda.synchronize()
+    r = oracle.compact(sel_ref, cnt_ref, b["bt"], b["seq_lens"], b["positions"], 1)
+    for got, want in zip(cv, r):
+        np.testing.assert_array_equal(got.cpu().numpy(), want)
+    return sel_ref, cnt_ref, cv
+
+
+def _check_rows(big, out, lse, samples, keys_for, qsrc, q_len, start):
+    """Oracle on sampled (request, KV group) pairs: every query row of that group."""
+    w, b = big.w, big.b
+    grp = w.Hq // w.Hkv
+    o = out.view(torch.int16).cpu().numpy().view(np.uint16)
+    lg = lse.cpu().numpy()
+    worst = 0.0
+    for bi, g in samples:
+        Kh, Vh, btl = big.host_group(bi, g)
+        qsub = qsrc[bi:bi + 1, :, g * grp:(g + 1) * grp]
+        ref, lref = oracle.attend(qsub, start[bi:bi + 1], Kh, Vh, btl, [keys_for(bi, g)], 1, 1)
+        got = oracle.widen(o.reshape(w.B, q_len, w.Hq, w.D)[bi, :, g * grp:(g + 1) * grp])
+        e = row_errors(got, ref[0])
+        worst = max(worst, float(e.max()))
+        d = np.abs(lg.reshape(w.B, q_len, w.Hq)[bi, :, g * grp:(g + 1) * grp] - lref[0]).max()
+        assert d <= LSE_TOL["bf16"], (bi, g, d)
+    assert worst <= TOL["bf16"], worst
+    return worst
+
+
+def _attention(big, sel_ref, cnt_ref, cv, samples):
+    w, b = big.w, big.b
+    G = w.Hkv if w.per_head else 1
+    cbt, clog, clen, _ = cv
+    ws = torch.empty(kap.attn_workspace_bytes(w.B, w.q_len, w.Hq, w.Hkv, w.D), dtype=torch.uint8,
+                     device="cuda")
+    lse = torch.empty((w.B, w.Hq), dtype=torch.float32, device="cuda")
+    out = kap.decode_attn(big.q, big.pos, big.K, big.V, cbt, clen, G=G, lse=lse, workspace=ws)
+    torch.cuda.synchronize()
+    keys_sel = oracle.keys_selected(sel_ref, cnt_ref, b["seq_lens"])
+    e1 = _check_rows(big, out, lse, samples,
+                     lambda bi, g: keys_sel[bi * G + (g if G > 1 else 0)],
+                     b["q"][:, None], 1, b["positions"])
+    out = kap.decode_attn(big.q, big.pos, big.K, big.V, big.bt, big.L, G=1, lse=lse, workspace=ws)
+    torch.cuda.synchronize()
+    e2 = _check_rows(big, out, lse, samples,
+                     lambda bi, g: np.arange(int(b["seq_lens"][bi]), dtype=np.int32),
+                     b["q"][:, None], 1, b["positions"])
+    e3 = 0.0
+    if w.q_len > 1:
+        vl = torch.empty((w.B, w.q_len, w.Hq), dtype=torch.float32, device="cuda")
+        vout = kap.verify_attn(big.qv, big.pos, big.K, big.V, big.bt, big.L, lse=vl, workspace=ws)
+        torch.cuda.synchronize()
+        e3 = _check_rows(big, vout, vl, samples,
+                         lambda bi, g: np.arange(int(b["seq_lens"][bi]), dtype=np.int32),
+                         b["qv"], w.q_len, b["positions"])
+    print(f"[{w.name}] sampled max rel err: selected {e1:.2e} full {e2:.2e} verify {e3:.2e}",
+          flush=True)
+
+
+def test_qwen32b_128k_b4_full_size():
+    """The benchmarked configuration: 4 x 131072 tokens, 64/8 heads, s = 451/8192."""
+    big = Big(W.spec("qwen32b_128k", B=4))
+    sel_ref, cnt_ref, cv = _routing(big)
+    assert np.all(cnt_ref == 451)
+    _attention(big, sel_ref, cnt_ref, cv, samples=[(0, 0), (1, 3), (2, 7), (3, 5)])
+
+
+def test_llama8b_32k_b8_full_size():
+    big = Big(W.spec("llama8b_32k"))
+    sel_ref, cnt_ref, cv = _routing(big)
+    assert np.all(cnt_ref == 113)
+    _attention(big, sel_ref, cnt_ref, cv, samples=[(0, 0), (3, 4), (7, 7)])
+
+
+def test_mixed_serving_b64_full_size():
+    """64 ragged requests (4K-128K) scattered over the 1,525,878-page (100 GB) pool."""
+    big = Big(W.spec("mixed_serving"))
+    sel_ref, cnt_ref, cv = _routing(big)
+    L = big.b["seq_lens"]
+    order = np.argsort(L)
+    samples = [(int(order[0]), 0), (int(order[len(order) // 2]), 5), (int(order[-1]), 7)]
+    _attention(big, sel_ref, cnt_ref, cv, samples=samples)
+    del big
+    torch.cuda.empty_cache()
+
+
+def test_early_route_40k_b8_full_size():
+    """Proxy query (4096 x 4096 W_q) -> per-head scores -> per-head top-8 -> decode."""
+    w = W.spec("early_route_40k", B=8)
+    big = Big(w)
+    b = big.b
+    hid, wq = torch.from_numpy(b["hidden"].view(np.int16)).cuda(), torch.from_numpy(b["wq"].view(np.int16)).cuda()
+    qp = kap.proxy_query(hid, wq)
+    torch.cuda.synchronize()
+    qref = oracle.proxy_query(b["hidden"], b["wq"])
+    e = np.abs(qp.cpu().numpy() - qref).max(axis=1) / np.linalg.norm(qref, axis=1)
+    assert e.max() <= 1e-5
+    sel_ref, cnt_ref, cv = _routing(big)
+    assert np.all(cnt_ref == 8)
+    _attention(big, sel_ref, cnt_ref, cv, samples=[(0, 0), (5, 6)])
