@@ -6,7 +6,8 @@ import os
 import torch
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
-_LIB = os.path.join(_HERE, "libkap.so")
+# KAP_LIB may name another build of the same library (e.g. for side-by-side timing)
+_LIB = os.environ.get("KAP_LIB") or os.path.join(_HERE, "libkap.so")
 
 F32, BF16 = 0, 1
 _STATUS = {0: "ok", 1: "invalid argument", 2: "unsupported", 3: "capacity", 4: "workspace",

@@ -1,16 +1,18 @@
 // Split-K paged attention for q = 1 decode and the short verify window.
 //
-// One launch sequence serves both entry points (KAP paper: proposal steps are
+// Two launches serve both entry points (KAP paper: proposal steps are
 // decode-like forwards over the compact view; the verifier scores a short
 // window over the full KV with the original positions):
-//   1. prep   : rotate the queries at their logical positions (fp64 angles) and
-//               build the split-K work plan from the per-row lengths on device
-//               (no host synchronization, so the sequence is graph-capturable).
-//   2. partial: one wave per work item = (request, KV head, chunk of pages,
-//               slice of 32 query rows).  All query rows that share a KV head
-//               (the GQA group times the window) are processed together, so
-//               every K/V byte is read once per item.
-//   3. merge  : log-sum-exp combine of an item's partials in item order.
+//   1. partial: one wave per work item = (request, KV head, chunk of pages,
+//               slice of up to 32 query rows).  Each wave derives its own item
+//               from the per-row lengths on the device (closed-form plan, no
+//               host synchronization, so calls are graph-capturable) and
+//               rotates its own query rows at their logical positions (fp64
+//               angles).  All query rows that share a KV head (the GQA group
+//               times the window) are processed together, so every K/V byte
+//               is read once per item.
+//   2. merge  : log-sum-exp combine of a (request, KV head)'s partials in item
+//               order (deterministic).
 //
 // bf16 path: QK^T and PV run on MFMA.  S^T = K Q^T with
 // v_mfma_f32_16x16x32_bf16 (A = 16 tokens x 32 dims of K straight from the
@@ -41,141 +43,120 @@ AttnWorkspace carve_attn_workspace(void* base, int32_t B, int32_t q_len, int32_t
   };
   w.n_items = (int32_t*)take(sizeof(int32_t));
   w.row_off = (int32_t*)take(sizeof(int32_t) * ((size_t)B * Hkv + 1));
-  w.items = (int4*)take(sizeof(int4) * (size_t)w.max_items);
-  w.qrot = (void*)take(sizeof(float) * (size_t)B * q_len * Hq * D);
   w.part_ml = (float2*)take(sizeof(float2) * (size_t)w.max_items * R);
   w.part_o = (float*)take(sizeof(float) * (size_t)w.max_items * R * D);
   w.bytes = off;
   return w;
 }
 
-struct PrepArgs {
-  const void* q;
-  int32_t q_dt;
-  const int32_t* pos;
-  double log2_theta;
-  int32_t B, q_len, Hq, Hkv, D, G, width;
+// ------------------------------------------------------------------ work plan
+// Rows are (request b, KV head g); row r reads table row (b, g or 0).  A row
+// of np pages is cut into ceil(np / chunk) items of chunk pages, with
+// chunk = max(kMinChunk, ceil(total pages / target)); items are numbered row by
+// row.  target is the number of waves the partial kernel keeps resident on the
+// device (CUs x resident blocks per CU), so a call runs as one round of equal
+// items.  Every wave evaluates this closed form for its own item id, so no
+// separate planning launch is needed.  At most target + rows items.
+struct PlanIn {
   const int32_t* lens;
-  AttnWorkspace ws;
+  int32_t B, Hkv, G, width;
+  int32_t target;  // items aimed at: the kernel's resident-wave capacity (<= kTargetItems)
 };
 
-// ------------------------------------------------------------------ prep
-// Blocks [0, n_rope): one thread per (b, i, h, pair) rotates a pair in fp64.
-// Last block: the split-K plan.
-__global__ __launch_bounds__(256) void attn_prep_kernel(PrepArgs a) {
-  if (blockIdx.x == gridDim.x - 1) {
-    // ---- plan: rows are (b, g); pages per row from the view length.  Row
-    // offsets live in LDS so that item emission (binary search) is cheap.
-    __shared__ int s_off[kMaxPlanRows + 1];
-    __shared__ int s_np[kMaxPlanRows];
-    __shared__ long long s_red[4];
-    __shared__ int s_wsum[4];
-    const int rows = a.B * a.Hkv;
-    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-    long long local = 0;
-    for (int r = tid; r < rows; r += 256) {
-      const int b = r / a.Hkv, g = r % a.Hkv;
-      const int gr = a.G == 1 ? 0 : g;
-      const int len = min(max(a.lens[b * a.G + gr], 0), a.width * kPage);
-      const int np = (len + kPage - 1) / kPage;
-      s_off[r] = np;
-      s_np[r] = np;
-      local += np;
+__device__ __forceinline__ int plan_row_pages(const PlanIn& p, int r) {
+  const int b = r / p.Hkv, g = r % p.Hkv;
+  const int gr = p.G == 1 ? 0 : g;
+  const int len = min(max(p.lens[b * p.G + gr], 0), p.width * kPage);
+  return (len + kPage - 1) / kPage;
+}
+
+constexpr int kPlanCachedTiles = 8;  // rows <= 512 keep their page counts in registers
+
+struct PlanItem {
+  int b, g, p0, p1;
+  bool valid;
+};
+
+// One wave.  If row_off is non-null, also publishes the per-row first item and
+// the item count (done by work item 0 for the merge kernel).
+__device__ PlanItem plan_find(const PlanIn& p, int item, int32_t* row_off, int32_t* n_items) {
+  const int lane = threadIdx.x & 63;
+  const int rows = p.B * p.Hkv;
+  int npc[kPlanCachedTiles];
+  long long local = 0;
+#pragma unroll
+  for (int t = 0; t < kPlanCachedTiles; ++t) {
+    const int r = t * 64 + lane;
+    npc[t] = (r < rows) ? plan_row_pages(p, r) : 0;
+    local += npc[t];
+  }
+  for (int r = kPlanCachedTiles * 64 + lane; r < rows; r += 64) local += plan_row_pages(p, r);
+  for (int o = 32; o > 0; o >>= 1) local += __shfl_xor(local, o);
+  const int chunk = max((int)((local + p.target - 1) / p.target), kMinChunk);
+  PlanItem it{0, 0, 0, 0, false};
+  int carry = 0;
+  for (int base = 0, t = 0; base < rows; base += 64, ++t) {
+    const int r = base + lane;
+    int np = 0;
+    if (t < kPlanCachedTiles) {
+#pragma unroll
+      for (int u = 0; u < kPlanCachedTiles; ++u)
+        if (u == t) np = npc[u];
+    } else if (r < rows) {
+      np = plan_row_pages(p, r);
     }
-    for (int o = 32; o > 0; o >>= 1) local += __shfl_xor(local, o);
-    if (lane == 0) s_red[wave] = local;
-    __syncthreads();
-    const long long total = s_red[0] + s_red[1] + s_red[2] + s_red[3];
-    const int chunk = max((int)((total + kTargetItems - 1) / kTargetItems), kMinChunk);
-    // items per row, then an exclusive scan: thread t owns a contiguous segment
-    const int seg = (rows + 255) / 256;
-    const int r0 = min(tid * seg, rows), r1 = min(r0 + seg, rows);
-    int mine = 0;
-    for (int r = r0; r < r1; ++r) {
-      const int n = (s_off[r] + chunk - 1) / chunk;
-      s_off[r] = n;
-      mine += n;
-    }
-    int x = mine;
+    const int n = (np + chunk - 1) / chunk;
+    int incl = n;
+#pragma unroll
     for (int o = 1; o < 64; o <<= 1) {
-      const int y = __shfl_up(x, o);
-      if (lane >= o) x += y;
+      const int y = __shfl_up(incl, o);
+      if (lane >= o) incl += y;
     }
-    if (lane == 63) s_wsum[wave] = x;
-    __syncthreads();
-    int base = x - mine;
-    for (int w = 0; w < wave; ++w) base += s_wsum[w];
-    for (int r = r0; r < r1; ++r) {
-      const int n = s_off[r];
-      s_off[r] = base;
-      a.ws.row_off[r] = base;
-      base += n;
+    const int excl = carry + incl - n;
+    if (row_off && r < rows) row_off[r] = excl;
+    const uint64_t hit = __ballot(r < rows && item >= excl && item < excl + n);
+    if (hit && !it.valid) {
+      const int src = __ffsll((unsigned long long)hit) - 1;
+      const int rr = base + src;
+      const int j = item - __shfl(excl, src);
+      it.b = rr / p.Hkv;
+      it.g = rr % p.Hkv;
+      it.p0 = j * chunk;
+      it.p1 = min(__shfl(np, src), it.p0 + chunk);
+      it.valid = true;
     }
-    const int n_items = s_wsum[0] + s_wsum[1] + s_wsum[2] + s_wsum[3];
-    if (tid == 0) {
-      s_off[rows] = n_items;
-      a.ws.row_off[rows] = n_items;
-      *a.ws.n_items = n_items;
-    }
-    __syncthreads();
-    for (int it = tid; it < n_items; it += 256) {
-      int lo = 0, hi = rows - 1;
-      while (lo < hi) {
-        const int mid = (lo + hi + 1) >> 1;
-        if (s_off[mid] <= it) lo = mid; else hi = mid - 1;
-      }
-      const int r = lo;
-      const int p0 = (it - s_off[r]) * chunk;
-      a.ws.items[it] = make_int4(r / a.Hkv, r % a.Hkv, p0, min(s_np[r], p0 + chunk));
-    }
-    return;
+    carry += __shfl(incl, 63);
+    if (it.valid && !row_off) break;
   }
-  // ---- RoPE of every query row, rotate-half pairing, fp64 angles
-  const int half = a.D / 2;
-  const long long idx = (long long)blockIdx.x * blockDim.x + threadIdx.x;
-  const long long total = (long long)a.B * a.q_len * a.Hq * half;
-  if (idx >= total) return;
-  const int pair = (int)(idx % half);
-  const long long rowi = idx / half;  // ((b * q_len + i) * Hq + h)
-  const int i = (int)((rowi / a.Hq) % a.q_len);
-  const int b = (int)(rowi / ((long long)a.Hq * a.q_len));
-  const double position = (double)a.pos[b] + (double)i;
-  double s, c;
-  rope_sincos(position, pair, a.D, a.log2_theta, &s, &c);
-  const long long e0 = rowi * a.D + pair, e1 = e0 + half;
-  double x, y;
-  if (a.q_dt == KAP_BF16) {
-    x = bf16_to_f32(((const uint16_t*)a.q)[e0]);
-    y = bf16_to_f32(((const uint16_t*)a.q)[e1]);
-  } else {
-    x = ((const float*)a.q)[e0];
-    y = ((const float*)a.q)[e1];
+  if (row_off && lane == 0) {
+    row_off[rows] = carry;
+    *n_items = carry;
   }
-  const float xr = (float)(x * c - y * s);
-  const float yr = (float)(y * c + x * s);
-  if (a.q_dt == KAP_BF16) {
-    ((uint16_t*)a.ws.qrot)[e0] = f32_to_bf16(xr);
-    ((uint16_t*)a.ws.qrot)[e1] = f32_to_bf16(yr);
-  } else {
-    ((float*)a.ws.qrot)[e0] = xr;
-    ((float*)a.ws.qrot)[e1] = yr;
-  }
+  return it;
+}
+
+// Rotate one query element pair at position `pos`: (x, y) -> (x c - y s, y c + x s).
+__device__ __forceinline__ float2 rope_pair(double x, double y, double s, double c) {
+  return make_float2((float)(x * c - y * s), (float)(y * c + x * s));
 }
 
 struct PartArgs {
-  const void* qrot;
+  const void* q;  // unrotated queries [B][q_len][Hq][D]
   const void* k;
   const void* v;
   const int32_t* table;
   int32_t width, G;
   const int32_t* lens;
   const int32_t* pos;
-  const int4* items;
-  const int32_t* n_items;
+  int32_t B;
+  int32_t* row_off;
+  int32_t* n_items;
   float* part_o;
   float2* part_ml;
   int32_t q_len, Hq, Hkv, grp, R;
   float scale_log2;
+  double log2_theta;
+  int32_t target;
 };
 
 // ------------------------------------------------------------------ bf16 MFMA partial
@@ -202,10 +183,12 @@ struct PageFrag {
 
 template <int D, int NT>
 __global__ __launch_bounds__(64) void attn_partial_bf16(PartArgs a) {
+  const PlanIn pin{a.lens, a.B, a.Hkv, a.G, a.width, a.target};
+  const bool publish = blockIdx.x == 0 && blockIdx.y == 0;
+  const PlanItem it = plan_find(pin, blockIdx.x, publish ? a.row_off : nullptr, a.n_items);
+  if (!it.valid) return;
   const int item = blockIdx.x;
-  if (item >= *a.n_items) return;
-  const int4 it = a.items[item];
-  const int b = it.x, g = it.y, p0 = it.z, p1 = it.w;
+  const int b = it.b, g = it.g, p0 = it.p0, p1 = it.p1;
   const int lane = threadIdx.x;
   const int l16 = lane & 15, q4 = lane >> 4;
   const int row0 = blockIdx.y * 16 * NT;
@@ -246,26 +229,58 @@ __global__ __launch_bounds__(64) void attn_partial_bf16(PartArgs a) {
   if (p0 + 1 < p1) load_page(p0 + 1, buf1);
   if (p0 + 2 < p1) load_page(p0 + 2, buf2);
 
-  // query fragments -> LDS (B operand of S^T = K Q^T: row l16, dims 8*q4 + 32*s)
+  // This slice's query rows, rotated at their positions, as LDS fragments in
+  // the B-operand layout of S^T = K Q^T (row l16, dims 32 s + 8 q4 .. + 7).
+  constexpr int SR = 16 * NT;  // rows per slice
+  __shared__ uint16_t sraw[SR][D];
   __shared__ uint4 sq[NT][KS][64];
   int qpos[NT];
-#pragma unroll
-  for (int t = 0; t < NT; ++t) {
-    const int r = row0 + 16 * t + l16;
-    qpos[t] = -1;
-    if (r < a.R) {
-      const int i = r / a.grp, hh = r % a.grp;
-      const int h = g * a.grp + hh;
-      qpos[t] = a.pos[b] + i;
-      const uint16_t* src = (const uint16_t*)a.qrot + (((int64_t)b * a.q_len + i) * a.Hq + h) * D + 8 * q4;
-#pragma unroll
-      for (int s = 0; s < KS; ++s) sq[t][s][lane] = *(const uint4*)(src + 32 * s);
-    } else {
-#pragma unroll
-      for (int s = 0; s < KS; ++s) sq[t][s][lane] = make_uint4(0, 0, 0, 0);
+  {
+    constexpr int CPR = D / 8;  // 16-byte chunks per row
+    const uint16_t* q = (const uint16_t*)a.q;
+    for (int e = lane; e < SR * CPR; e += 64) {
+      const int rr = e / CPR, c = e % CPR;
+      const int r = row0 + rr;
+      uint4 v = make_uint4(0, 0, 0, 0);
+      if (r < a.R) {
+        const int i = r / a.grp, h = g * a.grp + r % a.grp;
+        v = *(const uint4*)(q + (((int64_t)b * a.q_len + i) * a.Hq + h) * D + 8 * c);
+      }
+      *(uint4*)&sraw[rr][8 * c] = v;
     }
+    __syncthreads();
+    constexpr int HALF = D / 2, LPP = 64 / HALF;
+    const int pr = lane % HALF, rsub = lane / HALF;
+    uint16_t* sqh = (uint16_t*)&sq[0][0][0];
+    auto frag_at = [&](int rr, int dim) {
+      return ((((rr >> 4) * KS + (dim >> 5)) * 64) + (rr & 15) + 16 * ((dim & 31) >> 3)) * 8 +
+             (dim & 7);
+    };
+    int cur = -1;
+    double sn = 0.0, cs = 1.0;
+    for (int rr = rsub; rr < SR; rr += LPP) {
+      const int r = row0 + rr;
+      uint16_t xo = 0, yo = 0;
+      if (r < a.R) {
+        const int i = r / a.grp;
+        if (i != cur) {
+          rope_sincos((double)a.pos[b] + (double)i, pr, D, a.log2_theta, &sn, &cs);
+          cur = i;
+        }
+        const float2 v = rope_pair(bf16_to_f32(sraw[rr][pr]), bf16_to_f32(sraw[rr][pr + HALF]), sn, cs);
+        xo = f32_to_bf16(v.x);
+        yo = f32_to_bf16(v.y);
+      }
+      sqh[frag_at(rr, pr)] = xo;
+      sqh[frag_at(rr, pr + HALF)] = yo;
+    }
+#pragma unroll
+    for (int t = 0; t < NT; ++t) {
+      const int r = row0 + 16 * t + l16;
+      qpos[t] = (r < a.R) ? a.pos[b] + r / a.grp : -1;
+    }
+    __syncthreads();
   }
-  __syncthreads();
 
   floatx4 o[NT][NC];
   float m[NT], l[NT];
@@ -372,10 +387,12 @@ __global__ __launch_bounds__(64) void attn_partial_bf16(PartArgs a) {
 // lane owns (row, token) score pairs, then (row, dim) output pairs.
 template <int D>
 __global__ __launch_bounds__(64) void attn_partial_f32(PartArgs a) {
+  const PlanIn pin{a.lens, a.B, a.Hkv, a.G, a.width, a.target};
+  const bool publish = blockIdx.x == 0 && blockIdx.y == 0;
+  const PlanItem it = plan_find(pin, blockIdx.x, publish ? a.row_off : nullptr, a.n_items);
+  if (!it.valid) return;
   const int item = blockIdx.x;
-  if (item >= *a.n_items) return;
-  const int4 it = a.items[item];
-  const int b = it.x, g = it.y, p0 = it.z, p1 = it.w;
+  const int b = it.b, g = it.g, p0 = it.p0, p1 = it.p1;
   const int lane = threadIdx.x;
   constexpr int RS = 32;                 // rows per slice
   const int row0 = blockIdx.y * RS;
@@ -383,7 +400,7 @@ __global__ __launch_bounds__(64) void attn_partial_f32(PartArgs a) {
   const int gr = a.G == 1 ? 0 : g;
   const int len = a.lens[b * a.G + gr];
   const int32_t* trow = a.table + (int64_t)(b * a.G + gr) * a.width;
-  const float* qrot = (const float*)a.qrot;
+  const float* qin = (const float*)a.q;
   const float* kpool = (const float*)a.k;
   const float* vpool = (const float*)a.v;
 
@@ -393,11 +410,18 @@ __global__ __launch_bounds__(64) void attn_partial_f32(PartArgs a) {
   __shared__ float sp[RS][kPage];
   __shared__ float s_alpha[RS];
   __shared__ int s_qpos[RS];
-  for (int e = lane; e < nr * D; e += 64) {
-    const int rr = e / D, d = e % D;
+  // rotate this slice's query rows (fp64 angles) straight into LDS
+  constexpr int HALF = D / 2;
+  for (int e = lane; e < nr * HALF; e += 64) {
+    const int rr = e / HALF, pr = e % HALF;
     const int r = row0 + rr;
     const int i = r / a.grp, h = g * a.grp + r % a.grp;
-    sq[rr][d] = qrot[(((int64_t)b * a.q_len + i) * a.Hq + h) * D + d];
+    double sn, cs;
+    rope_sincos((double)a.pos[b] + (double)i, pr, D, a.log2_theta, &sn, &cs);
+    const float* src = qin + (((int64_t)b * a.q_len + i) * a.Hq + h) * D;
+    const float2 v = rope_pair(src[pr], src[pr + HALF], sn, cs);
+    sq[rr][pr] = v.x;
+    sq[rr][pr + HALF] = v.y;
   }
   if (lane < nr) s_qpos[lane] = a.pos[b] + (row0 + lane) / a.grp;
   constexpr int DPL = (D + 63) / 64;     // dims per lane
@@ -553,28 +577,8 @@ __global__ __launch_bounds__(256) void attn_merge_kernel(MergeArgs a) {
 kap_status launch_attention(const AttnCall& c) {
   const int grp = c.Hq / c.Hkv;
   const int R = grp * c.q_len;
-  PrepArgs pa{};
-  pa.q = c.q;
-  pa.q_dt = c.dtype;
-  pa.pos = c.positions;
-  pa.log2_theta = log2((double)c.theta);
-  pa.B = c.B;
-  pa.q_len = c.q_len;
-  pa.Hq = c.Hq;
-  pa.Hkv = c.Hkv;
-  pa.D = c.D;
-  pa.G = c.G;
-  pa.width = c.width;
-  pa.lens = c.lens;
-  pa.ws = c.ws;
-  const long long pairs = (long long)c.B * c.q_len * c.Hq * (c.D / 2);
-  const int n_rope = (int)((pairs + 255) / 256);
-  hipLaunchKernelGGL(attn_prep_kernel, dim3(n_rope + 1), dim3(256), 0, c.stream, pa);
-  kap_status st = check_launch("attention prep");
-  if (st != KAP_OK) return st;
-
   PartArgs a{};
-  a.qrot = c.ws.qrot;
+  a.q = c.q;
   a.k = c.k;
   a.v = c.v;
   a.table = c.table;
@@ -582,7 +586,8 @@ kap_status launch_attention(const AttnCall& c) {
   a.G = c.G;
   a.lens = c.lens;
   a.pos = c.positions;
-  a.items = c.ws.items;
+  a.B = c.B;
+  a.row_off = c.ws.row_off;
   a.n_items = c.ws.n_items;
   a.part_o = c.ws.part_o;
   a.part_ml = c.ws.part_ml;
@@ -592,23 +597,25 @@ kap_status launch_attention(const AttnCall& c) {
   a.grp = grp;
   a.R = R;
   a.scale_log2 = c.scale * 1.4426950408889634f;
+  a.log2_theta = log2((double)c.theta);
+  const void* fn;
+  int slices;
   if (c.dtype == KAP_BF16) {
     const int nt = R <= 16 ? 1 : 2;
-    const int slices = (R + 16 * nt - 1) / (16 * nt);
-    dim3 grid(c.ws.max_items, slices);
-    if (c.D == 128) {
-      if (nt == 1) hipLaunchKernelGGL((attn_partial_bf16<128, 1>), grid, dim3(64), 0, c.stream, a);
-      else hipLaunchKernelGGL((attn_partial_bf16<128, 2>), grid, dim3(64), 0, c.stream, a);
-    } else {
-      if (nt == 1) hipLaunchKernelGGL((attn_partial_bf16<64, 1>), grid, dim3(64), 0, c.stream, a);
-      else hipLaunchKernelGGL((attn_partial_bf16<64, 2>), grid, dim3(64), 0, c.stream, a);
-    }
+    slices = (R + 16 * nt - 1) / (16 * nt);
+    if (c.D == 128) fn = nt == 1 ? (const void*)attn_partial_bf16<128, 1> : (const void*)attn_partial_bf16<128, 2>;
+    else fn = nt == 1 ? (const void*)attn_partial_bf16<64, 1> : (const void*)attn_partial_bf16<64, 2>;
   } else {
-    dim3 grid(c.ws.max_items, (R + 31) / 32);
-    if (c.D == 128) hipLaunchKernelGGL((attn_partial_f32<128>), grid, dim3(64), 0, c.stream, a);
-    else hipLaunchKernelGGL((attn_partial_f32<64>), grid, dim3(64), 0, c.stream, a);
+    slices = (R + 31) / 32;
+    fn = c.D == 128 ? (const void*)attn_partial_f32<128> : (const void*)attn_partial_f32<64>;
   }
-  st = check_launch("attention partial");
+  // one round of resident waves, shared among the row slices
+  a.target = max(1, min(kTargetItems, resident_blocks(fn, 64) / slices));
+  void* args[] = {&a};
+  const int max_items = a.target + c.B * c.Hkv;  // the plan never makes more
+  const hipError_t e = hipLaunchKernel(fn, dim3(max_items, slices), dim3(64), args, 0, c.stream);
+  if (e != hipSuccess) return fail(KAP_ERR_HIP, "attention partial: %s", hipGetErrorString(e));
+  kap_status st = check_launch("attention partial");
   if (st != KAP_OK) return st;
 
   MergeArgs ma{};

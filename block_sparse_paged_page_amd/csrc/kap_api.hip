@@ -4,6 +4,8 @@
 #include <stdio.h>
 #include <string.h>
 
+#include <atomic>
+
 #include "kap_internal.h"
 
 namespace kap {
@@ -32,6 +34,39 @@ kap_status check_launch(const char* what) {
 }
 
 static bool dtype_ok(int32_t d) { return d == KAP_F32 || d == KAP_BF16; }
+
+// Blocks of `kernel` the current device keeps resident at once (CUs x blocks per
+// CU), cached per (device, kernel).  The only state the library keeps.
+int resident_blocks(const void* kernel, int block_threads) {
+  struct Entry {
+    std::atomic<const void*> fn;
+    std::atomic<int> dev, value;
+  };
+  static Entry cache[64];
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess) dev = 0;
+  for (auto& e : cache) {
+    const void* f = e.fn.load(std::memory_order_acquire);
+    if (f == nullptr) break;
+    if (f == kernel && e.dev.load(std::memory_order_relaxed) == dev) return e.value.load();
+  }
+  int cus = 0, per_cu = 0;
+  if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess ||
+      hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, kernel, block_threads, 0) != hipSuccess ||
+      cus <= 0 || per_cu <= 0) {
+    (void)hipGetLastError();
+    return kTargetItems;
+  }
+  const int value = cus * per_cu;
+  static std::atomic<int> next{0};
+  const int slot = next.fetch_add(1);
+  if (slot < 64) {
+    cache[slot].dev.store(dev);
+    cache[slot].value.store(value);
+    cache[slot].fn.store(kernel, std::memory_order_release);
+  }
+  return value;
+}
 
 static kap_status check_heads(int32_t Hq, int32_t Hkv, int32_t D, int32_t page_size) {
   if (Hq <= 0 || Hkv <= 0) return fail(KAP_ERR_INVALID_ARG, "Hq=%d Hkv=%d must be > 0", Hq, Hkv);

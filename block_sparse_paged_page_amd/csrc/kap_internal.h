@@ -75,16 +75,15 @@ __device__ __forceinline__ float wave_max_xor(float v, int from, int to) {
 void set_error(const char* fmt, ...);
 kap_status fail(kap_status s, const char* fmt, ...);
 kap_status check_launch(const char* what);
+int resident_blocks(const void* kernel, int block_threads);
 
 inline size_t align_up(size_t x, size_t a) { return (x + a - 1) / a * a; }
 
 // Workspace carving for the attention calls (decode and verify share it).
 struct AttnWorkspace {
   int32_t* n_items;     // [1]
-  int32_t* row_off;     // [B*Hkv + 1]
-  int4* items;          // [max_items] (b, g, page_begin, page_end)
-  void* qrot;           // [B][q_len][Hq][D] (bf16 or f32)
-  float2* part_ml;      // [max_items][R] (running max in log2 units, sum)
+  int32_t* row_off;     // [B*Hkv + 1] first work item of each (b, g)
+  float2* part_ml;      // [max_items][R] (reference max in log2 units, sum)
   float* part_o;        // [max_items][R][D]
   int32_t max_items;
   size_t bytes;
