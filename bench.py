@@ -48,6 +48,10 @@ def parse():
     ap.add_argument("--layers", type=int, default=0, help="layer copies (0: auto)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--quiet", action="store_true")
+    ap.add_argument("--workload", default="qwen32b_128k",
+                    choices=["qwen32b_128k", "llama8b_32k", "early_route_40k", "mixed_serving"],
+                    help="qwen32b_128k is the headline line; the others print their own "
+                         "measurement lines")
     return ap.parse_args()
 
 
@@ -139,6 +143,283 @@ def cpu_baseline(w, b, K, V, sel_budget, quiet, min_s=10.0, max_s=30.0):
                         f"pages and one 4-query verify over 131072 tokens; {dt:.1f} s of CPU time"))
 
 
+def time_call(fn, reps, stream, warm=3):
+    """Median duration (us) of fn() over reps launches, HIP events on `stream`."""
+    for _ in range(warm):
+        fn()
+    ev = [torch.cuda.Event(enable_timing=True) for _ in range(reps + 1)]
+    ev[0].record(stream)
+    for i in range(reps):
+        fn()
+        ev[i + 1].record(stream)
+    torch.cuda.synchronize()
+    return float(np.median([ev[i].elapsed_time(ev[i + 1]) for i in range(reps)])) * 1e3
+
+
+def _upload(b, dev):
+    to = lambda a: torch.from_numpy(np.ascontiguousarray(a)).to(dev)  # noqa: E731
+    return to
+
+
+def run_llama_sweep(args, dev):
+    """Llama-3-8B-shaped attention at 32K, batch 8: every routing call, the
+    selected (s = 113/2048) and full decodes, and decode time across retention
+    s in {1, 2, 5.5, 10, 25, 50, 100} % with a linear fit T(s) = T0 + s T1."""
+    w = W.spec("llama8b_32k")
+    B, Hq, Hkv, D = w.B, w.Hq, w.Hkv, w.D
+    b = W.make_device(w, dev)
+    to = _upload(b, dev)
+    bt, L, pos = to(b["bt"]), to(b["seq_lens"]), to(b["positions"])
+    anchor, recent = to(b["anchor"]), to(b["recent"])
+    q = to(b["q"].view(np.int16)).view(torch.bfloat16)
+    S = torch.zeros((b["pool_pages"], Hkv, D), dtype=torch.bfloat16, device=dev)
+    kap.build_summary(b["K"], bt, L, S)
+    layer_bytes = 2 * b["K"].numel() * EB
+    R = max(4, int(math.ceil(8 * 2**30 / layer_bytes)))
+    Ks = [b["K"]] + [b["K"].clone() for _ in range(R - 1)]
+    Vs = [b["V"]] + [b["V"].clone() for _ in range(R - 1)]
+    Ss = [S] + [S.clone() for _ in range(R - 1)]
+    torch.cuda.synchronize()
+    st = torch.cuda.current_stream()
+    ws = torch.empty(kap.attn_workspace_bytes(B, 1, Hq, Hkv, D), dtype=torch.uint8, device=dev)
+    out = torch.empty_like(q)
+    N = int(w.n_pages[0])
+    cnt_l = {"i": 0}
+
+    def lay():
+        cnt_l["i"] += 1
+        return cnt_l["i"] % R
+
+    scores = kap.score_blocks(q, pos, S, bt, L, Hkv)
+    kmid = to(b["k_mid"])
+    budget = int((b["anchor"] + b["recent"] + b["k_mid"]).max())
+    sel, cnt = kap.select_topk(scores, L, anchor, recent, kmid, budget, budget)
+    cv = kap.compact_view(sel, cnt, bt, L, pos, 1)
+    res = {}
+    res["score_us"] = time_call(lambda: kap.score_blocks(q, pos, Ss[lay()], bt, L, Hkv, scores=scores),
+                                args.steps, st)
+    res["select_us"] = time_call(lambda: kap.select_topk(scores, L, anchor, recent, kmid, budget,
+                                                         budget, sel=sel, cnt=cnt), args.steps, st)
+    res["compact_us"] = time_call(lambda: kap.compact_view(sel, cnt, bt, L, pos, 1, out=cv),
+                                  args.steps, st)
+    kv_tok = Hkv * 2 * D * EB
+    sweep = []
+    for num, den in ((1, 100), (2, 100), (55, 1000), (10, 100), (25, 100), (50, 100), (1, 1)):
+        bud = kap.budget_from_ratio(N, num, den, 1, 2)
+        km = torch.full((B,), bud - 3, dtype=torch.int32, device=dev)
+        sl, ct = kap.select_topk(scores, L, anchor, recent, km, bud, bud)
+        cb = kap.compact_view(sl, ct, bt, L, pos, 1)
+        us = time_call(lambda: kap.decode_attn(q, pos, Ks[lay()], Vs[lay()], cb[0], cb[2], out=out,
+                                               workspace=ws), args.steps, st)
+        nbytes = B * bud * 16 * kv_tok
+        sweep.append({"s": round(num / den, 4), "pages": bud, "us": round(us, 2),
+                      "GBps": round(nbytes / (us * 1e-6) / 1e9, 1)})
+    full_us = time_call(lambda: kap.decode_attn(q, pos, Ks[lay()], Vs[lay()], bt, L, out=out,
+                                                workspace=ws), args.steps, st)
+    xs = np.array([d["pages"] / N for d in sweep])
+    ys = np.array([d["us"] for d in sweep])
+    A = np.stack([np.ones_like(xs), xs], axis=1)
+    coef, *_ = np.linalg.lstsq(A, ys, rcond=None)
+    pred = A @ coef
+    r2 = 1 - ((ys - pred) ** 2).sum() / ((ys - ys.mean()) ** 2).sum()
+    sel_us = [d for d in sweep if d["pages"] == budget][0]["us"]
+    print(json.dumps({
+        "metric": METRIC, "workload": "llama8b_32k: B=8, Hq=32, Hkv=8, D=128, 32768-token "
+        "context, s=113/2048 (A1R2K110 pooled)", "unit": "tokens/s",
+        "value": round(B / (sel_us * 1e-6), 1), "dtype": "bf16", "data": "synthetic",
+        "layer_copies": R, "kernels": {k: round(v, 2) for k, v in res.items()},
+        "decode_selected_us": sel_us, "decode_full_us": round(full_us, 2),
+        "decode_full_GBps": round(B * int(w.seq_lens[0]) * kv_tok / (full_us * 1e-6) / 1e9, 1),
+        "selected_vs_full_decode_speedup": round(full_us / sel_us, 3),
+        "s_sweep": sweep,
+        "fit": {"T0_us": round(float(coef[0]), 2), "T_full_us": round(float(coef[1]), 2),
+                "r2": round(float(r2), 5), "T(100%)/T(full table)": round(ys[-1] / full_us, 4)},
+    }), flush=True)
+
+
+def run_early_route(args, dev):
+    """Early routing over 32 layers (40K inputs, per-head top-8 pages): the side
+    flow (proxy GEMV -> per-head scores -> top-8 -> compact) for layer l+1 runs on
+    a second stream while the main flow decodes layer l; compared with the same
+    work serialized on one stream."""
+    w = W.spec("early_route_40k", B=args.batch if args.batch != 4 else 8)
+    B, Hq, Hkv, D = w.B, w.Hq, w.Hkv, w.D
+    layers = 32
+    b = W.make_device(w, dev)
+    to = _upload(b, dev)
+    bt, L, pos = to(b["bt"]), to(b["seq_lens"]), to(b["positions"])
+    anchor, recent, kmid = to(b["anchor"]), to(b["recent"]), to(b["k_mid"])
+    S = torch.zeros((b["pool_pages"], Hkv, D), dtype=torch.bfloat16, device=dev)
+    kap.build_summary(b["K"], bt, L, S)
+    g = torch.Generator(device=dev)
+    g.manual_seed(int(w.seed) * 7919)
+    Ks = [b["K"]] + [b["K"].clone() for _ in range(layers - 1)]
+    Vs = [b["V"]] + [b["V"].clone() for _ in range(layers - 1)]
+    Ss = [S] + [S.clone() for _ in range(layers - 1)]
+    Wq = [(torch.randn((w.hidden_dim, Hq * D), generator=g, device=dev) / 64.0).bfloat16()
+          for _ in range(layers)]
+    hid = [torch.randn((B, w.hidden_dim), generator=g, device=dev).bfloat16() for _ in range(layers)]
+    qreal = [torch.randn((B, Hq, D), generator=g, device=dev).bfloat16() for _ in range(layers)]
+    torch.cuda.synchronize()
+    cap = 8
+    views = [(torch.empty((B, Hkv, cap), dtype=torch.int32, device=dev),
+              torch.empty((B, Hkv, cap), dtype=torch.int32, device=dev),
+              torch.empty((B, Hkv), dtype=torch.int32, device=dev),
+              torch.empty((B, 1), dtype=torch.int64, device=dev)) for _ in range(layers)]
+    qp = torch.empty((B, Hq * D), dtype=torch.float32, device=dev)
+    pws = torch.empty(kap.proxy_workspace_bytes(B, w.hidden_dim, Hq * D), dtype=torch.uint8, device=dev)
+    scores = torch.empty((B, Hkv, bt.shape[1]), dtype=torch.float32, device=dev)
+    sel = torch.empty((B, Hkv, cap), dtype=torch.int32, device=dev)
+    cnt = torch.empty((B, Hkv), dtype=torch.int32, device=dev)
+    aws = torch.empty(kap.attn_workspace_bytes(B, 1, Hq, Hkv, D), dtype=torch.uint8, device=dev)
+    out = torch.empty((B, Hq, D), dtype=torch.bfloat16, device=dev)
+
+    def route(l, s):
+        src = hid[l - 1] if l > 0 else hid[0]
+        kap.proxy_query(src, Wq[l], q_out=qp, workspace=pws, stream=s)
+        kap.score_blocks(qp.view(B, Hq, D), pos, Ss[l], bt, L, Hkv, scores=scores, stream=s)
+        kap.select_topk(scores, L, anchor, recent, kmid, cap, cap, per_head=True, sel=sel, cnt=cnt,
+                        stream=s)
+        kap.compact_view(sel, cnt, bt, L, pos, 1, out=views[l], stream=s)
+
+    def decode(l, s):
+        kap.decode_attn(qreal[l], pos, Ks[l], Vs[l], views[l][0], views[l][2], G=Hkv, out=out,
+                        workspace=aws, stream=s)
+
+    main = torch.cuda.current_stream()
+    side = torch.cuda.Stream(device=dev)  # default priority
+
+    def serialized():
+        cur = torch.cuda.current_stream()  # the capture stream while a graph is recorded
+        for l in range(layers):
+            route(l, cur)
+            decode(l, cur)
+
+    def overlapped():
+        cur = torch.cuda.current_stream()
+        done = [torch.cuda.Event() for _ in range(layers)]
+        side.wait_stream(cur)
+        route(0, side)
+        done[0].record(side)
+        for l in range(layers):
+            if l + 1 < layers:
+                route(l + 1, side)
+                done[l + 1].record(side)
+            cur.wait_event(done[l])
+            decode(l, cur)
+        cur.wait_stream(side)
+
+    def wall(fn, reps):
+        """Median GPU time of the 32-layer sequence replayed from a HIP graph, so that
+        host launch overhead does not hide the overlap."""
+        for _ in range(2):
+            fn()
+        torch.cuda.synchronize()
+        graph = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(graph):
+            fn()
+        torch.cuda.synchronize()
+        ts = []
+        for _ in range(reps):
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record(main)
+            graph.replay()
+            e1.record(main)
+            torch.cuda.synchronize()
+            ts.append(e0.elapsed_time(e1))
+        return float(np.median(ts)) * 1e3
+
+    reps = max(5, args.steps // 5)
+    t_ser = wall(serialized, reps)
+    t_ovl = wall(overlapped, reps)
+    parts = {
+        "proxy_gemv": time_call(lambda: kap.proxy_query(hid[4], Wq[5], q_out=qp, workspace=pws), args.steps, main),
+        "score": time_call(lambda: kap.score_blocks(qp.view(B, Hq, D), pos, Ss[5], bt, L, Hkv, scores=scores), args.steps, main),
+        "select": time_call(lambda: kap.select_topk(scores, L, anchor, recent, kmid, cap, cap, per_head=True, sel=sel, cnt=cnt), args.steps, main),
+        "compact": time_call(lambda: kap.compact_view(sel, cnt, bt, L, pos, 1, out=views[5]), args.steps, main),
+    }
+    t_route = time_call(lambda: route(5, main), args.steps, main)
+    t_dec = time_call(lambda: decode(5, main), args.steps, main)
+    hidden = (t_ser - t_ovl) / (layers * min(t_route, t_dec))
+    print(json.dumps({
+        "metric": METRIC, "workload": f"early_route_40k: B={B}, Hq=32, Hkv=8, D=128, 40000-token "
+        "inputs, per-head top-8 pages (128 tokens), proxy query 4096x4096 bf16 W_q, 32 layers",
+        "unit": "tokens/s", "value": round(B / (t_ovl * 1e-6), 1), "dtype": "bf16",
+        "data": "synthetic", "layers": layers,
+        "wall_us_32_layers": {"serialized": round(t_ser, 1), "overlapped": round(t_ovl, 1)},
+        "per_layer_us": {"route_side_flow": round(t_route, 2), "decode_main_flow": round(t_dec, 2),
+                         **{k: round(v, 2) for k, v in parts.items()}},
+        "proxy_gemv_GBps": round(w.hidden_dim * Hq * D * 2 / (parts["proxy_gemv"] * 1e-6) / 1e9, 1),
+        "timing": "32-layer sequences replayed from HIP graphs (both streams captured)",
+        "overlap_efficiency": round(hidden, 3),
+        "note": "efficiency = time saved / (layers x shorter flow per layer)",
+    }), flush=True)
+
+
+def run_mixed(args, dev):
+    """Mixed serving batch: 64 ragged requests (4K-128K, log-uniform) with
+    per-request retention {1, 5.5, 25, 100} % and A1R2/A4R4 splits, pages
+    scattered over a 1,525,878-page (100 GB) pool: one ragged decode launch."""
+    w = W.spec("mixed_serving")
+    B, Hq, Hkv, D = w.B, w.Hq, w.Hkv, w.D
+    b = W.make_device(w, dev)
+    to = _upload(b, dev)
+    bt, L, pos = to(b["bt"]), to(b["seq_lens"]), to(b["positions"])
+    anchor, recent = to(b["anchor"]), to(b["recent"])
+    N = w.n_pages
+    budgets = np.array([kap.budget_from_ratio(int(N[i]), r[0], r[1], int(b["anchor"][i]),
+                                              int(b["recent"][i])) for i, r in enumerate(b["ratio"])])
+    kmid = to((budgets - b["anchor"] - b["recent"]).astype(np.int32))
+    cap = int(budgets.max())
+    q = to(b["q"].view(np.int16)).view(torch.bfloat16)
+    S = torch.zeros((b["pool_pages"], Hkv, D), dtype=torch.bfloat16, device=dev)
+    kap.build_summary(b["K"], bt, L, S)
+    st = torch.cuda.current_stream()
+    scores = torch.empty((B, Hkv, bt.shape[1]), dtype=torch.float32, device=dev)
+    sel = torch.empty((B, 1, cap), dtype=torch.int32, device=dev)
+    cnt = torch.empty((B, 1), dtype=torch.int32, device=dev)
+    cv = (torch.empty((B, 1, cap), dtype=torch.int32, device=dev),
+          torch.empty((B, 1, cap), dtype=torch.int32, device=dev),
+          torch.empty((B, 1), dtype=torch.int32, device=dev),
+          torch.empty((B, 1), dtype=torch.int64, device=dev))
+    ws = torch.empty(kap.attn_workspace_bytes(B, 1, Hq, Hkv, D), dtype=torch.uint8, device=dev)
+    out = torch.empty_like(q)
+
+    def route():
+        kap.score_blocks(q, pos, S, bt, L, Hkv, scores=scores)
+        kap.select_topk(scores, L, anchor, recent, kmid, cap, cap, sel=sel, cnt=cnt)
+        kap.compact_view(sel, cnt, bt, L, pos, 1, out=cv)
+
+    route()
+    torch.cuda.synchronize()
+    t_route = time_call(route, args.steps, st)
+    t_sel = time_call(lambda: kap.decode_attn(q, pos, b["K"], b["V"], cv[0], cv[2], out=out,
+                                              workspace=ws), args.steps, st)
+    t_full = time_call(lambda: kap.decode_attn(q, pos, b["K"], b["V"], bt, L, out=out,
+                                               workspace=ws), args.steps, st)
+    clen = cv[2].cpu().numpy()[:, 0].astype(np.int64)
+    kv_tok = Hkv * 2 * D * EB
+    sel_bytes = int(clen.sum()) * kv_tok
+    full_bytes = int(b["seq_lens"].astype(np.int64).sum()) * kv_tok
+    pages = (clen + 15) // 16
+    print(json.dumps({
+        "metric": METRIC, "workload": "mixed_serving: B=64, Hq=32, Hkv=8, D=128, contexts "
+        "log-uniform 4K-128K, s in {1, 5.5, 25, 100} %, A1R2/A4R4, 100 GB pool",
+        "unit": "tokens/s", "value": round(B / (t_sel * 1e-6), 1), "dtype": "bf16",
+        "data": "synthetic",
+        "route_us": round(t_route, 2),
+        "decode_selected_us": round(t_sel, 2), "decode_selected_bytes": sel_bytes,
+        "decode_selected_GBps": round(sel_bytes / (t_sel * 1e-6) / 1e9, 1),
+        "decode_full_us": round(t_full, 2), "decode_full_bytes": full_bytes,
+        "decode_full_GBps": round(full_bytes / (t_full * 1e-6) / 1e9, 1),
+        "s_meas_bytes": round(sel_bytes / full_bytes, 4),
+        "selected_pages_per_request": {"min": int(pages.min()), "mean": round(float(pages.mean()), 1),
+                                       "max": int(pages.max())},
+        "context_tokens": {"min": int(b["seq_lens"].min()), "mean": round(float(b["seq_lens"].mean()), 1),
+                           "max": int(b["seq_lens"].max())},
+    }), flush=True)
+
+
 def main():
     args = parse()
     if args.gpus != 1:
@@ -150,6 +431,10 @@ def main():
     q = args.quiet
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
+    if args.workload != "qwen32b_128k":
+        {"llama8b_32k": run_llama_sweep, "early_route_40k": run_early_route,
+         "mixed_serving": run_mixed}[args.workload](args, dev)
+        return
     w = W.spec("qwen32b_128k", B=args.batch)
     B, Hq, Hkv, D = w.B, w.Hq, w.Hkv, w.D
     t0 = time.time()

@@ -52,8 +52,8 @@ AttnWorkspace carve_attn_workspace(void* base, int32_t B, int32_t q_len, int32_t
 // ------------------------------------------------------------------ work plan
 // Rows are (request b, KV head g); row r reads table row (b, g or 0).  A row
 // of np pages is cut into ceil(np / chunk) items of chunk pages, with
-// chunk = max(kMinChunk, ceil(total pages / target)); items are numbered row by
-// row.  target is the number of waves the partial kernel keeps resident on the
+// chunk = max(kMinChunk, ceil(total pages / max(target - rows, target / 2)));
+// items are numbered row by row.  target is the number of waves the partial kernel keeps resident on the
 // device (CUs x resident blocks per CU), so a call runs as one round of equal
 // items.  Every wave evaluates this closed form for its own item id, so no
 // separate planning launch is needed.  At most target + rows items.
@@ -92,7 +92,10 @@ __device__ PlanItem plan_find(const PlanIn& p, int item, int32_t* row_off, int32
   }
   for (int r = kPlanCachedTiles * 64 + lane; r < rows; r += 64) local += plan_row_pages(p, r);
   for (int o = 32; o > 0; o >>= 1) local += __shfl_xor(local, o);
-  const int chunk = max((int)((local + p.target - 1) / p.target), kMinChunk);
+  // every row may end in a partial item, so aim at target - rows full items
+  // (at least target / 2) to keep the whole plan within one resident round
+  const int aim = max(p.target - rows, max(p.target / 2, 1));
+  const int chunk = max((int)((local + aim - 1) / aim), kMinChunk);
   PlanItem it{0, 0, 0, 0, false};
   int carry = 0;
   for (int base = 0, t = 0; base < rows; base += 64, ++t) {

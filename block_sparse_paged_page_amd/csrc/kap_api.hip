@@ -123,7 +123,7 @@ kap_status kap_score_blocks(const void* q, int32_t q_dtype, const int32_t* posit
 
 size_t kap_proxy_workspace_bytes(int32_t B, int32_t d_model, int32_t n_out) {
   if (B <= 0 || d_model <= 0 || n_out <= 0) return 0;
-  return (size_t)(d_model / 512) * B * n_out * sizeof(float);
+  return (size_t)proxy_splits(d_model) * B * n_out * sizeof(float);
 }
 
 kap_status kap_proxy_query(const void* hidden, const void* w_q, int32_t B, int32_t d_model,
@@ -131,16 +131,16 @@ kap_status kap_proxy_query(const void* hidden, const void* w_q, int32_t B, int32
                            kap_stream stream) {
   g_err[0] = 0;
   if (B <= 0 || B > 16) return fail(KAP_ERR_UNSUPPORTED, "proxy batch %d (1..16)", B);
-  if (d_model <= 0 || d_model % 512 != 0)
-    return fail(KAP_ERR_UNSUPPORTED, "d_model %d (multiple of 512)", d_model);
-  if (n_out <= 0 || n_out % 64 != 0)
-    return fail(KAP_ERR_UNSUPPORTED, "n_out %d (multiple of 64)", n_out);
+  if (d_model <= 0 || d_model % 128 != 0)
+    return fail(KAP_ERR_UNSUPPORTED, "d_model %d (multiple of 128)", d_model);
+  if (n_out <= 0 || n_out % 512 != 0)
+    return fail(KAP_ERR_UNSUPPORTED, "n_out %d (multiple of 512)", n_out);
   if (!hidden || !w_q || !q_out) return fail(KAP_ERR_INVALID_ARG, "null pointer");
   const size_t need = kap_proxy_workspace_bytes(B, d_model, n_out);
   if (!workspace || workspace_bytes < need)
     return fail(KAP_ERR_WORKSPACE, "proxy workspace %zu < %zu bytes", workspace_bytes, need);
   return launch_proxy((const uint16_t*)hidden, (const uint16_t*)w_q, B, d_model, n_out, q_out,
-                      (float*)workspace, d_model / 512, (hipStream_t)stream);
+                      (float*)workspace, proxy_splits(d_model), (hipStream_t)stream);
 }
 
 kap_status kap_select_topk(const float* scores, int32_t B, int32_t Hkv, int32_t max_pages,

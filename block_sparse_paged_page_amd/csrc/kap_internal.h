@@ -127,6 +127,7 @@ kap_status launch_compact(const int32_t* sel, const int32_t* cnt, int32_t B, int
 kap_status launch_summary(const void* k, kap_dtype kv_dt, int32_t Hkv, int32_t D,
                           const int32_t* bt, int32_t max_pages, const int32_t* seq_lens,
                           int32_t B, void* summ, kap_dtype s_dt, hipStream_t stream);
+int proxy_splits(int d_model);
 kap_status launch_diag_read(const void* buf, size_t bytes, uint32_t* sink, hipStream_t stream);
 kap_status launch_proxy(const uint16_t* hidden, const uint16_t* wq, int32_t B, int32_t dm,
                         int32_t n_out, float* q_out, float* partial, int32_t splits,

@@ -2,18 +2,19 @@
 // side flow projects a preceding hidden state through the query projection to
 // obtain the routing query).  q_out = hidden @ W_q, bf16 inputs, fp32 sums.
 //
-// HBM-bound GEMV (B <= 16 rows share each W_q byte).  Block (256 threads)
-// owns 64 output columns x 512 rows of W_q: 8 lanes cover one 128-byte row
-// segment with 16-byte loads, so one wave-wide load reads 8 full rows.
-// Each lane accumulates B x 8 columns over its rows; partial sums are
-// reduced inside the block in a fixed order and written per row split, and a
-// second small kernel adds the splits in split order (deterministic).
+// HBM-bound GEMV (B <= 16 rows share each W_q byte).  A block (4 waves) owns a
+// tile of 512 output columns x kProxyRows rows of W_q; every wave-wide load
+// reads 1 KiB of one W_q row contiguously (lane l: columns 8l .. 8l+7), so DRAM
+// sees long contiguous runs.  Each lane accumulates B x 8 columns over its
+// rows; the four waves are added in wave order through LDS and each row split
+// writes its partial sums; a second kernel adds the splits in split order
+// (deterministic).
 #include "kap_internal.h"
 
 namespace kap {
 
-constexpr int kProxyCols = 64;
-constexpr int kProxyRows = 512;
+constexpr int kProxyCols = 512;  // columns per block: 64 lanes x 8
+constexpr int kProxyRows = 128;  // W_q rows per block (32 per wave)
 
 template <int BM>
 __global__ __launch_bounds__(256) void proxy_partial_kernel(const uint16_t* hidden,
@@ -23,7 +24,6 @@ __global__ __launch_bounds__(256) void proxy_partial_kernel(const uint16_t* hidd
   const int split = blockIdx.y;
   const int c0 = split * kProxyRows;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  const int part = lane & 7, rsub = lane >> 3;
   __shared__ float sh[BM][kProxyRows];
   for (int e = tid; e < BM * kProxyRows; e += 256) {
     const int b = e / kProxyRows, c = e % kProxyRows;
@@ -35,9 +35,19 @@ __global__ __launch_bounds__(256) void proxy_partial_kernel(const uint16_t* hidd
   for (int b = 0; b < BM; ++b)
 #pragma unroll
     for (int e = 0; e < 8; ++e) acc[b][e] = 0.f;
-  const uint16_t* wbase = wq + (int64_t)c0 * n_out + n0 + part * 8;
-  for (int r = wave * 8 + rsub; r < kProxyRows; r += 32) {
-    const uint4 w = *(const uint4*)(wbase + (int64_t)r * n_out);
+  constexpr int RPW = kProxyRows / 4;  // rows per wave
+  const uint16_t* wbase = wq + (int64_t)(c0 + wave * RPW) * n_out + n0 + lane * 8;
+  // rows in flight at once: all of the wave's rows, or 8 when the batch is 16
+  constexpr int INFL = BM >= 16 ? 8 : RPW;
+#pragma unroll
+  for (int r0 = 0; r0 < RPW; r0 += INFL) {
+  uint4 wrow[INFL];
+#pragma unroll
+  for (int r = 0; r < INFL; ++r) wrow[r] = *(const uint4*)(wbase + (int64_t)(r0 + r) * n_out);
+#pragma unroll
+  for (int rr = 0; rr < INFL; ++rr) {
+    const int r = r0 + rr;
+    const uint4 w = wrow[rr];
     const uint32_t ww[4] = {w.x, w.y, w.z, w.w};
     float wf[8];
 #pragma unroll
@@ -47,30 +57,40 @@ __global__ __launch_bounds__(256) void proxy_partial_kernel(const uint16_t* hidd
     }
 #pragma unroll
     for (int b = 0; b < BM; ++b) {
-      const float h = sh[b][r];
+      const float h = sh[b][wave * RPW + r];
 #pragma unroll
       for (int e = 0; e < 8; ++e) acc[b][e] += h * wf[e];
     }
   }
-  // lanes with the same `part` differ in bits 3..5: butterfly over them
-  __shared__ float red[4][BM][kProxyCols];
+  }
+  // waves 1..3 hand their sums to wave 0 through LDS, added in wave order,
+  // eight batch rows at a time
+  constexpr int BC = BM < 8 ? BM : 8;
+  __shared__ float red[3][BC][kProxyCols];
 #pragma unroll
-  for (int b = 0; b < BM; ++b)
+  for (int b0 = 0; b0 < BM; b0 += BC) {
+    if (wave > 0) {
 #pragma unroll
-    for (int e = 0; e < 8; ++e) {
-      float v = acc[b][e];
-      v += __shfl_xor(v, 8);
-      v += __shfl_xor(v, 16);
-      v += __shfl_xor(v, 32);
-      if (rsub == 0) red[wave][b][part * 8 + e] = v;
+      for (int bb = 0; bb < BC; ++bb)
+#pragma unroll
+        for (int e = 0; e < 8; ++e) red[wave - 1][bb][lane * 8 + e] = acc[b0 + bb][e];
     }
-  __syncthreads();
-  for (int e = tid; e < BM * kProxyCols; e += 256) {
-    const int b = e / kProxyCols, col = e % kProxyCols;
-    if (b < B) {
-      const float s = ((red[0][b][col] + red[1][b][col]) + red[2][b][col]) + red[3][b][col];
-      partial[((int64_t)split * B + b) * n_out + n0 + col] = s;
+    __syncthreads();
+    if (wave == 0) {
+#pragma unroll
+      for (int bb = 0; bb < BC; ++bb) {
+        const int b = b0 + bb;
+        if (b < B) {
+          float* dst = partial + ((int64_t)split * B + b) * n_out + n0 + lane * 8;
+#pragma unroll
+          for (int e = 0; e < 8; ++e) {
+            const int col = lane * 8 + e;
+            dst[e] = ((acc[b][e] + red[0][bb][col]) + red[1][bb][col]) + red[2][bb][col];
+          }
+        }
+      }
     }
+    __syncthreads();
   }
 }
 
@@ -79,9 +99,12 @@ __global__ __launch_bounds__(256) void proxy_reduce_kernel(const float* partial,
   const int i = blockIdx.x * 256 + threadIdx.x;
   if (i >= total) return;
   float s = 0.f;
+#pragma unroll 8
   for (int k = 0; k < splits; ++k) s += partial[(int64_t)k * total + i];
   out[i] = s;
 }
+
+int proxy_splits(int d_model) { return d_model / kProxyRows; }
 
 kap_status launch_proxy(const uint16_t* hidden, const uint16_t* wq, int32_t B, int32_t dm,
                         int32_t n_out, float* q_out, float* partial, int32_t splits,

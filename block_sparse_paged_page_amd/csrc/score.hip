@@ -62,7 +62,6 @@ __global__ __launch_bounds__(256) void score_kernel(ScoreArgs a) {
   constexpr int EPL = 16 / (int)sizeof(ST);  // elements per 16-byte load
   constexpr int LPR = D / EPL;               // lanes per summary row
   constexpr int RPL = 64 / LPR;              // rows per wave-wide load
-  constexpr int U = 8;                       // loads in flight per lane
   const int part = lane % LPR, sub = lane / LPR;
   float ur[EPL];
 #pragma unroll
@@ -71,43 +70,44 @@ __global__ __launch_bounds__(256) void score_kernel(ScoreArgs a) {
   const int N = (a.seq_lens[b] + kPage - 1) / kPage;
   const int blk0 = blockIdx.x * kScorePagesPerBlock;
   constexpr int per_wave = kScorePagesPerBlock / 4;
+  constexpr int U = per_wave / RPL;  // pages per lane group, all loads in flight at once
   const int w0 = blk0 + wave * per_wave;
   const int w1 = min(w0 + per_wave, a.max_pages);
   const int32_t* btrow = a.bt + (int64_t)b * a.max_pages;
   float* out = a.scores + ((int64_t)b * a.Hkv + g) * a.max_pages;
   const ST* summ = (const ST*)a.summ;
-  for (int base = w0; base < w1; base += RPL * U) {
-    uint4 v[U];
+  // the wave's page-table entries in one load (lane j: page w0 + j), then
+  // every summary row the lane needs, before any arithmetic
+  const int tr = (w0 + lane < min(w1, N)) ? btrow[w0 + lane] : 0;
+  uint4 v[U];
 #pragma unroll
-    for (int u = 0; u < U; ++u) {
-      const int p = base + u * RPL + sub;
-      v[u] = make_uint4(0, 0, 0, 0);
-      if (p < N && p < w1) {
-        const int64_t phys = btrow[p];
-        v[u] = *(const uint4*)(summ + (phys * a.Hkv + g) * D + part * EPL);
+  for (int u = 0; u < U; ++u) {
+    const int j = u * RPL + sub;
+    const int64_t phys = __shfl(tr, j);
+    v[u] = make_uint4(0, 0, 0, 0);
+    if (w0 + j < N && w0 + j < w1)
+      v[u] = *(const uint4*)(summ + (phys * a.Hkv + g) * D + part * EPL);
+  }
+#pragma unroll
+  for (int u = 0; u < U; ++u) {
+    float dot = 0.f;
+    if constexpr (sizeof(ST) == 2) {
+      const uint32_t w[4] = {v[u].x, v[u].y, v[u].z, v[u].w};
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        dot += ur[2 * e] * __uint_as_float(w[e] << 16);
+        dot += ur[2 * e + 1] * __uint_as_float(w[e] & 0xffff0000u);
       }
+    } else {
+      dot += ur[0] * __uint_as_float(v[u].x);
+      dot += ur[1] * __uint_as_float(v[u].y);
+      dot += ur[2] * __uint_as_float(v[u].z);
+      dot += ur[3] * __uint_as_float(v[u].w);
     }
 #pragma unroll
-    for (int u = 0; u < U; ++u) {
-      float dot = 0.f;
-      if constexpr (sizeof(ST) == 2) {
-        const uint32_t w[4] = {v[u].x, v[u].y, v[u].z, v[u].w};
-#pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          dot += ur[2 * e] * __uint_as_float(w[e] << 16);
-          dot += ur[2 * e + 1] * __uint_as_float(w[e] & 0xffff0000u);
-        }
-      } else {
-        dot += ur[0] * __uint_as_float(v[u].x);
-        dot += ur[1] * __uint_as_float(v[u].y);
-        dot += ur[2] * __uint_as_float(v[u].z);
-        dot += ur[3] * __uint_as_float(v[u].w);
-      }
-#pragma unroll
-      for (int m = 1; m < LPR; m <<= 1) dot += __shfl_xor(dot, m);
-      const int p = base + u * RPL + sub;
-      if (part == 0 && p < w1) out[p] = (p < N) ? dot : -INFINITY;
-    }
+    for (int m = 1; m < LPR; m <<= 1) dot += __shfl_xor(dot, m);
+    const int p = w0 + u * RPL + sub;
+    if (part == 0 && p < w1) out[p] = (p < N) ? dot : -INFINITY;
   }
 }
 

@@ -15,6 +15,8 @@
 
 namespace kap {
 
+constexpr int kSelectStagedPages = 11264;  // keys staged in LDS up to this table width (44 KiB)
+
 struct SelArgs {
   const float* scores;
   int32_t Hkv, max_pages;
@@ -64,13 +66,13 @@ __device__ __forceinline__ int block_exclusive_scan(int v, int* s_wave, int* tot
   return excl;
 }
 
-template <int KPT>
+template <int KPT, bool STAGED>
 __global__ __launch_bounds__(1024) void select_kernel(SelArgs a) {
   const int gr = blockIdx.x, b = blockIdx.y;
   const int G = a.per_head ? a.Hkv : 1;
   const int tid = threadIdx.x;
   __shared__ int s_hist[16][256];  // one private histogram per wave
-  __shared__ int s_suf[257];
+  __shared__ int s_suf[8];
   __shared__ int s_wave[33];
   __shared__ uint32_t s_digit;
   const int N = min((max(a.seq_lens[b], 0) + kPage - 1) / kPage, a.max_pages);
@@ -80,43 +82,83 @@ __global__ __launch_bounds__(1024) void select_kernel(SelArgs a) {
   const int mid_lo = na, mid_hi = N - nr;
   const int take = all ? 0 : min(max(nk, 0), mid_hi - mid_lo);
 
+  // ---- keys.  STAGED: pooled (or per-head) scores go through LDS with
+  // coalesced loads (consecutive threads read consecutive pages of one head
+  // row); all heads of a page are folded by one thread in head order.
+  // Otherwise (very long tables) each thread reads its own pages directly.
+  const int pbase = tid * KPT;
+  const int nh = a.per_head ? 1 : a.Hkv;
+  const float* base = a.scores + ((int64_t)b * a.Hkv + (a.per_head ? gr : 0)) * a.max_pages;
   uint32_t key[KPT];
   uint64_t cand = 0;  // bit j: page t*KPT+j is a middle candidate
-  const int pbase = tid * KPT;
-  float kv[KPT];
-  if (!all) {
-    // pooled: fold heads in ascending order, 4 heads' loads in flight at a time
-    const int nh = a.per_head ? 1 : a.Hkv;
-    const float* base = a.scores + ((int64_t)b * a.Hkv + (a.per_head ? gr : 0)) * a.max_pages;
-    for (int g0 = 0; g0 < nh; g0 += 4) {
-      float v[4][KPT];
+  if constexpr (STAGED) {
+    extern __shared__ float s_key[];  // [max_pages]
+    if (!all) {
+      for (int p0 = mid_lo; p0 < mid_hi; p0 += 1024 * 4) {
+        float v[4];
 #pragma unroll
-      for (int gi = 0; gi < 4; ++gi)
+        for (int u = 0; u < 4; ++u) {
+          const int p = p0 + u * 1024 + tid;
+          v[u] = (p < mid_hi) ? base[p] : 0.f;
+        }
+        for (int g = 1; g < nh; ++g) {
+          float w[4];
 #pragma unroll
-        for (int j = 0; j < KPT; ++j) {
-          const int p = pbase + j;
-          v[gi][j] = (g0 + gi < nh && p >= mid_lo && p < mid_hi)
-                         ? base[(int64_t)(g0 + gi) * a.max_pages + p] : 0.f;
+          for (int u = 0; u < 4; ++u) {
+            const int p = p0 + u * 1024 + tid;
+            w[u] = (p < mid_hi) ? base[(int64_t)g * a.max_pages + p] : 0.f;
+          }
+#pragma unroll
+          for (int u = 0; u < 4; ++u) v[u] = __fadd_rn(v[u], w[u]);
         }
 #pragma unroll
-      for (int gi = 0; gi < 4; ++gi)
+        for (int u = 0; u < 4; ++u) {
+          const int p = p0 + u * 1024 + tid;
+          if (p < mid_hi) s_key[p] = a.per_head ? v[u] : __fdiv_rn(v[u], (float)a.Hkv);
+        }
+      }
+    }
+    __syncthreads();
 #pragma unroll
-        for (int j = 0; j < KPT; ++j)
-          if (g0 + gi < nh) kv[j] = (g0 + gi == 0) ? v[gi][j] : __fadd_rn(kv[j], v[gi][j]);
+    for (int j = 0; j < KPT; ++j) {
+      const int p = pbase + j;
+      key[j] = 0u;
+      if (!all && p >= mid_lo && p < mid_hi) {
+        key[j] = order_key(s_key[p]);
+        cand |= 1ull << j;
+      }
+    }
+  } else {
+    float kv[KPT];
+#pragma unroll
+    for (int j = 0; j < KPT; ++j) kv[j] = 0.f;
+    if (!all) {
+      for (int g0 = 0; g0 < nh; g0 += 4) {
+        float v[4][KPT];
+#pragma unroll
+        for (int gi = 0; gi < 4; ++gi)
+#pragma unroll
+          for (int j = 0; j < KPT; ++j) {
+            const int p = pbase + j;
+            v[gi][j] = (g0 + gi < nh && p >= mid_lo && p < mid_hi)
+                           ? base[(int64_t)(g0 + gi) * a.max_pages + p] : 0.f;
+          }
+#pragma unroll
+        for (int gi = 0; gi < 4; ++gi)
+#pragma unroll
+          for (int j = 0; j < KPT; ++j)
+            if (g0 + gi < nh) kv[j] = (g0 + gi == 0) ? v[gi][j] : __fadd_rn(kv[j], v[gi][j]);
+      }
     }
 #pragma unroll
     for (int j = 0; j < KPT; ++j) {
       const int p = pbase + j;
       key[j] = 0u;
-      if (p >= mid_lo && p < mid_hi) {
-        const float k = a.per_head ? kv[j] : __fdiv_rn(kv[j], (float)a.Hkv);
-        key[j] = order_key(k);
+      if (!all && p >= mid_lo && p < mid_hi) {
+        key[j] = order_key(a.per_head ? kv[j] : __fdiv_rn(kv[j], (float)a.Hkv));
         cand |= 1ull << j;
       }
     }
-  } else {
-#pragma unroll
-    for (int j = 0; j < KPT; ++j) key[j] = 0u;
   }
 
   // ---- radix select of the take-th largest candidate key
@@ -132,25 +174,31 @@ __global__ __launch_bounds__(1024) void select_kernel(SelArgs a) {
         if (((cand >> j) & 1ull) && (key[j] & pmask) == prefix)
           atomicAdd(&s_hist[wv][(key[j] >> shift) & 255u], 1);
       __syncthreads();
+      // bins 0..255 live in waves 0..3: suffix sums by shuffles, 3 barriers per pass
+      int h = 0;
       if (tid < 256) {
-        int h = 0;
 #pragma unroll
         for (int w = 0; w < 16; ++w) h += s_hist[w][tid];
-        s_suf[tid] = h;
       }
-      if (tid == 0) s_suf[256] = 0;
+      int suf = h;  // inclusive suffix sum inside the wave (lanes above)
+#pragma unroll
+      for (int o = 1; o < 64; o <<= 1) {
+        const int y = __shfl_down(suf, o);
+        if ((tid & 63) + o < 64) suf += y;
+      }
+      if (tid < 256 && (tid & 63) == 0) s_suf[tid >> 6] = suf;  // wave totals
       __syncthreads();
-      for (int o = 1; o < 256; o <<= 1) {  // suffix sums: s_suf[d] = sum over digits >= d
-        int v = 0;
-        if (tid < 256 && tid + o < 256) v = s_suf[tid + o];
-        __syncthreads();
-        if (tid < 256) s_suf[tid] += v;
-        __syncthreads();
+      if (tid < 256) {
+        for (int w = (tid >> 6) + 1; w < 4; ++w) suf += s_suf[w];
+        const int above = suf - h;  // keys with digit > this bin
+        if (suf >= remaining && above < remaining) {
+          s_digit = tid;
+          s_suf[4] = above;
+        }
       }
-      if (tid < 256 && s_suf[tid] >= remaining && s_suf[tid + 1] < remaining) s_digit = tid;
       __syncthreads();
       const uint32_t d = s_digit;
-      remaining -= s_suf[d + 1];
+      remaining -= s_suf[4];
       prefix |= d << shift;
       pmask |= 0xffu << shift;
       __syncthreads();
@@ -207,7 +255,13 @@ kap_status launch_select(const float* scores, int32_t B, int32_t Hkv, int32_t ma
   const int G = per_head ? Hkv : 1;
   dim3 grid(G, B);
   const int kpt = (max_pages + 1023) / 1024;
-#define KAP_SEL(K) hipLaunchKernelGGL((select_kernel<K>), grid, dim3(1024), 0, stream, a)
+  const bool staged = max_pages <= kSelectStagedPages;
+  const size_t lds = staged ? (size_t)max_pages * sizeof(float) : 0;
+#define KAP_SEL(K)                                                                              \
+  do {                                                                                          \
+    if (staged) hipLaunchKernelGGL((select_kernel<K, true>), grid, dim3(1024), lds, stream, a); \
+    else hipLaunchKernelGGL((select_kernel<K, false>), grid, dim3(1024), 0, stream, a);        \
+  } while (0)
   if (kpt <= 1) KAP_SEL(1);
   else if (kpt <= 2) KAP_SEL(2);
   else if (kpt <= 4) KAP_SEL(4);

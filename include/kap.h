@@ -100,12 +100,12 @@ KAP_API kap_status kap_score_blocks(const void* q, int32_t q_dtype, const int32_
  * a proxy query from a preceding hidden state through the query projection,
  * then scores and selects over the K-summary cache before the target layer.
  *   q_out[b][n] = sum_c hidden[b][c] * w_q[c][n]     (bf16 inputs, fp32 accumulation,
- *                 row splits of 512 added in split order: deterministic)
+ *                 row splits of 128 added in split order: deterministic)
  *   hidden device [B][d_model] bf16; w_q device [d_model][n_out] bf16 (row-major)
  *   q_out  device out [B][n_out] float -- feed to kap_score_blocks as KAP_F32
  *          with n_out = Hq * D.
  *   workspace device, >= kap_proxy_workspace_bytes(B, d_model, n_out)
- * 1 <= B <= 16; d_model a multiple of 512; n_out a multiple of 64.
+ * 1 <= B <= 16; d_model a multiple of 128; n_out a multiple of 512.
  */
 KAP_API size_t kap_proxy_workspace_bytes(int32_t B, int32_t d_model, int32_t n_out);
 KAP_API kap_status kap_proxy_query(const void* hidden, const void* w_q, int32_t B, int32_t d_model,

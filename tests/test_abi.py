@@ -143,7 +143,7 @@ def test_workspace_sizes_are_monotone(lib):
     b = kap.attn_workspace_bytes(4, 4, 64, 8, 128)
     assert 0 < a < b
     assert kap.attn_workspace_bytes(0, 1, 8, 2, 64) == 0
-    assert kap.proxy_workspace_bytes(8, 4096, 4096) == 8 * 8 * 4096 * 4
+    assert kap.proxy_workspace_bytes(8, 4096, 4096) == (4096 // 128) * 8 * 4096 * 4
 
 
 def test_proxy_validation(lib):
@@ -151,6 +151,7 @@ def test_proxy_validation(lib):
     assert f(NP, NP, 0, 4096, 4096, NP, NP, 1 << 30, None) == UNSUPPORTED
     assert f(NP, NP, 17, 4096, 4096, NP, NP, 1 << 30, None) == UNSUPPORTED
     assert f(NP, NP, 1, 1000, 4096, NP, NP, 1 << 30, None) == UNSUPPORTED
+    assert f(NP, NP, 1, 4096, 4000, NP, NP, 1 << 30, None) == UNSUPPORTED
     assert f(NP, NP, 1, 4096, 4096, NP, NP, 16, None) == WORKSPACE
 
 
