@@ -207,6 +207,28 @@ __global__ __launch_bounds__(64) void attn_partial_bf16(PartArgs a) {
   const int k_lane = l16 * D + 8 * q4;
   const int v_lane = l16 * kPage + 4 * q4;
 
+  // Prologue order matters under load: the query rows are fetched first (they
+  // gate the first MFMA), then the page-table window, then the first pages;
+  // the rotation runs while those pages are in flight.
+  constexpr int SR = 16 * NT;   // rows per slice
+  constexpr int CPR = D / 8;    // 16-byte chunks per row
+  constexpr int QPL = SR * CPR / 64;  // chunks per lane
+  uint4 qraw[QPL];
+  {
+    const uint16_t* q = (const uint16_t*)a.q;
+#pragma unroll
+    for (int k = 0; k < QPL; ++k) {
+      const int e = k * 64 + lane;
+      const int rr = e / CPR, c = e % CPR;
+      const int r = row0 + rr;
+      qraw[k] = make_uint4(0, 0, 0, 0);
+      if (r < a.R) {
+        const int i = r / a.grp, h = g * a.grp + r % a.grp;
+        qraw[k] = *(const uint4*)(q + (((int64_t)b * a.q_len + i) * a.Hq + h) * D + 8 * c);
+      }
+    }
+  }
+
   // page-table window: lane j holds trow[wbase + j]
   int wbase = p0;
   int tr = (p0 + lane < p1) ? trow[p0 + lane] : 0;
@@ -234,22 +256,14 @@ __global__ __launch_bounds__(64) void attn_partial_bf16(PartArgs a) {
 
   // This slice's query rows, rotated at their positions, as LDS fragments in
   // the B-operand layout of S^T = K Q^T (row l16, dims 32 s + 8 q4 .. + 7).
-  constexpr int SR = 16 * NT;  // rows per slice
   __shared__ uint16_t sraw[SR][D];
   __shared__ uint4 sq[NT][KS][64];
   int qpos[NT];
   {
-    constexpr int CPR = D / 8;  // 16-byte chunks per row
-    const uint16_t* q = (const uint16_t*)a.q;
-    for (int e = lane; e < SR * CPR; e += 64) {
-      const int rr = e / CPR, c = e % CPR;
-      const int r = row0 + rr;
-      uint4 v = make_uint4(0, 0, 0, 0);
-      if (r < a.R) {
-        const int i = r / a.grp, h = g * a.grp + r % a.grp;
-        v = *(const uint4*)(q + (((int64_t)b * a.q_len + i) * a.Hq + h) * D + 8 * c);
-      }
-      *(uint4*)&sraw[rr][8 * c] = v;
+#pragma unroll
+    for (int k = 0; k < QPL; ++k) {
+      const int e = k * 64 + lane;
+      *(uint4*)&sraw[e / CPR][8 * (e % CPR)] = qraw[k];
     }
     __syncthreads();
     constexpr int HALF = D / 2, LPP = 64 / HALF;

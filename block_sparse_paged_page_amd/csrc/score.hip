@@ -36,14 +36,49 @@ template <int D, typename ST, typename QT>
 __global__ __launch_bounds__(256) void score_kernel(ScoreArgs a) {
   const int b = blockIdx.z, g = blockIdx.y;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  constexpr int EPL = 16 / (int)sizeof(ST);  // elements per 16-byte load
+  constexpr int LPR = D / EPL;               // lanes per summary row
+  constexpr int RPL = 64 / LPR;              // rows per wave-wide load
+  const int part = lane % LPR, sub = lane / LPR;
+  const int N = (a.seq_lens[b] + kPage - 1) / kPage;
+  const int blk0 = blockIdx.x * kScorePagesPerBlock;
+  constexpr int per_wave = kScorePagesPerBlock / 4;
+  constexpr int U = per_wave / RPL;  // pages per lane group, all loads in flight at once
+  const int w0 = blk0 + wave * per_wave;
+  const int w1 = min(w0 + per_wave, a.max_pages);
+  const int32_t* btrow = a.bt + (int64_t)b * a.max_pages;
+  float* out = a.scores + ((int64_t)b * a.Hkv + g) * a.max_pages;
+  const ST* summ = (const ST*)a.summ;
+
+  // The group's query heads are fetched first, then the wave's page-table
+  // entries (lane j: page w0 + j) and every summary row the lane needs; the
+  // group query is rotated and summed while the summary rows are in flight.
   __shared__ float su[D];
   __shared__ float sq[16 * D];  // the group's query heads (grp <= 16)
-  constexpr int half = D / 2;
+  constexpr int QPT = 16 * D / 256;
+  float qv[QPT];
   {
     const int64_t q0 = ((int64_t)b * a.Hq + g * a.grp) * D;  // group heads are contiguous
-    for (int e = tid; e < a.grp * D; e += 256) sq[e] = (float)widen_any<QT>(a.q, q0 + e);
+#pragma unroll
+    for (int k = 0; k < QPT; ++k) {
+      const int e = k * 256 + tid;
+      qv[k] = e < a.grp * D ? (float)widen_any<QT>(a.q, q0 + e) : 0.f;
+    }
   }
+  const int tr = (w0 + lane < min(w1, N)) ? btrow[w0 + lane] : 0;
+  uint4 v[U];
+#pragma unroll
+  for (int u = 0; u < U; ++u) {
+    const int j = u * RPL + sub;
+    const int64_t phys = __shfl(tr, j);
+    v[u] = make_uint4(0, 0, 0, 0);
+    if (w0 + j < N && w0 + j < w1)
+      v[u] = *(const uint4*)(summ + (phys * a.Hkv + g) * D + part * EPL);
+  }
+#pragma unroll
+  for (int k = 0; k < QPT; ++k) sq[k * 256 + tid] = qv[k];
   __syncthreads();
+  constexpr int half = D / 2;
   for (int pair = tid; pair < half; pair += 256) {
     double s, c;
     rope_sincos((double)a.pos[b], pair, D, a.log2_theta, &s, &c);
@@ -58,36 +93,10 @@ __global__ __launch_bounds__(256) void score_kernel(ScoreArgs a) {
     su[pair + half] = (float)uy;
   }
   __syncthreads();
-
-  constexpr int EPL = 16 / (int)sizeof(ST);  // elements per 16-byte load
-  constexpr int LPR = D / EPL;               // lanes per summary row
-  constexpr int RPL = 64 / LPR;              // rows per wave-wide load
-  const int part = lane % LPR, sub = lane / LPR;
   float ur[EPL];
 #pragma unroll
   for (int e = 0; e < EPL; ++e) ur[e] = su[part * EPL + e];
 
-  const int N = (a.seq_lens[b] + kPage - 1) / kPage;
-  const int blk0 = blockIdx.x * kScorePagesPerBlock;
-  constexpr int per_wave = kScorePagesPerBlock / 4;
-  constexpr int U = per_wave / RPL;  // pages per lane group, all loads in flight at once
-  const int w0 = blk0 + wave * per_wave;
-  const int w1 = min(w0 + per_wave, a.max_pages);
-  const int32_t* btrow = a.bt + (int64_t)b * a.max_pages;
-  float* out = a.scores + ((int64_t)b * a.Hkv + g) * a.max_pages;
-  const ST* summ = (const ST*)a.summ;
-  // the wave's page-table entries in one load (lane j: page w0 + j), then
-  // every summary row the lane needs, before any arithmetic
-  const int tr = (w0 + lane < min(w1, N)) ? btrow[w0 + lane] : 0;
-  uint4 v[U];
-#pragma unroll
-  for (int u = 0; u < U; ++u) {
-    const int j = u * RPL + sub;
-    const int64_t phys = __shfl(tr, j);
-    v[u] = make_uint4(0, 0, 0, 0);
-    if (w0 + j < N && w0 + j < w1)
-      v[u] = *(const uint4*)(summ + (phys * a.Hkv + g) * D + part * EPL);
-  }
 #pragma unroll
   for (int u = 0; u < U; ++u) {
     float dot = 0.f;

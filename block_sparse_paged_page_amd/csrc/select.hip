@@ -94,25 +94,28 @@ __global__ __launch_bounds__(1024) void select_kernel(SelArgs a) {
   if constexpr (STAGED) {
     extern __shared__ float s_key[];  // [max_pages]
     if (!all) {
-      for (int p0 = mid_lo; p0 < mid_hi; p0 += 1024 * 4) {
-        float v[4];
+      // up to 8 heads x 4 pages of loads in flight per thread, folded in head order
+      constexpr int SU = 4, SG = 8;
+      for (int p0 = mid_lo; p0 < mid_hi; p0 += 1024 * SU) {
+        float v[SU];
+        for (int g0 = 0; g0 < nh; g0 += SG) {
+          float w[SG][SU];
 #pragma unroll
-        for (int u = 0; u < 4; ++u) {
-          const int p = p0 + u * 1024 + tid;
-          v[u] = (p < mid_hi) ? base[p] : 0.f;
+          for (int gi = 0; gi < SG; ++gi)
+#pragma unroll
+            for (int u = 0; u < SU; ++u) {
+              const int p = p0 + u * 1024 + tid;
+              w[gi][u] = (g0 + gi < nh && p < mid_hi) ? base[(int64_t)(g0 + gi) * a.max_pages + p]
+                                                      : 0.f;
+            }
+#pragma unroll
+          for (int gi = 0; gi < SG; ++gi)
+#pragma unroll
+            for (int u = 0; u < SU; ++u)
+              if (g0 + gi < nh) v[u] = (g0 + gi == 0) ? w[gi][u] : __fadd_rn(v[u], w[gi][u]);
         }
-        for (int g = 1; g < nh; ++g) {
-          float w[4];
 #pragma unroll
-          for (int u = 0; u < 4; ++u) {
-            const int p = p0 + u * 1024 + tid;
-            w[u] = (p < mid_hi) ? base[(int64_t)g * a.max_pages + p] : 0.f;
-          }
-#pragma unroll
-          for (int u = 0; u < 4; ++u) v[u] = __fadd_rn(v[u], w[u]);
-        }
-#pragma unroll
-        for (int u = 0; u < 4; ++u) {
+        for (int u = 0; u < SU; ++u) {
           const int p = p0 + u * 1024 + tid;
           if (p < mid_hi) s_key[p] = a.per_head ? v[u] : __fdiv_rn(v[u], (float)a.Hkv);
         }
