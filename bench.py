@@ -91,8 +91,11 @@ def read_traffic(kernel_key):
     path = os.path.join(ROOT, "profiles", "attn_qwen32b_128k_b4_hbm_traffic.md")
     if not os.path.exists(path):
         return None
-    src = os.path.join(ROOT, "block_sparse_paged_page_amd", "csrc", "attn.hip")
-    sha = hashlib.sha256(open(src, "rb").read()).hexdigest()[:16]
+    csrc = os.path.join(ROOT, "block_sparse_paged_page_amd", "csrc")
+    h = hashlib.sha256()
+    for name in ("attn.hip", "kap_internal.h"):   # the kernel's source and its shared header
+        h.update(open(os.path.join(csrc, name), "rb").read())
+    sha = h.hexdigest()[:16]
     for line in open(path):
         if line.startswith("traffic:"):
             f = dict(kv.split("=") for kv in line.split()[1:])
@@ -554,7 +557,7 @@ def main():
     gbs = lambda nb, ms: nb / (ms * 1e-3) / 1e9  # noqa: E731
     ver_gbs = gbs(nbytes["verify"], ver_ms)
     traffic = read_traffic("verify")
-    roofline = {"bound": "hbm", "kernel": "kap_verify_attn (prep + MFMA split-K partial + merge)",
+    roofline = {"bound": "hbm", "kernel": "kap_verify_attn (MFMA split-K partial + LSE merge, 2 launches)",
                 "achieved": round(ver_gbs, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
                 "frac": round(ver_gbs / HBM_PEAK_GBS, 4), "traffic": traffic,
                 "measured_read_ceiling_GBps": round(ceiling_gbs, 1),
