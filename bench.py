@@ -49,7 +49,8 @@ def parse():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--quiet", action="store_true")
     ap.add_argument("--workload", default="qwen32b_128k",
-                    choices=["qwen32b_128k", "llama8b_32k", "early_route_40k", "mixed_serving"],
+                    choices=["qwen32b_128k", "qwen32b_128k_commit", "llama8b_32k",
+                             "early_route_40k", "mixed_serving"],
                     help="qwen32b_128k is the headline line; the others print their own "
                          "measurement lines")
     return ap.parse_args()
@@ -418,8 +419,104 @@ def run_mixed(args, dev):
         "s_meas_bytes": round(sel_bytes / full_bytes, 4),
         "selected_pages_per_request": {"min": int(pages.min()), "mean": round(float(pages.mean()), 1),
                                        "max": int(pages.max())},
+        # load balance: the batch's own imbalance, and how much of the uniform
+        # full-table rate the one ragged launch keeps
+        "request_imbalance_max_over_mean": round(float(pages.max() / pages.mean()), 2),
+        "ragged_over_full_GBps": round((sel_bytes / t_sel) / (full_bytes / t_full), 3),
         "context_tokens": {"min": int(b["seq_lens"].min()), "mean": round(float(b["seq_lens"].mean()), 1),
                            "max": int(b["seq_lens"].max())},
+    }), flush=True)
+
+
+def run_commit(args, dev):
+    """The committed-state advance at 128K (batch 4): route, 4 proposal decodes,
+    then the k+1 = 5 token window's K/V appended through the slot mapping, the
+    touched summary rows recomputed, and the causal verify over 131077 tokens.
+    Every call rotates over layer copies like the headline step."""
+    w = W.spec("qwen32b_128k", B=args.batch, q_len=K_PROPOSE + 1)
+    B, Hq, Hkv, D = w.B, w.Hq, w.Hkv, w.D
+    b = W.make_device(w, dev)
+    to = _upload(b, dev)
+    bt, L, pos = to(b["bt"]), to(b["seq_lens"]), to(b["positions"])
+    L2 = to((b["seq_lens"] + w.q_len).astype(np.int32))
+    anchor, recent, k_mid = to(b["anchor"]), to(b["recent"]), to(b["k_mid"])
+    cap = int((b["anchor"] + b["recent"] + b["k_mid"]).max())
+    qv = to(b["qv"].view(np.int16)).view(torch.bfloat16)                 # [B][5][Hq][D]
+    q_prop = [qv[:, j].contiguous() for j in range(K_PROPOSE)]
+    pos_prop = [pos + j for j in range(K_PROPOSE)]
+    q_route = to(b["q"].view(np.int16)).view(torch.bfloat16)
+    kn, vn = W.draft_kv(w)
+    kn = to(kn.view(np.int16)).view(torch.bfloat16)
+    vn = to(vn.view(np.int16)).view(torch.bfloat16)
+    S0 = torch.zeros((b["pool_pages"], Hkv, D), dtype=torch.bfloat16, device=dev)
+    kap.build_summary(b["K"], bt, L, S0)
+    R = args.layers or 8
+    layers = [Layer(b["K"], b["V"], S0)]
+    for _ in range(R - 1):
+        layers.append(Layer(b["K"].clone(), b["V"].clone(), S0.clone()))
+    ws = torch.empty(kap.attn_workspace_bytes(B, w.q_len, Hq, Hkv, D), dtype=torch.uint8, device=dev)
+    scores = torch.empty((B, Hkv, bt.shape[1]), dtype=torch.float32, device=dev)
+    sel = torch.empty((B, 1, cap), dtype=torch.int32, device=dev)
+    cnt = torch.empty((B, 1), dtype=torch.int32, device=dev)
+    cv = (torch.empty((B, 1, cap), dtype=torch.int32, device=dev),
+          torch.empty((B, 1, cap), dtype=torch.int32, device=dev),
+          torch.empty((B, 1), dtype=torch.int32, device=dev),
+          torch.empty((B, w.q_len), dtype=torch.int64, device=dev))
+    out1 = torch.empty((B, Hq, D), dtype=torch.bfloat16, device=dev)
+    outv = torch.empty((B, w.q_len, Hq, D), dtype=torch.bfloat16, device=dev)
+    st = torch.cuda.current_stream()
+    it = [0]
+
+    def lay():
+        it[0] = (it[0] + 1) % R
+        return layers[it[0]]
+
+    def route(ly):
+        kap.score_blocks(q_route, pos, ly.S, bt, L, Hkv, scores=scores)
+        kap.select_topk(scores, L, anchor, recent, k_mid, cap, cap, sel=sel, cnt=cnt)
+        kap.compact_view(sel, cnt, bt, L, pos, w.q_len, out=cv)       # slot mapping of the window
+
+    def propose(ly):
+        for j in range(K_PROPOSE):
+            kap.decode_attn(q_prop[j], pos_prop[j], ly.K, ly.V, cv[0], cv[2], out=out1, workspace=ws)
+
+    def commit(ly):
+        kap.append_kv(kn, vn, cv[3], ly.K, ly.V)
+        kap.update_summary(ly.K, bt, L2, pos, w.q_len, ly.S)
+        kap.verify_attn(qv, pos, ly.K, ly.V, bt, L2, out=outv, workspace=ws)
+
+    def cycle():
+        ly = lay()
+        route(ly)
+        propose(ly)
+        commit(ly)
+
+    for _ in range(max(args.warmup, 2)):
+        cycle()
+    torch.cuda.synchronize()
+    t0 = time.time()
+    for _ in range(args.steps):
+        cycle()
+    torch.cuda.synchronize()
+    t_cycle = (time.time() - t0) / args.steps * 1e6
+    t_app = time_call(lambda: kap.append_kv(kn, vn, cv[3], lay().K, layers[it[0]].V), args.steps, st)
+    t_upd = time_call(lambda: kap.update_summary(lay().K, bt, L2, pos, w.q_len, layers[it[0]].S),
+                      args.steps, st)
+    t_ver = time_call(lambda: (lambda ly: kap.verify_attn(qv, pos, ly.K, ly.V, bt, L2, out=outv,
+                                                          workspace=ws))(lay()), args.steps, st)
+    kv_tok = Hkv * 2 * D * EB
+    q_bytes = B * Hq * D * EB
+    Ltot = int(b["seq_lens"].sum()) + B * w.q_len
+    ver_bytes = Ltot * kv_tok + 4 * int(((b["seq_lens"] + w.q_len + 15) // 16).sum()) + 2 * w.q_len * q_bytes
+    print(json.dumps({
+        "metric": METRIC, "workload": f"qwen32b_128k commit cycle: B={B}, route + {K_PROPOSE} selected "
+        f"decodes + append of the {w.q_len}-token window + summary update + causal verify over "
+        f"{int(b['seq_lens'][0]) + w.q_len} tokens",
+        "unit": "tokens/s", "value": round(B * K_PROPOSE / (t_cycle * 1e-6), 1), "dtype": "bf16",
+        "data": "synthetic", "layer_copies": R, "cycle_us": round(t_cycle, 2),
+        "append_kv_us": round(t_app, 2), "update_summary_us": round(t_upd, 2),
+        "verify_causal_us": round(t_ver, 2), "verify_causal_bytes": ver_bytes,
+        "verify_causal_GBps": round(ver_bytes / (t_ver * 1e-6) / 1e9, 1),
     }), flush=True)
 
 
@@ -436,7 +533,7 @@ def main():
     torch.cuda.set_device(dev)
     if args.workload != "qwen32b_128k":
         {"llama8b_32k": run_llama_sweep, "early_route_40k": run_early_route,
-         "mixed_serving": run_mixed}[args.workload](args, dev)
+         "mixed_serving": run_mixed, "qwen32b_128k_commit": run_commit}[args.workload](args, dev)
         return
     w = W.spec("qwen32b_128k", B=args.batch)
     B, Hq, Hkv, D = w.B, w.Hq, w.Hkv, w.D

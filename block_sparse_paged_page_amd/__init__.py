@@ -11,7 +11,7 @@ holding bf16 bit patterns; fp32 data are torch.float32; index tensors int32
 (slot mapping int64).  All tensors must be contiguous and on the same GPU.
 """
 from ._lib import (  # noqa: F401
-    BF16, F32, KapError, KapLibraryMissing, attn_workspace_bytes, budget_from_ratio,
+    BF16, F32, KapError, KapLibraryMissing, append_kv, attn_workspace_bytes, budget_from_ratio,
     build_summary, compact_view, decode_attn, diag_stream_read, lib_path, load, proxy_query,
-    proxy_workspace_bytes, score_blocks, select_topk, verify_attn, version,
+    proxy_workspace_bytes, score_blocks, select_topk, update_summary, verify_attn, version,
 )

@@ -45,6 +45,9 @@ _SIGS = {
                          _P, _I32, _I32, _P, _P, _P, _SZ, _P], _I32),
     "kap_diag_stream_read": ([_P, _SZ, _P, _P], _I32),
     "kap_build_summary": ([_P, _I32, _I32, _I32, _I32, _I32, _P, _I32, _P, _I32, _P, _I32, _P], _I32),
+    "kap_update_summary": ([_P, _I32, _I32, _I32, _I32, _I32, _P, _I32, _P, _P, _I32, _I32, _P, _I32,
+                            _P], _I32),
+    "kap_append_kv": ([_P, _P, _I32, _P, _I32, _I32, _I32, _I32, _I32, _I32, _P, _P, _P], _I32),
 }
 _lib = None
 
@@ -238,3 +241,32 @@ def build_summary(k_pool, block_table, seq_lens, summary, stream=None):
                                _p(summary), _dt(summary), _stream(stream))
     _check(st, "kap_build_summary")
     return summary
+
+
+def update_summary(k_pool, block_table, seq_lens, positions, q_new, summary, stream=None):
+    """kap_update_summary: recompute the summary rows of the pages holding tokens
+    positions[b] .. positions[b] + q_new - 1 (seq_lens: lengths after the append)."""
+    lib = load()
+    num_pages, Hkv, ps, D = k_pool.shape
+    st = lib.kap_update_summary(_p(k_pool), _dt(k_pool), num_pages, Hkv, D, ps, _p(block_table),
+                                block_table.shape[1], _p(seq_lens), _p(positions), int(q_new),
+                                block_table.shape[0], _p(summary), _dt(summary), _stream(stream))
+    _check(st, "kap_update_summary")
+    return summary
+
+
+def append_kv(k_new, v_new, slot_mapping, k_pool, v_pool, stream=None):
+    """kap_append_kv: write k_new/v_new [B][q_new][Hkv][D] into the pools at slot_mapping [B][q_new]."""
+    lib = load()
+    B, q_new, Hkv, D = k_new.shape
+    num_pages, _, ps, _ = k_pool.shape
+    if tuple(v_new.shape) != tuple(k_new.shape) or tuple(slot_mapping.shape) != (B, q_new):
+        raise ValueError("k_new, v_new must be [B][q_new][Hkv][D] and slot_mapping [B][q_new]")
+    if slot_mapping.dtype != torch.int64:
+        raise ValueError("slot_mapping must be int64")
+    if _dt(k_new) != _dt(k_pool) or _dt(v_new) != _dt(v_pool):
+        raise ValueError("new K/V must have the pool's dtype")
+    st = lib.kap_append_kv(_p(k_new), _p(v_new), _dt(k_pool), _p(slot_mapping), B, q_new, Hkv, D,
+                           ps, num_pages, _p(k_pool), _p(v_pool), _stream(stream))
+    _check(st, "kap_append_kv")
+    return k_pool, v_pool

@@ -170,7 +170,9 @@ struct PartArgs {
 // in flight while the third is consumed; the item's page-table entries are
 // fetched 64 at a time into one lane register each and broadcast with
 // readlane.  The query fragments live in LDS (re-read per page) to keep the
-// register footprint low enough for two waves per SIMD at NT = 2.
+// register footprint in budget: at D = 128, NT = 1 runs two waves per SIMD and
+// NT = 2..4 one, with no spills.  NT = 3 and 4 let a (b, g) row group of up to
+// 64 rows (e.g. a 5..8-token window under GQA 8:1) read each page once.
 // Online softmax with a lazy reference max: a row's reference only moves
 // when its running max exceeds it by more than 2^8 (log2 units), so the
 // O rescale is skipped wave-wide on almost every page; probabilities stay
@@ -328,49 +330,72 @@ __global__ __launch_bounds__(64) void attn_partial_bf16(PartArgs a) {
     // the compiler from hoisting them into registers)
     int ql = lane;
     asm volatile("" : "+v"(ql));
+    // The NT row tiles are independent: each stage runs across all tiles
+    // before the next, so one tile's MFMA latency hides behind another's
+    // VALU work, and one wave-wide vote decides the rare reference move.
+    floatx4 sacc[NT];
+#pragma unroll
+    for (int t = 0; t < NT; ++t) sacc[t] = floatx4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int s = 0; s < KS; ++s)
+#pragma unroll
+      for (int t = 0; t < NT; ++t)
+        sacc[t] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, f.k[s]),
+                                                         __builtin_bit_cast(bf16x8, sq[t][s][ql]),
+                                                         sacc[t], 0, 0, 0);
+    float z[NT][4], mx[NT];
 #pragma unroll
     for (int t = 0; t < NT; ++t) {
-      floatx4 sacc = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-      for (int s = 0; s < KS; ++s)
-        sacc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, f.k[s]),
-                                                      __builtin_bit_cast(bf16x8, sq[t][s][ql]),
-                                                      sacc, 0, 0, 0);
-      float z[4];
-      float mx = -INFINITY;
+      mx[t] = -INFINITY;
 #pragma unroll
       for (int j = 0; j < 4; ++j) {
         const int tok = tok0 + j;
         const bool vis = tok < len && tok <= qpos[t];
-        z[j] = vis ? sacc[j] * a.scale_log2 : -INFINITY;
-        mx = fmaxf(mx, z[j]);
+        z[t][j] = vis ? sacc[t][j] * a.scale_log2 : -INFINITY;
+        mx[t] = fmaxf(mx[t], z[t][j]);
       }
-      mx = wave_max_xor(mx, 16, 64);
-      // move the reference only when the running max clears it by kLazyRescale
-      const bool bump = mx > m[t] + kLazyRescale || (m[t] == -INFINITY && mx != -INFINITY);
-      if (__ballot(bump)) {
-        const float mn = bump ? mx : m[t];
+    }
+#pragma unroll
+    for (int t = 0; t < NT; ++t) mx[t] = wave_max_xor(mx[t], 16, 64);
+    // move a row's reference only when its running max clears it by kLazyRescale
+    bool bump[NT];
+    bool any = false;
+#pragma unroll
+    for (int t = 0; t < NT; ++t) {
+      bump[t] = mx[t] > m[t] + kLazyRescale || (m[t] == -INFINITY && mx[t] != -INFINITY);
+      any = any || bump[t];
+    }
+    if (__ballot(any)) {
+#pragma unroll
+      for (int t = 0; t < NT; ++t) {
+        const float mn = bump[t] ? mx[t] : m[t];  // unmoved rows scale by exp2(0) = 1
         const float alpha = (m[t] == -INFINITY) ? 0.f : __builtin_amdgcn_exp2f(m[t] - mn);
         l[t] *= alpha;
 #pragma unroll
         for (int c = 0; c < NC; ++c) o[t][c] *= alpha;
         m[t] = mn;
       }
+    }
+    short4v pf[NT];
+#pragma unroll
+    for (int t = 0; t < NT; ++t) {
       float pj[4];
       float psum = 0.f;
 #pragma unroll
       for (int j = 0; j < 4; ++j) {
-        pj[j] = (z[j] == -INFINITY) ? 0.f : __builtin_amdgcn_exp2f(z[j] - m[t]);
+        pj[j] = (z[t][j] == -INFINITY) ? 0.f : __builtin_amdgcn_exp2f(z[t][j] - m[t]);
         psum += pj[j];
       }
       l[t] += psum;
-      const short4v pf = __builtin_bit_cast(
-          short4v, make_uint2(pack_bf16x2(pj[0], pj[1]), pack_bf16x2(pj[2], pj[3])));
-#pragma unroll
-      for (int c = 0; c < NC; ++c)
-        o[t][c] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(__builtin_bit_cast(short4v, f.v[c]),
-                                                           pf, o[t][c], 0, 0, 0);
+      pf[t] = __builtin_bit_cast(short4v,
+                                 make_uint2(pack_bf16x2(pj[0], pj[1]), pack_bf16x2(pj[2], pj[3])));
     }
+#pragma unroll
+    for (int c = 0; c < NC; ++c)
+#pragma unroll
+      for (int t = 0; t < NT; ++t)
+        o[t][c] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(__builtin_bit_cast(short4v, f.v[c]),
+                                                           pf[t], o[t][c], 0, 0, 0);
   };
 
   for (int p = p0; p < p1; p += 3) {
@@ -618,10 +643,15 @@ kap_status launch_attention(const AttnCall& c) {
   const void* fn;
   int slices;
   if (c.dtype == KAP_BF16) {
-    const int nt = R <= 16 ? 1 : 2;
+    // one row slice whenever the rows fit in 64, so each page is read once per (b, g)
+    const int nt = R <= 16 ? 1 : R <= 32 ? 2 : R <= 48 ? 3 : 4;
     slices = (R + 16 * nt - 1) / (16 * nt);
-    if (c.D == 128) fn = nt == 1 ? (const void*)attn_partial_bf16<128, 1> : (const void*)attn_partial_bf16<128, 2>;
-    else fn = nt == 1 ? (const void*)attn_partial_bf16<64, 1> : (const void*)attn_partial_bf16<64, 2>;
+    static const void* const fns[2][4] = {
+        {(const void*)attn_partial_bf16<64, 1>, (const void*)attn_partial_bf16<64, 2>,
+         (const void*)attn_partial_bf16<64, 3>, (const void*)attn_partial_bf16<64, 4>},
+        {(const void*)attn_partial_bf16<128, 1>, (const void*)attn_partial_bf16<128, 2>,
+         (const void*)attn_partial_bf16<128, 3>, (const void*)attn_partial_bf16<128, 4>}};
+    fn = fns[c.D == 128 ? 1 : 0][nt - 1];
   } else {
     slices = (R + 31) / 32;
     fn = c.D == 128 ? (const void*)attn_partial_f32<128> : (const void*)attn_partial_f32<64>;

@@ -85,12 +85,22 @@ struct SummaryArgs {
   const int32_t* bt;
   int32_t max_pages;
   const int32_t* seq_lens;
+  const int32_t* first_pos;  // nullptr: all pages; else the pages of a token window
+  int32_t q_new;
   void* summ;
 };
 
 template <typename KT, typename ST>
 __global__ __launch_bounds__(256) void summary_kernel(SummaryArgs a) {
-  const int p = blockIdx.x, b = blockIdx.y;
+  const int b = blockIdx.y;
+  int p = blockIdx.x;
+  if (a.first_pos) {  // window [P, P + q_new): pages P/16 .. (P + q_new - 1)/16
+    const int P = a.first_pos[b];
+    const int t0 = max(P, 0), t1 = P + a.q_new - 1;
+    if (t1 < t0) return;
+    p += t0 / kPage;
+    if (p > t1 / kPage) return;
+  }
   const int L = a.seq_lens[b];
   const int N = min((max(L, 0) + kPage - 1) / kPage, a.max_pages);
   if (p >= N) return;
@@ -110,9 +120,12 @@ __global__ __launch_bounds__(256) void summary_kernel(SummaryArgs a) {
 
 kap_status launch_summary(const void* k, kap_dtype kv_dt, int32_t Hkv, int32_t D,
                           const int32_t* bt, int32_t max_pages, const int32_t* seq_lens,
-                          int32_t B, void* summ, kap_dtype s_dt, hipStream_t stream) {
-  SummaryArgs a{k, Hkv, D, bt, max_pages, seq_lens, summ};
-  dim3 grid(max_pages, B);
+                          const int32_t* first_pos, int32_t q_new, int32_t B, void* summ,
+                          kap_dtype s_dt, hipStream_t stream) {
+  SummaryArgs a{k, Hkv, D, bt, max_pages, seq_lens, first_pos, q_new, summ};
+  // a window of q_new tokens spans at most (q_new - 1) / 16 + 2 pages
+  const int span = first_pos ? min(max_pages, (q_new - 1) / kPage + 2) : max_pages;
+  dim3 grid(span, B);
   if (kv_dt == KAP_BF16 && s_dt == KAP_BF16)
     hipLaunchKernelGGL((summary_kernel<uint16_t, uint16_t>), grid, dim3(256), 0, stream, a);
   else if (kv_dt == KAP_BF16)

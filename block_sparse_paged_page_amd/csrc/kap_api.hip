@@ -295,8 +295,45 @@ kap_status kap_build_summary(const void* k_pool, int32_t kv_dtype, int32_t num_p
   if (B == 0 || max_pages == 0) return KAP_OK;
   if (!k_pool || !block_table || !seq_lens || !summary)
     return fail(KAP_ERR_INVALID_ARG, "null pointer");
-  return launch_summary(k_pool, (kap_dtype)kv_dtype, Hkv, D, block_table, max_pages, seq_lens, B,
-                        summary, (kap_dtype)sum_dtype, (hipStream_t)stream);
+  return launch_summary(k_pool, (kap_dtype)kv_dtype, Hkv, D, block_table, max_pages, seq_lens,
+                        nullptr, 0, B, summary, (kap_dtype)sum_dtype, (hipStream_t)stream);
+}
+
+kap_status kap_update_summary(const void* k_pool, int32_t kv_dtype, int32_t num_pages,
+                              int32_t Hkv, int32_t D, int32_t page_size,
+                              const int32_t* block_table, int32_t max_pages,
+                              const int32_t* seq_lens, const int32_t* positions, int32_t q_new,
+                              int32_t B, void* summary, int32_t sum_dtype, kap_stream stream) {
+  g_err[0] = 0;
+  if (B < 0 || max_pages < 0 || num_pages < 0 || Hkv <= 0 || q_new < 0)
+    return fail(KAP_ERR_INVALID_ARG, "bad size");
+  if (D != 64 && D != 128) return fail(KAP_ERR_UNSUPPORTED, "head_dim %d (64 or 128)", D);
+  if (page_size != kPage) return fail(KAP_ERR_UNSUPPORTED, "page_size %d (16)", page_size);
+  if (!dtype_ok(kv_dtype) || !dtype_ok(sum_dtype))
+    return fail(KAP_ERR_UNSUPPORTED, "dtype kv=%d summary=%d", kv_dtype, sum_dtype);
+  if (B == 0 || max_pages == 0 || q_new == 0) return KAP_OK;
+  if (!k_pool || !block_table || !seq_lens || !positions || !summary)
+    return fail(KAP_ERR_INVALID_ARG, "null pointer");
+  return launch_summary(k_pool, (kap_dtype)kv_dtype, Hkv, D, block_table, max_pages, seq_lens,
+                        positions, q_new, B, summary, (kap_dtype)sum_dtype, (hipStream_t)stream);
+}
+
+kap_status kap_append_kv(const void* k_new, const void* v_new, int32_t kv_dtype,
+                         const int64_t* slot_mapping, int32_t B, int32_t q_new, int32_t Hkv,
+                         int32_t D, int32_t page_size, int32_t num_pages, void* k_pool,
+                         void* v_pool, kap_stream stream) {
+  g_err[0] = 0;
+  if (B < 0 || q_new < 0 || num_pages < 0 || Hkv <= 0)
+    return fail(KAP_ERR_INVALID_ARG, "bad size (B %d, q_new %d, Hkv %d)", B, q_new, Hkv);
+  if (D != 64 && D != 128) return fail(KAP_ERR_UNSUPPORTED, "head_dim %d (64 or 128)", D);
+  if (page_size != kPage) return fail(KAP_ERR_UNSUPPORTED, "page_size %d (16)", page_size);
+  if (!dtype_ok(kv_dtype)) return fail(KAP_ERR_UNSUPPORTED, "dtype %d", kv_dtype);
+  if ((int64_t)B * q_new > 0x7fffffffLL) return fail(KAP_ERR_UNSUPPORTED, "B * q_new too large");
+  if (B == 0 || q_new == 0) return KAP_OK;
+  if (!k_new || !v_new || !slot_mapping || !k_pool || !v_pool)
+    return fail(KAP_ERR_INVALID_ARG, "null pointer");
+  return launch_append(k_new, v_new, (kap_dtype)kv_dtype, slot_mapping, B, q_new, Hkv, D,
+                       (int64_t)num_pages * kPage, k_pool, v_pool, (hipStream_t)stream);
 }
 
 kap_status kap_diag_stream_read(const void* buf, size_t bytes, uint32_t* sink, kap_stream stream) {

@@ -124,9 +124,15 @@ kap_status launch_compact(const int32_t* sel, const int32_t* cnt, int32_t B, int
                           const int32_t* seq_lens, const int32_t* pos, int32_t q_new,
                           int32_t* cbt, int32_t* clog, int32_t* clen, int64_t* slot,
                           hipStream_t stream);
+// first_pos == nullptr: every logical page; else only the pages holding
+// tokens first_pos[b] .. first_pos[b] + q_new - 1.
 kap_status launch_summary(const void* k, kap_dtype kv_dt, int32_t Hkv, int32_t D,
                           const int32_t* bt, int32_t max_pages, const int32_t* seq_lens,
-                          int32_t B, void* summ, kap_dtype s_dt, hipStream_t stream);
+                          const int32_t* first_pos, int32_t q_new, int32_t B, void* summ,
+                          kap_dtype s_dt, hipStream_t stream);
+kap_status launch_append(const void* k_new, const void* v_new, kap_dtype dt, const int64_t* slot,
+                         int32_t B, int32_t q_new, int32_t Hkv, int32_t D, int64_t num_slots,
+                         void* k, void* v, hipStream_t stream);
 int proxy_splits(int d_model);
 kap_status launch_diag_read(const void* buf, size_t bytes, uint32_t* sink, hipStream_t stream);
 kap_status launch_proxy(const uint16_t* hidden, const uint16_t* wq, int32_t B, int32_t dm,

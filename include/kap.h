@@ -8,6 +8,10 @@
  *   3. kap_compact_view  compact block table + slot mapping over the pick
  *   4. kap_decode_attn   q = 1 GQA decode over the compact view
  *   5. kap_verify_attn   short query window over the full paged KV
+ * and around it: kap_append_kv writes the window's K/V through the slot
+ * mapping (so the verify can attend causally to it), kap_update_summary /
+ * kap_build_summary keep the block-mean K summaries current, kap_proxy_query
+ * forms an early-routing query.
  *
  * Sources (web pages the method is described on):
  *   [KAP]  "KAP: Bridging the Knowledge Selection-Runtime Consumption Gap in
@@ -236,6 +240,41 @@ KAP_API kap_status kap_build_summary(const void* k_pool, int32_t kv_dtype, int32
                              const int32_t* block_table, int32_t max_pages,
                              const int32_t* seq_lens, int32_t B, void* summary,
                              int32_t sum_dtype, kap_stream stream);
+
+/*
+ * Block-mean K summary update after an append ([ESKV] the K-summary cache is
+ * kept current as tokens arrive).  Recomputes, exactly as kap_build_summary
+ * does, only the logical pages that hold the tokens at positions[b] + i,
+ * 0 <= i < q_new (pages at or past ceil(seq_lens[b] / 16) are skipped).
+ * seq_lens are the lengths after the append.  Every other summary row is
+ * untouched.
+ *   positions device [B] int32 (first new token's logical position)
+ */
+KAP_API kap_status kap_update_summary(const void* k_pool, int32_t kv_dtype, int32_t num_pages,
+                                      int32_t Hkv, int32_t D, int32_t page_size,
+                                      const int32_t* block_table, int32_t max_pages,
+                                      const int32_t* seq_lens, const int32_t* positions,
+                                      int32_t q_new, int32_t B, void* summary, int32_t sum_dtype,
+                                      kap_stream stream);
+
+/*
+ * KV append through a slot mapping ([KAP] verifier: verification advances the
+ * committed full-context KV state; [KAP] selected-KV view: slot mappings place
+ * newly scheduled tokens into their physical KV slots).  Token i of request b
+ * goes to slot s = slot_mapping[b][i] = page * 16 + offset: its K row for KV
+ * head g becomes k_pool[page][g][offset][:] and its V values become
+ * v_pool[page][g][:][offset].  Rows are copied bit for bit (K as the cache
+ * holds it, already rotated).  Slots equal to -1, or at or beyond
+ * num_pages * 16, are skipped.  Two tokens with the same slot race; the caller
+ * keeps slots distinct (kap_compact_view's slot mapping is).
+ *   k_new, v_new device [B][q_new][Hkv][D] in kv_dtype
+ *   slot_mapping device [B][q_new] int64
+ *   k_pool, v_pool device, updated in place (layouts as in kap_decode_attn)
+ */
+KAP_API kap_status kap_append_kv(const void* k_new, const void* v_new, int32_t kv_dtype,
+                                 const int64_t* slot_mapping, int32_t B, int32_t q_new,
+                                 int32_t Hkv, int32_t D, int32_t page_size, int32_t num_pages,
+                                 void* k_pool, void* v_pool, kap_stream stream);
 
 /*
  * Diagnostic, not part of the path: reads `bytes` (a multiple of 16) of device

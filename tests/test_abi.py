@@ -155,6 +155,23 @@ def test_proxy_validation(lib):
     assert f(NP, NP, 1, 4096, 4096, NP, NP, 16, None) == WORKSPACE
 
 
+def test_append_and_summary_update_validation(lib):
+    ap = lib.kap_append_kv
+    #        k_new v_new dt slot B  q  Hkv  D   ps  pages k   v   stream
+    assert ap(NP, NP, 1, NP, 2, 5, 8, 96, 16, 100, NP, NP, None) == UNSUPPORTED
+    assert ap(NP, NP, 1, NP, 2, 5, 8, 128, 32, 100, NP, NP, None) == UNSUPPORTED
+    assert ap(NP, NP, 5, NP, 2, 5, 8, 128, 16, 100, NP, NP, None) == UNSUPPORTED
+    assert ap(NP, NP, 1, None, 2, 5, 8, 128, 16, 100, NP, NP, None) == INVALID
+    assert ap(NP, NP, 1, NP, -1, 5, 8, 128, 16, 100, NP, NP, None) == INVALID
+    assert ap(None, None, 1, None, 0, 5, 8, 128, 16, 100, None, None, None) == OK  # nothing to do
+    up = lib.kap_update_summary
+    #        k  dt pages Hkv D   ps  bt  maxp lens pos q  B  summ sdt stream
+    assert up(NP, 1, 100, 8, 128, 16, NP, 64, NP, None, 5, 2, NP, 1, None) == INVALID
+    assert up(NP, 1, 100, 8, 64, 8, NP, 64, NP, NP, 5, 2, NP, 1, None) == UNSUPPORTED
+    assert up(NP, 1, 100, 8, 128, 16, NP, 64, NP, NP, -1, 2, NP, 1, None) == INVALID
+    assert up(None, 1, 100, 8, 128, 16, None, 64, None, None, 0, 2, None, 1, None) == OK
+
+
 def test_product_binding_never_imports_oracle():
     pkg = os.path.join(ROOT, "block_sparse_paged_page_amd")
     for dirpath, _, files in os.walk(pkg):

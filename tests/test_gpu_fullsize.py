@@ -215,3 +215,42 @@ def test_early_route_40k_b8_full_size():
     sel_ref, cnt_ref, cv = _routing(big)
     assert np.all(cnt_ref == 8)
     _attention(big, sel_ref, cnt_ref, cv, samples=[(0, 0), (5, 6)])
+
+
+def test_qwen32b_128k_b4_append_and_causal_verify():
+    """The k+1 = 5 token window at 131072..131076: its K/V appended through the
+    slot mapping, then the causal verify over 131077 tokens, sampled rows."""
+    w = W.spec("qwen32b_128k", B=4, q_len=5)
+    big = Big(w)
+    b = big.b
+    kn, vn = W.draft_kv(w)
+    samples = [(0, 2), (3, 6)]
+    hosts = {s: big.host_group(*s) for s in samples}     # oracle copies, taken before the append
+    to = lambda a: torch.from_numpy(np.ascontiguousarray(a)).cuda()  # noqa: E731
+    sel, cnt = np.full((w.B, 1, 1), -1, np.int32), np.zeros((w.B, 1), np.int32)
+    slot = kap.compact_view(to(sel), to(cnt), big.bt, big.L, big.pos, w.q_len)[3]
+    kap.append_kv(to(kn.view(np.int16)), to(vn.view(np.int16)), slot, big.K, big.V)
+    L2 = (b["seq_lens"] + w.q_len).astype(np.int32)
+    ws = torch.empty(kap.attn_workspace_bytes(w.B, w.q_len, w.Hq, w.Hkv, w.D), dtype=torch.uint8,
+                     device="cuda")
+    vl = torch.empty((w.B, w.q_len, w.Hq), dtype=torch.float32, device="cuda")
+    vout = kap.verify_attn(big.qv, big.pos, big.K, big.V, big.bt, to(L2), lse=vl, workspace=ws)
+    torch.cuda.synchronize()
+    s_ref = oracle.compact(sel, cnt, b["bt"], b["seq_lens"], b["positions"], w.q_len)[3]
+    np.testing.assert_array_equal(slot.cpu().numpy(), s_ref)
+    grp = w.Hq // w.Hkv
+    o = vout.view(torch.int16).cpu().numpy().view(np.uint16).reshape(w.B, w.q_len, w.Hq, w.D)
+    lg = vl.cpu().numpy()
+    worst = 0.0
+    for (bi, g), (Kh, Vh, btl) in hosts.items():
+        P = int(b["positions"][bi])
+        local_slot = np.arange(P, P + w.q_len, dtype=np.int64)[None]   # pages in logical order
+        oracle.append_kv(kn[bi:bi + 1, :, g:g + 1], vn[bi:bi + 1, :, g:g + 1], local_slot, Kh, Vh)
+        qsub = b["qv"][bi:bi + 1, :, g * grp:(g + 1) * grp]
+        ref, lref = oracle.attend(qsub, b["positions"][bi:bi + 1], Kh, Vh, btl,
+                                  [np.arange(int(L2[bi]), dtype=np.int32)], 1, 1)
+        got = oracle.widen(o[bi, :, g * grp:(g + 1) * grp])
+        worst = max(worst, float(row_errors(got, ref[0]).max()))
+        assert np.abs(lg[bi, :, g * grp:(g + 1) * grp] - lref[0]).max() <= LSE_TOL["bf16"]
+    assert worst <= TOL["bf16"], worst
+    print(f"[qwen32b_128k append] causal verify over 131077 tokens max rel err {worst:.2e}", flush=True)

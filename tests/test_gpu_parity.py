@@ -196,6 +196,30 @@ def test_gpu_chain_end_to_end(name):
     assert e.max() <= TOL[w.dtype]
 
 
+@pytest.mark.parametrize("name,q_len,D", [
+    ("qwen", 5, 128),    # 40 rows per KV head: one 48-row tile
+    ("qwen", 8, 128),    # 64 rows: one 64-row tile
+    ("qwen", 16, 128),   # 128 rows: two 64-row slices
+    ("llama", 16, 128),  # GQA 4:1, 64 rows
+    ("llama", 12, 64),   # head_dim 64, 48 rows
+    ("llama", 16, 64),   # head_dim 64, 64 rows
+])
+def test_verify_row_tiles(name, q_len, D):
+    """Windows whose row group (GQA group x window) needs 48- and 64-row tiles,
+    in causal overlap with the context end."""
+    base = CASES[name]()
+    w = W.spec(base.name, B=base.B, seq_lens=list(base.seq_lens), q_len=q_len, D=D)
+    c = Case(w)
+    start = np.maximum(c.b["positions"] - 7, 0).astype(np.int32)
+    lse = torch.empty((w.B, q_len, w.Hq), dtype=torch.float32, device="cuda")
+    out = kap.verify_attn(c.qv, t(start), c.K, c.V, c.bt, c.L, lse=lse)
+    torch.cuda.synchronize()
+    ref, lref = oracle.attend(c.b["qv"], start, c.Kl, c.Vl, c.btl,
+                              oracle.keys_full(c.b["seq_lens"]), 1, w.Hkv)
+    err = _check_attn(c, out, lse, ref, lref)
+    print(f"[{name} q_len {q_len} D {D}] verify max rel err {err:.2e}", flush=True)
+
+
 def test_verify_window_k_plus_one():
     """The KAP paper's verify window is k+1 tokens (carry + k drafts): q_len 5 on the tiny case."""
     w = W.spec("tiny", q_len=5)

@@ -16,6 +16,9 @@ Then, outside the per-request streams:
   6. physical placement: one permutation of the pool from
      default_rng(SeedSequence([seed, 1_000_003])); request b's logical page p
      lives at the next unused entry.
+  7. (draft_kv) the verify window's new K and V rows, [q_len][Hkv][D] each,
+     N(0, sigma^2), from default_rng(SeedSequence([seed, b, 2_000_029])), so
+     that drawing them changes nothing above.
 Needle keys: on every valid token of a needle page and every KV head g,
 K += alpha * dir[b][g], alpha = needle_scale * sigma * sqrt(D).  dir is taken
 from the caller when given; otherwise it is the unit vector along the sum of the
@@ -250,6 +253,18 @@ def make(w: Workload, needle_dir: Optional[np.ndarray] = None, with_kv: bool = T
         out["hidden"] = _to_bf16_bits(hidden)
         out["wq"] = _to_bf16_bits(wq)
     return out
+
+
+def draft_kv(w: Workload):
+    """K and V rows of the q_len window tokens (appended before the causal verify):
+    two [B][q_len][Hkv][D] arrays in the workload's storage type."""
+    shape = (w.q_len, w.Hkv, w.D)
+    ks, vs = [], []
+    for b in range(w.B):
+        rng = np.random.default_rng(np.random.SeedSequence([w.seed, b, 2_000_029]))
+        ks.append(rng.standard_normal(shape, dtype=np.float32) * np.float32(w.sigma))
+        vs.append(rng.standard_normal(shape, dtype=np.float32) * np.float32(w.sigma))
+    return _store(np.stack(ks), w.dtype), _store(np.stack(vs), w.dtype)
 
 
 def dense_pool(batch: dict):
