@@ -560,9 +560,10 @@ struct MergeArgs {
 
 // ------------------------------------------------------------------ merge
 // Block (b, g, query row r): IG item groups x D/4 threads (4 dims each).  Each
-// item group folds the items j = i0 + ig, i0 + ig + IG, ... (max, then the
-// e^(m_j - M) weighted sums); the groups are combined in group order through
-// LDS, so the result does not depend on scheduling.
+// item group folds the items j = i0 + ig, i0 + ig + IG, ... in one pass with a
+// running max (weights e^(m_j - M) rescaled as M grows); the groups are then
+// combined in group order through LDS, so the result does not depend on
+// scheduling.
 template <int D>
 __global__ __launch_bounds__(256) void attn_merge_kernel(MergeArgs a) {
   constexpr int TPR = D / 4, IG = 256 / TPR;
@@ -572,35 +573,39 @@ __global__ __launch_bounds__(256) void attn_merge_kernel(MergeArgs a) {
   const int i0 = a.row_off[bg], i1 = a.row_off[bg + 1];
   __shared__ float s_m[IG], s_l[IG];
   __shared__ floatx4 s_o[IG][TPR];
-  float m = -INFINITY;
-  for (int j = i0 + ig; j < i1; j += IG) m = fmaxf(m, a.part_ml[(int64_t)j * a.R + r].x);
-  if (t4 == 0) s_m[ig] = m;
-  __syncthreads();
-  float M = -INFINITY;
-#pragma unroll
-  for (int k = 0; k < IG; ++k) M = fmaxf(M, s_m[k]);
-  float L = 0.f;
+  float M = -INFINITY, L = 0.f;
   floatx4 O = {0.f, 0.f, 0.f, 0.f};
-  if (M != -INFINITY) {
 #pragma unroll 4
-    for (int j = i0 + ig; j < i1; j += IG) {
-      const float2 ml = a.part_ml[(int64_t)j * a.R + r];
-      const floatx4 o = *(const floatx4*)(a.part_o + ((int64_t)j * a.R + r) * D + d4);
-      const float w = exp2f(ml.x - M);  // 0 for items that saw no key (m = -inf)
-      L += w * ml.y;
-      O += w * o;
-    }
+  for (int j = i0 + ig; j < i1; j += IG) {
+    const float2 ml = a.part_ml[(int64_t)j * a.R + r];
+    const floatx4 o = *(const floatx4*)(a.part_o + ((int64_t)j * a.R + r) * D + d4);
+    const bool seen = ml.x != -INFINITY;  // an item that saw no key adds nothing
+    const float Mn = seen ? fmaxf(M, ml.x) : M;
+    const float sc = (M == -INFINITY) ? 0.f : exp2f(M - Mn);
+    const float w = seen ? exp2f(ml.x - Mn) : 0.f;
+    L = L * sc + w * ml.y;
+    O = O * sc + w * o;
+    M = Mn;
   }
-  if (t4 == 0) s_l[ig] = L;
+  if (t4 == 0) {
+    s_m[ig] = M;
+    s_l[ig] = L;
+  }
   s_o[ig][t4] = O;
   __syncthreads();
   if (ig != 0) return;
+  M = -INFINITY;
+#pragma unroll
+  for (int k = 0; k < IG; ++k) M = fmaxf(M, s_m[k]);
   L = 0.f;
   O = floatx4{0.f, 0.f, 0.f, 0.f};
+  if (M != -INFINITY) {
 #pragma unroll
-  for (int k = 0; k < IG; ++k) {
-    L += s_l[k];
-    O += s_o[k][t4];
+    for (int k = 0; k < IG; ++k) {
+      const float w = exp2f(s_m[k] - M);  // 0 for groups that saw no key
+      L += w * s_l[k];
+      O += w * s_o[k][t4];
+    }
   }
   const int i = r / a.grp, h = g * a.grp + r % a.grp;
   const int64_t orow = ((int64_t)b * a.q_len + i) * a.Hq + h;
