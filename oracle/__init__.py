@@ -51,6 +51,7 @@ def _load():
                                _I, _I, _I, _P, _P]
     lib.kor_num_threads.restype = _I
     lib.kor_append_kv.argtypes = [_P, _P, _I, _P, _I, _I, _I, _I, _I, _P, _P]
+    lib.kor_materialize.argtypes = [_P, _P, _I, _I, _I, _I, _P, _I, _I, _I, _P, _P, _P]
     _lib = lib
     return lib
 
@@ -264,3 +265,24 @@ def append_kv(k_new, v_new, slot, K, V, page_size: int = 16):
     B, q_new, Hkv, D = k_new.shape
     lib.kor_append_kv(_ptr(k_new), _ptr(v_new), _dt(K), _ptr(slot), B, q_new, Hkv, D, page_size,
                       _ptr(K), _ptr(V))
+
+
+def materialize(K, V, cbt, Kws=None, Vws=None, page_size: int = 16):
+    """Copy the compact view's pages into a workspace of B*cap pages (page b*cap + j,
+    head slot g = head g of compact page j of row (b, g or 0)).  Returns
+    (Kws, Vws, ws_table [B][G][cap])."""
+    lib = _load()
+    K = _c(K)
+    V = _c(V)
+    cbt = _c(cbt, np.int32)
+    B, G, cap = cbt.shape
+    P, Hkv, ps, D = K.shape
+    assert ps == page_size and _dt(K) == _dt(V)
+    if Kws is None:
+        Kws = np.zeros((B * cap,) + K.shape[1:], dtype=K.dtype)
+        Vws = np.zeros((B * cap,) + V.shape[1:], dtype=V.dtype)
+    assert Kws.flags.c_contiguous and Vws.flags.c_contiguous and Kws.shape[0] >= B * cap
+    table = np.empty_like(cbt)
+    lib.kor_materialize(_ptr(K), _ptr(V), _dt(K), Hkv, D, page_size, _ptr(cbt), B, G, cap,
+                        _ptr(Kws), _ptr(Vws), _ptr(table))
+    return Kws, Vws, table

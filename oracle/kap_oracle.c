@@ -396,3 +396,33 @@ void kor_append_kv(const void* k_new, const void* v_new, int kv_dt, const int64_
         }
     }
 }
+
+/*
+ * O5'. Compact KV workspace ([KAP] selected-KV view: the executor materializes
+ * a compact physical view of the selected pages; shape stabilization: a
+ * reusable compact KV workspace).  Workspace page b*cap + j holds, in head slot
+ * g, head g of compact page j of selection row (b, G == 1 ? 0 : g): K and V
+ * tiles are copied bit for bit.  ws_table[b][gr][j] = b*cap + j where
+ * cbt[b][gr][j] >= 0, else -1.  Workspace slots with no source stay untouched.
+ */
+void kor_materialize(const void* K, const void* V, int kv_dt, int Hkv, int D, int page_size,
+                     const int32_t* cbt, int B, int G, int cap, void* Kws, void* Vws,
+                     int32_t* ws_table) {
+  size_t eb = kv_dt == KOR_F32 ? 4 : 2;
+  size_t tile = (size_t)page_size * D * eb;   /* one (page, head) K or V tile */
+  for (int b = 0; b < B; b++)
+    for (int j = 0; j < cap; j++) {
+      int64_t dst = (int64_t)b * cap + j;
+      for (int g = 0; g < Hkv; g++) {
+        int gr = G == 1 ? 0 : g;
+        int32_t src = cbt[((int64_t)b * G + gr) * cap + j];
+        if (src < 0) continue;
+        memcpy((char*)Kws + (dst * Hkv + g) * tile, (const char*)K + ((int64_t)src * Hkv + g) * tile, tile);
+        memcpy((char*)Vws + (dst * Hkv + g) * tile, (const char*)V + ((int64_t)src * Hkv + g) * tile, tile);
+      }
+      for (int gr = 0; gr < G; gr++) {
+        int64_t t = ((int64_t)b * G + gr) * cap + j;
+        ws_table[t] = cbt[t] >= 0 ? (int32_t)dst : -1;
+      }
+    }
+}

@@ -422,6 +422,55 @@ def test_append_then_attend_sees_new_tokens():
     np.testing.assert_allclose(out[0, 0, 0], vn[0, 2, 0], atol=1e-7)
 
 
+def test_materialize_places_each_head_of_each_selected_page():
+    """Every K/V element encodes its (page, head); the workspace must show, in page
+    b*cap + j and head slot g, the code of compact page j of row (b, g or 0)."""
+    ps, H, D, P = 16, 4, 8, 12
+    code = (100 * np.arange(P)[:, None] + np.arange(H)[None, :]).astype(np.float32)  # [P][H]
+    K = np.broadcast_to(code[:, :, None, None], (P, H, ps, D)).copy()
+    V = np.broadcast_to(-code[:, :, None, None], (P, H, D, ps)).copy()
+    B, cap = 2, 3
+    for G in (1, H):
+        cbt = np.full((B, G, cap), -1, np.int32)
+        rng = np.random.default_rng(40 + G)
+        for b in range(B):
+            for gr in range(G):
+                n = int(rng.integers(1, cap + 1))
+                cbt[b, gr, :n] = rng.choice(P, size=n, replace=False)
+        Kws, Vws, tab = oracle.materialize(K, V, cbt)
+        for b in range(B):
+            for j in range(cap):
+                for g in range(H):
+                    src = cbt[b, 0 if G == 1 else g, j]
+                    want = 100 * src + g if src >= 0 else 0.0
+                    assert np.all(Kws[b * cap + j, g] == want) and np.all(Vws[b * cap + j, g] == -want)
+        expect = np.where(cbt >= 0, (np.arange(B)[:, None, None] * cap + np.arange(cap)[None, None, :]), -1)
+        np.testing.assert_array_equal(tab, np.broadcast_to(expect, cbt.shape))
+
+
+def test_attention_over_materialized_view_is_unchanged():
+    """Selected-page decode reads the same keys through the workspace table."""
+    rng = np.random.default_rng(41)
+    ps, H, Hq, D, P = 16, 2, 4, 8, 10
+    K = rng.standard_normal((P, H, ps, D)).astype(np.float32)
+    V = rng.standard_normal((P, H, D, ps)).astype(np.float32)
+    bt = rng.permutation(P).astype(np.int32)[None, :8]
+    L = [8 * ps - 5]
+    sel = np.array([[[0, 3, 7, -1]]], np.int32)
+    cnt = np.array([[3]], np.int32)
+    cbt, clog, clen, _ = oracle.compact(sel, cnt, bt, L, L, 0)
+    Kws, Vws, tab = oracle.materialize(K, V, cbt)
+    # the workspace view as a logical table: selected logical page -> workspace page
+    bt_ws = np.full_like(bt, -1)
+    bt_ws[0, clog[0, 0, :3]] = tab[0, 0, :3]
+    keys = oracle.keys_selected(sel, cnt, L)
+    q = rng.standard_normal((1, 1, Hq, D)).astype(np.float32)
+    o1, l1 = oracle.attend(q, L, K, V, bt, keys, 1, H)
+    o2, l2 = oracle.attend(q, L, Kws, Vws, bt_ws, keys, 1, H)
+    np.testing.assert_array_equal(o1, o2)
+    np.testing.assert_array_equal(l1, l2)
+
+
 # ----------------------------------------------------------------------------- cost model
 def test_phase_boundary_identity():
     rng = np.random.default_rng(12)
