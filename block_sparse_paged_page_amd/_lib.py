@@ -48,6 +48,8 @@ _SIGS = {
     "kap_update_summary": ([_P, _I32, _I32, _I32, _I32, _I32, _P, _I32, _P, _P, _I32, _I32, _P, _I32,
                             _P], _I32),
     "kap_append_kv": ([_P, _P, _I32, _P, _I32, _I32, _I32, _I32, _I32, _I32, _P, _P, _P], _I32),
+    "kap_materialize_view": ([_P, _P, _I32, _I32, _I32, _I32, _I32, _P, _I32, _I32, _I32, _P, _P,
+                              _I32, _P, _P], _I32),
 }
 _lib = None
 
@@ -270,3 +272,25 @@ def append_kv(k_new, v_new, slot_mapping, k_pool, v_pool, stream=None):
                            ps, num_pages, _p(k_pool), _p(v_pool), _stream(stream))
     _check(st, "kap_append_kv")
     return k_pool, v_pool
+
+
+def materialize_view(k_pool, v_pool, compact_bt, k_ws=None, v_ws=None, ws_table=None, stream=None):
+    """kap_materialize_view: copy the compact view's pages into a workspace of
+    B*capacity pages; returns (k_ws, v_ws, ws_table)."""
+    lib = load()
+    num_pages, Hkv, ps, D = k_pool.shape
+    B, G, cap = compact_bt.shape
+    if k_ws is None:
+        k_ws = torch.empty((B * cap,) + tuple(k_pool.shape[1:]), dtype=k_pool.dtype, device=k_pool.device)
+        v_ws = torch.empty((B * cap,) + tuple(v_pool.shape[1:]), dtype=v_pool.dtype, device=v_pool.device)
+    if ws_table is None:
+        ws_table = torch.empty_like(compact_bt)
+    if _dt(k_ws) != _dt(k_pool) or _dt(v_ws) != _dt(v_pool) or _dt(k_pool) != _dt(v_pool):
+        raise ValueError("workspace and pool dtypes differ")
+    if tuple(k_ws.shape[1:]) != tuple(k_pool.shape[1:]) or tuple(v_ws.shape[1:]) != tuple(v_pool.shape[1:]):
+        raise ValueError("workspace page shape differs from the pool's")
+    st = lib.kap_materialize_view(_p(k_pool), _p(v_pool), _dt(k_pool), num_pages, Hkv, D, ps,
+                                  _p(compact_bt), B, G, cap, _p(k_ws), _p(v_ws), k_ws.shape[0],
+                                  _p(ws_table), _stream(stream))
+    _check(st, "kap_materialize_view")
+    return k_ws, v_ws, ws_table

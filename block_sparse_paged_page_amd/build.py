@@ -12,7 +12,7 @@ HERE = os.path.dirname(os.path.abspath(__file__))
 CSRC = os.path.join(HERE, "csrc")
 LIB = os.path.join(HERE, "libkap.so")
 SOURCES = ["kap_api.hip", "attn.hip", "score.hip", "select.hip", "compact.hip", "proxy.hip",
-           "append.hip", "diag.hip"]
+           "kvcopy.hip", "diag.hip"]
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 
 FLAGS = [

@@ -318,6 +318,29 @@ kap_status kap_update_summary(const void* k_pool, int32_t kv_dtype, int32_t num_
                         positions, q_new, B, summary, (kap_dtype)sum_dtype, (hipStream_t)stream);
 }
 
+kap_status kap_materialize_view(const void* k_pool, const void* v_pool, int32_t kv_dtype,
+                                int32_t num_pages, int32_t Hkv, int32_t D, int32_t page_size,
+                                const int32_t* compact_bt, int32_t B, int32_t G, int32_t capacity,
+                                void* k_ws, void* v_ws, int32_t ws_pages, int32_t* ws_table,
+                                kap_stream stream) {
+  g_err[0] = 0;
+  if (B < 0 || capacity < 0 || num_pages < 0 || ws_pages < 0 || Hkv <= 0 || Hkv > 256)
+    return fail(KAP_ERR_INVALID_ARG, "bad size");
+  if (G != 1 && G != Hkv) return fail(KAP_ERR_INVALID_ARG, "G %d must be 1 or Hkv (%d)", G, Hkv);
+  if (D != 64 && D != 128) return fail(KAP_ERR_UNSUPPORTED, "head_dim %d (64 or 128)", D);
+  if (page_size != kPage) return fail(KAP_ERR_UNSUPPORTED, "page_size %d (16)", page_size);
+  if (!dtype_ok(kv_dtype)) return fail(KAP_ERR_UNSUPPORTED, "dtype %d", kv_dtype);
+  if ((int64_t)B * capacity > ws_pages)
+    return fail(KAP_ERR_WORKSPACE, "workspace holds %d pages, B * capacity = %lld", ws_pages,
+                (long long)B * capacity);
+  if (B == 0 || capacity == 0) return KAP_OK;
+  if (capacity > 65535 || B > 65535) return fail(KAP_ERR_UNSUPPORTED, "grid too large");
+  if (!k_pool || !v_pool || !compact_bt || !k_ws || !v_ws || !ws_table)
+    return fail(KAP_ERR_INVALID_ARG, "null pointer");
+  return launch_materialize(k_pool, v_pool, (kap_dtype)kv_dtype, Hkv, D, compact_bt, B, G,
+                            capacity, k_ws, v_ws, ws_table, (hipStream_t)stream);
+}
+
 kap_status kap_append_kv(const void* k_new, const void* v_new, int32_t kv_dtype,
                          const int64_t* slot_mapping, int32_t B, int32_t q_new, int32_t Hkv,
                          int32_t D, int32_t page_size, int32_t num_pages, void* k_pool,

@@ -130,6 +130,9 @@ kap_status launch_summary(const void* k, kap_dtype kv_dt, int32_t Hkv, int32_t D
                           const int32_t* bt, int32_t max_pages, const int32_t* seq_lens,
                           const int32_t* first_pos, int32_t q_new, int32_t B, void* summ,
                           kap_dtype s_dt, hipStream_t stream);
+kap_status launch_materialize(const void* k, const void* v, kap_dtype dt, int32_t Hkv, int32_t D,
+                              const int32_t* cbt, int32_t B, int32_t G, int32_t cap, void* kws,
+                              void* vws, int32_t* ws_table, hipStream_t stream);
 kap_status launch_append(const void* k_new, const void* v_new, kap_dtype dt, const int64_t* slot,
                          int32_t B, int32_t q_new, int32_t Hkv, int32_t D, int64_t num_slots,
                          void* k, void* v, hipStream_t stream);

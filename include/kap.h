@@ -258,6 +258,28 @@ KAP_API kap_status kap_update_summary(const void* k_pool, int32_t kv_dtype, int3
                                       kap_stream stream);
 
 /*
+ * Compact KV workspace ([KAP] selected-KV view: the executor materializes a
+ * compact physical view of the selected pages; [KAP] shape stabilization: a
+ * reusable compact KV workspace, filled once per plan).  Workspace page
+ * b*capacity + j receives, in head slot g, head g of compact page j of row
+ * (b, G == 1 ? 0 : g) -- K and V tiles copied bit for bit -- and
+ * ws_table[b][gr][j] = b*capacity + j where compact_bt[b][gr][j] >= 0, else -1.
+ * kap_decode_attn over (k_ws, v_ws, ws_table, compact_len) then gives the same
+ * bits as over (k_pool, v_pool, compact_bt, compact_len), reading contiguous
+ * workspace pages instead of scattered pool pages.  Workspace slots without a
+ * source page are left as they were.
+ *   compact_bt device [B][G][capacity] (kap_compact_view); G is 1 or Hkv
+ *   k_ws, v_ws device [ws_pages][Hkv][16][D] and [ws_pages][Hkv][D][16], kv_dtype;
+ *     ws_pages >= B * capacity, else KAP_ERR_WORKSPACE
+ *   ws_table device out [B][G][capacity]
+ */
+KAP_API kap_status kap_materialize_view(const void* k_pool, const void* v_pool, int32_t kv_dtype,
+                                        int32_t num_pages, int32_t Hkv, int32_t D,
+                                        int32_t page_size, const int32_t* compact_bt, int32_t B,
+                                        int32_t G, int32_t capacity, void* k_ws, void* v_ws,
+                                        int32_t ws_pages, int32_t* ws_table, kap_stream stream);
+
+/*
  * KV append through a slot mapping ([KAP] verifier: verification advances the
  * committed full-context KV state; [KAP] selected-KV view: slot mappings place
  * newly scheduled tokens into their physical KV slots).  Token i of request b

@@ -172,6 +172,16 @@ def test_append_and_summary_update_validation(lib):
     assert up(None, 1, 100, 8, 128, 16, None, 64, None, None, 0, 2, None, 1, None) == OK
 
 
+def test_materialize_validation(lib):
+    m = lib.kap_materialize_view
+    #        k   v  dt pages Hkv D   ps cbt  B  G  cap kws vws wsp tab stream
+    assert m(NP, NP, 1, 100, 8, 128, 16, NP, 2, 1, 10, NP, NP, 19, NP, None) == WORKSPACE
+    assert m(NP, NP, 1, 100, 8, 128, 16, NP, 2, 3, 10, NP, NP, 20, NP, None) == INVALID
+    assert m(NP, NP, 1, 100, 8, 96, 16, NP, 2, 1, 10, NP, NP, 20, NP, None) == UNSUPPORTED
+    assert m(NP, NP, 1, 100, 8, 128, 16, None, 2, 1, 10, NP, NP, 20, NP, None) == INVALID
+    assert m(None, None, 1, 100, 8, 128, 16, None, 0, 1, 10, None, None, 0, None, None) == OK
+
+
 def test_product_binding_never_imports_oracle():
     pkg = os.path.join(ROOT, "block_sparse_paged_page_amd")
     for dirpath, _, files in os.walk(pkg):
