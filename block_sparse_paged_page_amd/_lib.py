@@ -3,6 +3,7 @@ import ctypes
 import math
 import os
 
+import numpy as np
 import torch
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
@@ -50,6 +51,11 @@ _SIGS = {
     "kap_append_kv": ([_P, _P, _I32, _P, _I32, _I32, _I32, _I32, _I32, _I32, _P, _P, _P], _I32),
     "kap_materialize_view": ([_P, _P, _I32, _I32, _I32, _I32, _I32, _P, _I32, _I32, _I32, _P, _P,
                               _I32, _P, _P], _I32),
+    "kap_host_proxy_query": ([_P, _P, _I32, _I32, _I32, _P, _I32], _I32),
+    "kap_host_score_blocks": ([_P, _P, ctypes.c_float, _P, _I32, _P, _I32, _P, _I32, _I32, _I32,
+                               _I32, _I32, _P, _I32], _I32),
+    "kap_host_select_topk": ([_P, _I32, _I32, _I32, _P, _I32, _I32, _P, _P, _P, _I32, _P, _P,
+                              _I32], _I32),
 }
 _lib = None
 
@@ -294,3 +300,73 @@ def materialize_view(k_pool, v_pool, compact_bt, k_ws=None, v_ws=None, ws_table=
                                   _p(ws_table), _stream(stream))
     _check(st, "kap_materialize_view")
     return k_ws, v_ws, ws_table
+
+
+# ----------------------------------------------------------------------------- host routing
+# CPU-offloaded early routing: numpy arrays in host memory, results in host
+# memory (to be uploaded as page indices).  Synchronous; ctypes releases the
+# GIL for the call, so a Python thread can route while the GPU works.
+def _h(a, dtype):
+    a = np.asarray(a)
+    if a.dtype != dtype:
+        raise TypeError(f"expected {np.dtype(dtype).name}, got {a.dtype}")
+    if not a.flags.c_contiguous:
+        raise ValueError("host arrays must be C-contiguous")
+    return a
+
+
+def _hp(a):
+    return ctypes.c_void_p(a.ctypes.data)
+
+
+def host_proxy_query(hidden, w_q, q_out=None, threads=0):
+    """kap_host_proxy_query: hidden [B][d_model], w_q [d_model][n] bf16 bits (uint16) -> fp32 [B][n]."""
+    hidden = _h(hidden, np.uint16)
+    w_q = _h(w_q, np.uint16)
+    B, dm = hidden.shape
+    n = w_q.shape[1]
+    if q_out is None:
+        q_out = np.empty((B, n), np.float32)
+    q_out = _h(q_out, np.float32)
+    _check(load().kap_host_proxy_query(_hp(hidden), _hp(w_q), B, dm, n, _hp(q_out), threads),
+           "kap_host_proxy_query")
+    return q_out
+
+
+def host_score_blocks(q, positions, summary, block_table, seq_lens, Hkv, theta=1e4, scores=None,
+                      threads=0):
+    """kap_host_score_blocks: q [B][Hq][D] fp32, summary [P][Hkv][D] bf16 bits -> [B][Hkv][max_pages]."""
+    q = _h(q, np.float32)
+    summary = _h(summary, np.uint16)
+    block_table = _h(block_table, np.int32)
+    positions = _h(positions, np.int32)
+    seq_lens = _h(seq_lens, np.int32)
+    B, Hq, D = q.shape
+    max_pages = block_table.shape[1]
+    if scores is None:
+        scores = np.empty((B, Hkv, max_pages), np.float32)
+    scores = _h(scores, np.float32)
+    _check(load().kap_host_score_blocks(_hp(q), _hp(positions), theta, _hp(summary),
+                                        summary.shape[0], _hp(block_table), max_pages,
+                                        _hp(seq_lens), B, Hq, Hkv, D, 16, _hp(scores), threads),
+           "kap_host_score_blocks")
+    return scores
+
+
+def host_select_topk(scores, seq_lens, anchor, recent, k_mid, capacity, per_head=False, sel=None,
+                     cnt=None, threads=0):
+    """kap_host_select_topk: same selection as select_topk, on host arrays."""
+    scores = _h(scores, np.float32)
+    seq_lens, anchor = _h(seq_lens, np.int32), _h(anchor, np.int32)
+    recent, k_mid = _h(recent, np.int32), _h(k_mid, np.int32)
+    B, Hkv, max_pages = scores.shape
+    G = Hkv if per_head else 1
+    if sel is None:
+        sel = np.empty((B, G, capacity), np.int32)
+        cnt = np.empty((B, G), np.int32)
+    sel, cnt = _h(sel, np.int32), _h(cnt, np.int32)
+    _check(load().kap_host_select_topk(_hp(scores), B, Hkv, max_pages, _hp(seq_lens), 16,
+                                       int(per_head), _hp(anchor), _hp(recent), _hp(k_mid),
+                                       capacity, _hp(sel), _hp(cnt), threads),
+           "kap_host_select_topk")
+    return sel, cnt

@@ -13,7 +13,11 @@ CSRC = os.path.join(HERE, "csrc")
 LIB = os.path.join(HERE, "libkap.so")
 SOURCES = ["kap_api.hip", "attn.hip", "score.hip", "select.hip", "compact.hip", "proxy.hip",
            "kvcopy.hip", "diag.hip"]
+HOST_SOURCES = ["host_route.cpp"]  # host-only C++ (CPU-offloaded routing)
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
+CXX = os.environ.get("CXX", "g++")
+HOST_FLAGS = ["-O3", "-std=c++17", "-fPIC", "-Wall", "-fvisibility=hidden", "-pthread",
+              "-I", os.path.join(os.path.dirname(HERE), "include")]
 
 FLAGS = [
     "--offload-arch=gfx950", "-O3", "-std=c++17", "-fPIC", "-Wall",
@@ -36,9 +40,16 @@ def build(verbose: bool = False, jobs: int = 6) -> str:
         procs.append((src, subprocess.Popen(cmd, stdout=subprocess.PIPE, stderr=subprocess.STDOUT)))
         if len(procs) >= jobs:
             _wait(procs.pop(0))
+    for src in HOST_SOURCES:
+        obj = os.path.join(objdir, src.replace(".cpp", ".o"))
+        objs.append(obj)
+        cmd = [CXX] + HOST_FLAGS + ["-c", os.path.join(CSRC, src), "-o", obj]
+        if verbose:
+            print(" ".join(cmd), flush=True)
+        procs.append((src, subprocess.Popen(cmd, stdout=subprocess.PIPE, stderr=subprocess.STDOUT)))
     for p in procs:
         _wait(p)
-    link = [HIPCC, "--offload-arch=gfx950", "-shared", "-fPIC", "-o", LIB + ".tmp"] + objs
+    link = [HIPCC, "--offload-arch=gfx950", "-shared", "-fPIC", "-pthread", "-o", LIB + ".tmp"] + objs
     if verbose:
         print(" ".join(link), flush=True)
     subprocess.run(link, check=True)
@@ -55,7 +66,7 @@ def _wait(entry):
     if lines:
         print("\n".join(lines), flush=True)
     if p.returncode != 0:
-        raise RuntimeError(f"hipcc failed on {src}")
+        raise RuntimeError(f"compiler failed on {src}")
 
 
 if __name__ == "__main__":

@@ -299,6 +299,40 @@ KAP_API kap_status kap_append_kv(const void* k_new, const void* v_new, int32_t k
                                  void* k_pool, void* v_pool, kap_stream stream);
 
 /*
+ * CPU-offloaded early routing ([ESKV] Interpretation: once indices are
+ * available early, proxy-query construction, routing and the K-summary state
+ * can move to the CPU and finish before target attention; the GPU keeps the
+ * KV and receives only page indices).  Same definitions as kap_proxy_query,
+ * kap_score_blocks and kap_select_topk, computed on host threads over HOST
+ * memory; every pointer below is host memory.  Synchronous; `threads` <= 0
+ * means OMP_NUM_THREADS, else the CPUs this process may run on.  The GPU side
+ * takes sel_pages / sel_count as uploaded indices (copy them to the device,
+ * then kap_compact_view).
+ *   kap_host_proxy_query: q_out [B][n_out] fp32 = hidden [B][d_model] (bf16)
+ *     . w_q [d_model][n_out] (bf16); fp32 sums in index order; B <= 64.
+ *   kap_host_score_blocks: q [B][Hq][D] fp32 (unrotated), summary
+ *     [num_pages][Hkv][D] bf16, scores [B][Hkv][max_pages] (-inf past N_b);
+ *     rotation and group sum in fp64, dot in fp64, one rounding to fp32.
+ *   kap_host_select_topk: as kap_select_topk, bit-identical on the same scores;
+ *     returns KAP_ERR_CAPACITY if some request's a + r + k exceeds capacity.
+ */
+KAP_API kap_status kap_host_proxy_query(const uint16_t* hidden, const uint16_t* w_q, int32_t B,
+                                        int32_t d_model, int32_t n_out, float* q_out,
+                                        int32_t threads);
+KAP_API kap_status kap_host_score_blocks(const float* q, const int32_t* positions,
+                                         float rope_theta, const uint16_t* summary,
+                                         int32_t num_pages, const int32_t* block_table,
+                                         int32_t max_pages, const int32_t* seq_lens, int32_t B,
+                                         int32_t Hq, int32_t Hkv, int32_t D, int32_t page_size,
+                                         float* scores, int32_t threads);
+KAP_API kap_status kap_host_select_topk(const float* scores, int32_t B, int32_t Hkv,
+                                        int32_t max_pages, const int32_t* seq_lens,
+                                        int32_t page_size, int32_t per_head,
+                                        const int32_t* anchor, const int32_t* recent,
+                                        const int32_t* k_mid, int32_t capacity,
+                                        int32_t* sel_pages, int32_t* sel_count, int32_t threads);
+
+/*
  * Diagnostic, not part of the path: reads `bytes` (a multiple of 16) of device
  * memory with 16-byte loads from a 2048 x 256 grid-stride kernel, the load
  * shape of the attention kernels.  Timing it gives the sustained read
