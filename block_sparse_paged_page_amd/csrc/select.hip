@@ -72,7 +72,7 @@ __global__ __launch_bounds__(1024) void select_kernel(SelArgs a) {
   const int G = a.per_head ? a.Hkv : 1;
   const int tid = threadIdx.x;
   __shared__ int s_hist[16][256];  // one private histogram per wave
-  __shared__ int s_suf[8];
+  __shared__ int s_suf[8];  // [0..3] wave totals, [4] keys above the bin, [5] keys in the bin
   __shared__ int s_wave[33];
   __shared__ uint32_t s_digit;
   const int N = min((max(a.seq_lens[b], 0) + kPage - 1) / kPage, a.max_pages);
@@ -94,7 +94,8 @@ __global__ __launch_bounds__(1024) void select_kernel(SelArgs a) {
   if constexpr (STAGED) {
     extern __shared__ float s_key[];  // [max_pages]
     if (!all) {
-      // up to 8 heads x 4 pages of loads in flight per thread, folded in head order
+      // up to 8 heads x 4 pages of loads in flight per thread (more would not
+      // fit the 128 registers of a 1024-thread block), folded in head order
       constexpr int SU = 4, SG = 8;
       for (int p0 = mid_lo; p0 < mid_hi; p0 += 1024 * SU) {
         float v[SU];
@@ -167,6 +168,7 @@ __global__ __launch_bounds__(1024) void select_kernel(SelArgs a) {
   // ---- radix select of the take-th largest candidate key
   uint32_t prefix = 0, pmask = 0;
   int remaining = take;
+  int bin_count = 0;  // keys in the chosen bin of the last pass: after shift 0, those equal to T
   if (take > 0) {
     for (int shift = 24; shift >= 0; shift -= 8) {
       for (int e = tid; e < 16 * 256; e += 1024) (&s_hist[0][0])[e] = 0;
@@ -197,11 +199,13 @@ __global__ __launch_bounds__(1024) void select_kernel(SelArgs a) {
         if (suf >= remaining && above < remaining) {
           s_digit = tid;
           s_suf[4] = above;
+          s_suf[5] = h;
         }
       }
       __syncthreads();
       const uint32_t d = s_digit;
       remaining -= s_suf[4];
+      bin_count = s_suf[5];
       prefix |= d << shift;
       pmask |= 0xffu << shift;
       __syncthreads();
@@ -209,13 +213,18 @@ __global__ __launch_bounds__(1024) void select_kernel(SelArgs a) {
   }
   const uint32_t T = prefix;
 
-  // ---- ties at T: lowest indices first
-  int n_eq = 0;
+  // ---- ties at T: lowest indices first.  When every key equal to T is taken
+  // (the usual case: the last pass's bin holds exactly the remaining count),
+  // no ranks are needed; the test is block-uniform.
+  int eq_rank = 0;
+  if (take > 0 && bin_count != remaining) {
+    int n_eq = 0;
 #pragma unroll
-  for (int j = 0; j < KPT; ++j)
-    if (take > 0 && ((cand >> j) & 1ull) && key[j] == T) ++n_eq;
-  int tot;
-  int eq_rank = block_exclusive_scan(n_eq, s_wave, &tot);
+    for (int j = 0; j < KPT; ++j)
+      if (((cand >> j) & 1ull) && key[j] == T) ++n_eq;
+    int tot;
+    eq_rank = block_exclusive_scan(n_eq, s_wave, &tot);
+  }
 
   uint64_t chosen = 0;
 #pragma unroll
