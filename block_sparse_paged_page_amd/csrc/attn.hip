@@ -180,6 +180,8 @@ struct PartArgs {
 // reference, so the merged result is the same softmax.
 constexpr float kLazyRescale = 8.0f;
 
+typedef unsigned int u32x2v __attribute__((ext_vector_type(2)));
+
 template <int D>
 struct PageFrag {
   uint4 k[D / 32];
@@ -251,10 +253,17 @@ __global__ __launch_bounds__(64) void attn_partial_bf16(PartArgs a) {
     for (int c = 0; c < NC; ++c) f.v[c] = *(const uint2*)(vp + 16 * kPage * c);
   };
 
-  PageFrag<D> buf0, buf1, buf2;
+  // four page buffers: two pairs, one pair's loads in flight while the other
+  // pair is consumed
+  PageFrag<D> buf0, buf1, buf2, buf3;
+#pragma unroll
+  for (int s = 0; s < KS; ++s) buf0.k[s] = buf1.k[s] = buf2.k[s] = buf3.k[s] = make_uint4(0, 0, 0, 0);
+#pragma unroll
+  for (int c = 0; c < NC; ++c) buf0.v[c] = buf1.v[c] = buf2.v[c] = buf3.v[c] = make_uint2(0, 0);
   if (p0 < p1) load_page(p0, buf0);
   if (p0 + 1 < p1) load_page(p0 + 1, buf1);
   if (p0 + 2 < p1) load_page(p0 + 2, buf2);
+  if (p0 + 3 < p1) load_page(p0 + 3, buf3);
 
   // This slice's query rows, rotated at their positions, as LDS fragments in
   // the B-operand layout of S^T = K Q^T (row l16, dims 32 s + 8 q4 .. + 7).
@@ -311,10 +320,10 @@ __global__ __launch_bounds__(64) void attn_partial_bf16(PartArgs a) {
     for (int c = 0; c < NC; ++c) o[t][c] = floatx4{0.f, 0.f, 0.f, 0.f};
   }
 
-  auto consume = [&](int p, PageFrag<D>& f) {
-    const int tok0 = p * kPage + 4 * q4;
+  // Invisible slots of a partial last page may hold anything: zero their V.
+  auto mask_v = [&](int p, PageFrag<D>& f) {
     const int nvalid = len - p * kPage;
-    if (nvalid < kPage) {  // partial last page: invisible slots may hold anything
+    if (nvalid < kPage) {
 #pragma unroll
       for (int c = 0; c < NC; ++c) {
         uint32_t lo = f.v[c].x, hi = f.v[c].y;
@@ -326,33 +335,53 @@ __global__ __launch_bounds__(64) void attn_partial_bf16(PartArgs a) {
         f.v[c] = make_uint2(lo, hi);
       }
     }
-    // re-read the query fragments from LDS every page (an opaque index keeps
+  };
+
+  // One pair of pages (p, p + 1).  S^T for each page on 16x16x32 MFMAs; one
+  // softmax reference per pair; then O^T += V^T P^T over the pair's 32 tokens
+  // on 16x16x32 MFMAs, with contraction index 8 q4 + e standing for token
+  // 4 q4 + e of page p (e < 4) or 4 q4 + e - 4 of page p + 1 (e >= 4): the
+  // lane's V^T operand is its two 8-byte V loads side by side, its P^T operand
+  // its two groups of 4 probabilities.  When page p + 1 is not part of the
+  // item (hb false) its scores are masked and its buffer holds finite values
+  // (zeros or an earlier, already masked page), so it adds nothing.
+  auto consume2 = [&](int p, PageFrag<D>& fa, PageFrag<D>& fb, bool hb) {
+    mask_v(p, fa);
+    mask_v(p + 1, fb);
+    // re-read the query fragments from LDS every pair (an opaque index keeps
     // the compiler from hoisting them into registers)
     int ql = lane;
     asm volatile("" : "+v"(ql));
     // The NT row tiles are independent: each stage runs across all tiles
     // before the next, so one tile's MFMA latency hides behind another's
     // VALU work, and one wave-wide vote decides the rare reference move.
-    floatx4 sacc[NT];
+    floatx4 sa[NT], sb[NT];
 #pragma unroll
-    for (int t = 0; t < NT; ++t) sacc[t] = floatx4{0.f, 0.f, 0.f, 0.f};
+    for (int t = 0; t < NT; ++t) {
+      sa[t] = floatx4{0.f, 0.f, 0.f, 0.f};
+      sb[t] = floatx4{0.f, 0.f, 0.f, 0.f};
+    }
 #pragma unroll
     for (int s = 0; s < KS; ++s)
 #pragma unroll
-      for (int t = 0; t < NT; ++t)
-        sacc[t] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, f.k[s]),
-                                                         __builtin_bit_cast(bf16x8, sq[t][s][ql]),
-                                                         sacc[t], 0, 0, 0);
-    float z[NT][4], mx[NT];
+      for (int t = 0; t < NT; ++t) {
+        const bf16x8 qf = __builtin_bit_cast(bf16x8, sq[t][s][ql]);
+        sa[t] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, fa.k[s]), qf,
+                                                       sa[t], 0, 0, 0);
+        sb[t] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, fb.k[s]), qf,
+                                                       sb[t], 0, 0, 0);
+      }
+    const int tok0 = p * kPage + 4 * q4;
+    float za[NT][4], zb[NT][4], mx[NT];
 #pragma unroll
     for (int t = 0; t < NT; ++t) {
       mx[t] = -INFINITY;
 #pragma unroll
       for (int j = 0; j < 4; ++j) {
-        const int tok = tok0 + j;
-        const bool vis = tok < len && tok <= qpos[t];
-        z[t][j] = vis ? sacc[t][j] * a.scale_log2 : -INFINITY;
-        mx[t] = fmaxf(mx[t], z[t][j]);
+        const int ta = tok0 + j, tb = tok0 + kPage + j;
+        za[t][j] = (ta < len && ta <= qpos[t]) ? sa[t][j] * a.scale_log2 : -INFINITY;
+        zb[t][j] = (hb && tb < len && tb <= qpos[t]) ? sb[t][j] * a.scale_log2 : -INFINITY;
+        mx[t] = fmaxf(mx[t], fmaxf(za[t][j], zb[t][j]));
       }
     }
 #pragma unroll
@@ -376,38 +405,41 @@ __global__ __launch_bounds__(64) void attn_partial_bf16(PartArgs a) {
         m[t] = mn;
       }
     }
-    short4v pf[NT];
+    bf16x8 pf[NT];
 #pragma unroll
     for (int t = 0; t < NT; ++t) {
-      float pj[4];
+      float pa[4], pb[4];
       float psum = 0.f;
 #pragma unroll
       for (int j = 0; j < 4; ++j) {
-        pj[j] = (z[t][j] == -INFINITY) ? 0.f : __builtin_amdgcn_exp2f(z[t][j] - m[t]);
-        psum += pj[j];
+        pa[j] = (za[t][j] == -INFINITY) ? 0.f : __builtin_amdgcn_exp2f(za[t][j] - m[t]);
+        pb[j] = (zb[t][j] == -INFINITY) ? 0.f : __builtin_amdgcn_exp2f(zb[t][j] - m[t]);
+        psum += pa[j] + pb[j];
       }
       l[t] += psum;
-      pf[t] = __builtin_bit_cast(short4v,
-                                 make_uint2(pack_bf16x2(pj[0], pj[1]), pack_bf16x2(pj[2], pj[3])));
+      pf[t] = __builtin_bit_cast(bf16x8, make_uint4(pack_bf16x2(pa[0], pa[1]), pack_bf16x2(pa[2], pa[3]),
+                                                    pack_bf16x2(pb[0], pb[1]), pack_bf16x2(pb[2], pb[3])));
     }
 #pragma unroll
-    for (int c = 0; c < NC; ++c)
+    for (int c = 0; c < NC; ++c) {
+      // the two pages' 8-byte V loads side by side (as native vectors: kept in registers)
+      const bf16x8 vf = __builtin_bit_cast(
+          bf16x8, __builtin_shufflevector(__builtin_bit_cast(u32x2v, fa.v[c]),
+                                          __builtin_bit_cast(u32x2v, fb.v[c]), 0, 1, 2, 3));
 #pragma unroll
       for (int t = 0; t < NT; ++t)
-        o[t][c] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(__builtin_bit_cast(short4v, f.v[c]),
-                                                           pf[t], o[t][c], 0, 0, 0);
+        o[t][c] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(vf, pf[t], o[t][c], 0, 0, 0);
+    }
   };
 
-  for (int p = p0; p < p1; p += 3) {
-    consume(p, buf0);
-    if (p + 3 < p1) load_page(p + 3, buf0);
-    if (p + 1 < p1) {
-      consume(p + 1, buf1);
-      if (p + 4 < p1) load_page(p + 4, buf1);
-    }
+  for (int p = p0; p < p1; p += 4) {
+    consume2(p, buf0, buf1, p + 1 < p1);
+    if (p + 4 < p1) load_page(p + 4, buf0);
+    if (p + 5 < p1) load_page(p + 5, buf1);
     if (p + 2 < p1) {
-      consume(p + 2, buf2);
-      if (p + 5 < p1) load_page(p + 5, buf2);
+      consume2(p + 2, buf2, buf3, p + 3 < p1);
+      if (p + 6 < p1) load_page(p + 6, buf2);
+      if (p + 7 < p1) load_page(p + 7, buf3);
     }
   }
 #pragma unroll
