@@ -49,9 +49,9 @@ def parse():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--quiet", action="store_true")
     ap.add_argument("--workload", default="qwen32b_128k",
-                    choices=["qwen32b_128k", "qwen32b_128k_commit", "qwen32b_128k_workspace",
-                             "llama8b_32k", "early_route_40k", "early_route_40k_cpu",
-                             "mixed_serving"],
+                    choices=["qwen32b_128k", "qwen32b_128k_sweep", "qwen32b_128k_commit",
+                             "qwen32b_128k_workspace", "llama8b_32k", "early_route_40k",
+                             "early_route_40k_cpu", "mixed_serving"],
                     help="qwen32b_128k is the headline line; the others print their own "
                          "measurement lines")
     return ap.parse_args()
@@ -106,9 +106,10 @@ def read_traffic(kernel_key):
     return None
 
 
-def cpu_baseline(w, b, K, V, sel_budget, quiet, min_s=10.0, max_s=30.0):
+def cpu_baseline(w, b, K, V, sel_budget, quiet, min_s=10.0, max_s=30.0, one_core_s=8.0):
     """Oracle cycles (route + 4 selected decodes + one verify) over the batch's
-    requests in turn, until at least min_s seconds of CPU work have run."""
+    requests in turn, until at least min_s seconds of CPU work have run, on all
+    of the process's threads; then a shorter leg on one thread."""
     import oracle
     T0 = time.time()
     NA = w.alloc_pages
@@ -123,29 +124,40 @@ def cpu_baseline(w, b, K, V, sel_budget, quiet, min_s=10.0, max_s=30.0):
         summ = oracle.round_to_bf16(oracle.summary(Kh, btl, Lb))
         host.append((Kh, Vh, btl, Lb, summ))
     log(f"cpu baseline inputs ready in {time.time() - T0:.1f}s", quiet)
+    def run(budget_s):
+        done = 0
+        t0 = time.perf_counter()
+        while True:
+            bi = done % w.B
+            Kh, Vh, btl, Lb, summ = host[bi]
+            sl = slice(bi, bi + 1)
+            s = oracle.score(b["q"][sl], b["positions"][sl], summ, btl, Lb, w.Hkv)
+            sel, cnt = oracle.select(s.astype(np.float32), Lb, b["anchor"][sl], b["recent"][sl],
+                                     b["k_mid"][sl], sel_budget)
+            oracle.compact(sel, cnt, btl, Lb, b["positions"][sl], 1)
+            keys = oracle.keys_selected(sel, cnt, Lb)
+            for j in range(K_PROPOSE):
+                oracle.attend(b["qv"][sl, j:j + 1], b["positions"][sl] + j, Kh, Vh, btl, keys, 1,
+                              w.Hkv)
+            oracle.attend(b["qv"][sl], b["positions"][sl], Kh, Vh, btl, oracle.keys_full(Lb), 1,
+                          w.Hkv)
+            done += 1
+            dt = time.perf_counter() - t0
+            if dt >= budget_s or (dt >= max_s / 2 and done >= 1):
+                return done, dt
+
     threads = oracle.num_threads()
-    done = 0
-    t0 = time.perf_counter()
-    while True:
-        bi = done % w.B
-        Kh, Vh, btl, Lb, summ = host[bi]
-        sl = slice(bi, bi + 1)
-        s = oracle.score(b["q"][sl], b["positions"][sl], summ, btl, Lb, w.Hkv)
-        sel, cnt = oracle.select(s.astype(np.float32), Lb, b["anchor"][sl], b["recent"][sl],
-                                 b["k_mid"][sl], sel_budget)
-        oracle.compact(sel, cnt, btl, Lb, b["positions"][sl], 1)
-        keys = oracle.keys_selected(sel, cnt, Lb)
-        for j in range(K_PROPOSE):
-            oracle.attend(b["qv"][sl, j:j + 1], b["positions"][sl] + j, Kh, Vh, btl, keys, 1, w.Hkv)
-        oracle.attend(b["qv"][sl], b["positions"][sl], Kh, Vh, btl, oracle.keys_full(Lb), 1, w.Hkv)
-        done += 1
-        dt = time.perf_counter() - t0
-        if dt >= min_s or (dt >= max_s / 2 and done >= 1):
-            break
+    done, dt = run(min_s)
+    oracle.set_threads(1)
+    done1, dt1 = run(one_core_s)
+    oracle.set_threads(threads)
+    what = ("request-cycles of the same batch (requests taken in turn): each is score+select+"
+            "compact over 8192 pages, 4 selected-KV decodes over 451 pages and one 4-query verify "
+            "over 131072 tokens")
     return dict(value=round(K_PROPOSE * done / dt, 3), unit="tokens/s", cores=threads, kind="oracle",
-                sample=(f"{done} request-cycles of the same batch (requests taken in turn): each "
-                        "is score+select+compact over 8192 pages, 4 selected-KV decodes over 451 "
-                        f"pages and one 4-query verify over 131072 tokens; {dt:.1f} s of CPU time"))
+                sample=f"{done} {what}; {dt:.1f} s of CPU time",
+                single_core={"value": round(K_PROPOSE * done1 / dt1, 3), "cores": 1,
+                             "sample": f"{done1} {what}; {dt1:.1f} s"})
 
 
 def time_call(fn, reps, stream, warm=3):
@@ -171,6 +183,21 @@ def run_llama_sweep(args, dev):
     selected (s = 113/2048) and full decodes, and decode time across retention
     s in {1, 2, 5.5, 10, 25, 50, 100} % with a linear fit T(s) = T0 + s T1."""
     w = W.spec("llama8b_32k")
+    _sweep(args, dev, w, "llama8b_32k: B=8, Hq=32, Hkv=8, D=128, 32768-token context, "
+           "s=113/2048 (A1R2K110 pooled)")
+
+
+def run_qwen_sweep(args, dev):
+    """The 128K configuration at batch 1, 2 and 4: routing calls, selected
+    (s = 451/8192) and full decodes, and the same retention sweep and fit."""
+    for B in (1, 2, 4):
+        w = W.spec("qwen32b_128k", B=B)
+        _sweep(args, dev, w, f"qwen32b_128k: B={B}, Hq=64, Hkv=8, D=128, 131072-token context, "
+               "s=451/8192 (A1R2K448 pooled)")
+        torch.cuda.empty_cache()
+
+
+def _sweep(args, dev, w, label):
     B, Hq, Hkv, D = w.B, w.Hq, w.Hkv, w.D
     b = W.make_device(w, dev)
     to = _upload(b, dev)
@@ -229,8 +256,7 @@ def run_llama_sweep(args, dev):
     r2 = 1 - ((ys - pred) ** 2).sum() / ((ys - ys.mean()) ** 2).sum()
     sel_us = [d for d in sweep if d["pages"] == budget][0]["us"]
     print(json.dumps({
-        "metric": METRIC, "workload": "llama8b_32k: B=8, Hq=32, Hkv=8, D=128, 32768-token "
-        "context, s=113/2048 (A1R2K110 pooled)", "unit": "tokens/s",
+        "metric": METRIC, "workload": label, "unit": "tokens/s",
         "value": round(B / (sel_us * 1e-6), 1), "dtype": "bf16", "data": "synthetic",
         "layer_copies": R, "kernels": {k: round(v, 2) for k, v in res.items()},
         "decode_selected_us": sel_us, "decode_full_us": round(full_us, 2),
@@ -713,7 +739,7 @@ def main():
     if args.workload != "qwen32b_128k":
         {"llama8b_32k": run_llama_sweep, "early_route_40k": run_early_route,
          "mixed_serving": run_mixed, "qwen32b_128k_commit": run_commit,
-         "qwen32b_128k_workspace": run_workspace,
+         "qwen32b_128k_workspace": run_workspace, "qwen32b_128k_sweep": run_qwen_sweep,
          "early_route_40k_cpu": run_early_route_cpu}[args.workload](args, dev)
         return
     w = W.spec("qwen32b_128k", B=args.batch)
@@ -835,12 +861,17 @@ def main():
     gbs = lambda nb, ms: nb / (ms * 1e-3) / 1e9  # noqa: E731
     ver_gbs = gbs(nbytes["verify"], ver_ms)
     traffic = read_traffic("verify")
+    # the verify's dense contraction: QK and PV, 2 D flops each per (query row, visible key)
+    ver_flops = 4 * D * Hq * w.q_len * int(b["seq_lens"].astype(np.int64).sum())
+    ver_tflops = ver_flops / (ver_ms * 1e-3) / 1e12
     roofline = {"bound": "hbm", "kernel": "kap_verify_attn (MFMA split-K partial + LSE merge, 2 launches)",
                 "achieved": round(ver_gbs, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
                 "frac": round(ver_gbs / HBM_PEAK_GBS, 4), "traffic": traffic,
                 "measured_read_ceiling_GBps": round(ceiling_gbs, 1),
                 "frac_of_measured_ceiling": round(ver_gbs / ceiling_gbs, 4),
-                "bytes_per_launch": nbytes["verify"], "avg_launch_us": round(ver_ms * 1e3, 2)}
+                "bytes_per_launch": nbytes["verify"], "avg_launch_us": round(ver_ms * 1e3, 2),
+                "mfma": {"flops_per_launch": ver_flops, "tflops": round(ver_tflops, 1),
+                         "frac_of_bf16_dense_peak": round(ver_tflops / 2500.0, 4)}}
     s_meas = nbytes["decode_selected"] / nbytes["decode_full"]
     h = 0.952  # KAP paper Table 5 at 128K: s + (h - s) = 0.055 + 0.897
     result = {

@@ -52,6 +52,7 @@ def _load():
     lib.kor_num_threads.restype = _I
     lib.kor_append_kv.argtypes = [_P, _P, _I, _P, _I, _I, _I, _I, _I, _P, _P]
     lib.kor_materialize.argtypes = [_P, _P, _I, _I, _I, _I, _P, _I, _I, _I, _P, _P, _P]
+    lib.kor_set_threads.argtypes = [_I]
     _lib = lib
     return lib
 
@@ -59,6 +60,11 @@ def _load():
 def num_threads() -> int:
     """OpenMP threads the oracle runs on."""
     return int(_load().kor_num_threads())
+
+
+def set_threads(n: int) -> None:
+    """Sets the OpenMP thread count of the oracle's loops (n >= 1)."""
+    _load().kor_set_threads(int(n))
 
 
 def _dt(a: np.ndarray) -> int:

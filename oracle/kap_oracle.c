@@ -38,6 +38,9 @@ enum { KOR_F32 = 0, KOR_BF16 = 1 };
 /* Threads the OpenMP loops below use. */
 int kor_num_threads(void) { return omp_get_max_threads(); }
 
+/* Sets that thread count (for timing the oracle on one core). */
+void kor_set_threads(int n) { omp_set_num_threads(n > 0 ? n : 1); }
+
 /* Exact widening of one stored element to double. */
 static double widen(const void* base, int dtype, int64_t i) {
   if (dtype == KOR_F32) return (double)((const float*)base)[i];
