@@ -10,7 +10,7 @@ namespace kap {
 
 // ---------------------------------------------------------------- constants
 constexpr int kPage = 16;            // tokens per KV page
-constexpr int kTargetItems = 2048;   // split-K work items aimed at per attention call
+constexpr int kTargetItems = 1280;   // split-K work items aimed at per call (measured best at 128K, B = 4)
 constexpr int kMinChunk = 2;         // minimum pages per work item
 constexpr int kMaxSelectPages = 65536;
 constexpr int kMaxPlanRows = 4096;      // batch x KV heads per attention call
