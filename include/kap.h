@@ -175,10 +175,11 @@ KAP_API kap_status kap_compact_view(const int32_t* sel_pages, const int32_t* sel
                             int64_t* slot_mapping, kap_stream stream);
 
 /*
- * Workspace for kap_decode_attn (q_len = 1) and kap_verify_attn: rotated
- * queries, the split-K work plan and the split partials.  Caller-owned device
- * memory of at least this many bytes; its contents need no initialization and
- * are overwritten by every call (so concurrent calls need separate workspaces).
+ * Workspace for kap_decode_attn (q_len = 1) and kap_verify_attn: the split-K
+ * work plan's per-row offsets and the split partials (m, l, o in fp32).
+ * Caller-owned device memory of at least this many bytes; its contents need
+ * no initialization and are overwritten by every call (so concurrent calls
+ * need separate workspaces).
  */
 KAP_API size_t kap_attn_workspace_bytes(int32_t B, int32_t q_len, int32_t Hq, int32_t Hkv, int32_t D);
 
@@ -195,6 +196,9 @@ KAP_API size_t kap_attn_workspace_bytes(int32_t B, int32_t q_len, int32_t Hq, in
  * combine in fixed order.  Use (block_table, max_pages, G = 1, seq_lens) for
  * full-context decode and (compact_bt, capacity, G, compact_len) for the
  * selected view.  A row with no key yields out = 0 and lse = -inf.
+ * Precision: bf16 K/V run on the matrix cores with the rotated query and the
+ * probabilities rounded to bf16 and fp32 accumulation, softmax and merge;
+ * fp32 K/V run in fp32 throughout.
  *   q        device [B][Hq][D], q_dtype; out device [B][Hq][D], same dtype as q
  *   lse      device out [B][Hq] float, natural log, or NULL
  *   k_pool, v_pool device, kv_dtype, layouts above; q_dtype must equal kv_dtype
