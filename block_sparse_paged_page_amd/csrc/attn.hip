@@ -4,7 +4,7 @@
 // decode-like forwards over the compact view; the verifier scores a short
 // window over the full KV with the original positions):
 //   1. partial: one wave per work item = (request, KV head, chunk of pages,
-//               slice of up to 32 query rows).  Each wave derives its own item
+//               slice of up to 64 query rows).  Each wave derives its own item
 //               from the per-row lengths on the device (closed-form plan, no
 //               host synchronization, so calls are graph-capturable) and
 //               rotates its own query rows at their logical positions (fp64
@@ -17,11 +17,13 @@
 // bf16 path: QK^T and PV run on MFMA.  S^T = K Q^T with
 // v_mfma_f32_16x16x32_bf16 (A = 16 tokens x 32 dims of K straight from the
 // page, B = 32 dims x 16 query rows), which leaves each lane holding one query
-// row and 4 tokens -- exactly the B-operand layout of P^T for
-// O^T = V^T P^T on v_mfma_f32_16x16x16_bf16.  V pages are stored dim-major,
-// so the V^T operand (one dim, 4 consecutive tokens per lane) is a contiguous
-// 8-byte load and no transpose is needed anywhere.  The output accumulator
-// then holds one query row per lane, so the online-softmax rescale is local.
+// row and 4 tokens of the page.  Pages go in pairs: the lane's 4 + 4
+// probabilities of the two pages form the B operand of P^T for O^T = V^T P^T
+// on the same 16x16x32 instruction (contraction over the pair's 32 tokens).
+// V pages are stored dim-major, so the V^T operand (one dim, 4 consecutive
+// tokens of each page) is two contiguous 8-byte loads and no transpose is
+// needed anywhere.  The output accumulator holds one query row per lane, so
+// the online-softmax rescale is local.
 // fp32 path: plain VALU loops (used for the small fp32 workloads).
 #include "kap_internal.h"
 
@@ -166,16 +168,16 @@ struct PartArgs {
 // NT row tiles of 16 query rows per wave (rows = GQA group x window, row r is
 // query r / grp of head g*grp + r % grp).
 //
-// Memory pipeline: three page buffers in a ring, so two pages' K/V loads are
-// in flight while the third is consumed; the item's page-table entries are
-// fetched 64 at a time into one lane register each and broadcast with
-// readlane.  The query fragments live in LDS (re-read per page) to keep the
-// register footprint in budget: at D = 128, NT = 1 runs two waves per SIMD and
-// NT = 2..4 one, with no spills.  NT = 3 and 4 let a (b, g) row group of up to
+// Memory pipeline: four page buffers (two pairs) in a ring, so one pair's K/V
+// loads are in flight while the other pair is consumed; the item's page-table
+// entries are fetched 64 at a time into one lane register each and broadcast
+// with readlane.  The query fragments live in LDS (re-read per pair) to keep
+// the register footprint in budget: at D = 128, NT = 1 runs two waves per SIMD
+// and NT = 2..4 one, with no spills.  NT = 3 and 4 let a (b, g) row group of up to
 // 64 rows (e.g. a 5..8-token window under GQA 8:1) read each page once.
 // Online softmax with a lazy reference max: a row's reference only moves
 // when its running max exceeds it by more than 2^8 (log2 units), so the
-// O rescale is skipped wave-wide on almost every page; probabilities stay
+// O rescale is skipped wave-wide on almost every pair; probabilities stay
 // below 2^8, well inside bf16/fp32 range.  The final (m, l) pair uses the
 // reference, so the merged result is the same softmax.
 constexpr float kLazyRescale = 8.0f;
