@@ -87,17 +87,30 @@ def algorithmic_bytes(w, b, sel_pages):
     return dict(decode_selected=dec_sel, decode_full=dec_full, verify=verify, score=score)
 
 
+def kernel_source_hash():
+    """Hash of the attention kernel's code (attn.hip and its shared header) with
+    comments and blank lines removed, so that only code changes invalidate
+    counters taken earlier."""
+    import hashlib
+    import re
+    csrc = os.path.join(ROOT, "block_sparse_paged_page_amd", "csrc")
+    h = hashlib.sha256()
+    for name in ("attn.hip", "kap_internal.h"):
+        text = open(os.path.join(csrc, name)).read()
+        text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+        text = re.sub(r"//[^\n]*", "", text)
+        lines = [ln.rstrip() for ln in text.splitlines() if ln.strip()]
+        h.update("\n".join(lines).encode())
+    return h.hexdigest()[:16]
+
+
 def read_traffic(kernel_key):
     """HBM traffic per launch recorded from rocprofv3 PMC runs, if the kernel source still matches."""
     import hashlib
     path = os.path.join(ROOT, "profiles", "attn_qwen32b_128k_b4_hbm_traffic.md")
     if not os.path.exists(path):
         return None
-    csrc = os.path.join(ROOT, "block_sparse_paged_page_amd", "csrc")
-    h = hashlib.sha256()
-    for name in ("attn.hip", "kap_internal.h"):   # the kernel's source and its shared header
-        h.update(open(os.path.join(csrc, name), "rb").read())
-    sha = h.hexdigest()[:16]
+    sha = kernel_source_hash()
     for line in open(path):
         if line.startswith("traffic:"):
             f = dict(kv.split("=") for kv in line.split()[1:])
