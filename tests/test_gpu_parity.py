@@ -220,6 +220,46 @@ def test_verify_row_tiles(name, q_len, D):
     print(f"[{name} q_len {q_len} D {D}] verify max rel err {err:.2e}", flush=True)
 
 
+@pytest.mark.parametrize("Hq,Hkv,D,dtype", [
+    (8, 8, 128, "bf16"),     # MHA: one query row per KV head
+    (16, 1, 64, "bf16"),     # MQA, head_dim 64
+    (128, 8, 128, "bf16"),   # GQA 16:1 (decode 16 rows, verify 64 rows per KV head)
+    (32, 8, 64, "f32"),      # fp32 path, head_dim 64, verify 64 rows (two 32-row slices)
+])
+def test_head_layouts(Hq, Hkv, D, dtype):
+    """Score, top-K, selected decode and a 16-token verify on other head shapes."""
+    over = dict(B=2, seq_lens=[3000, 1777], Hq=Hq, Hkv=Hkv, D=D, q_len=16, dtype=dtype)
+    if dtype == "f32":
+        over["sigma"] = 1.0 / 8.0
+    c = Case(W.spec("llama8b_32k", **over))
+    w = c.w
+    s = kap.score_blocks(c.q, c.pos, c.S, c.bt, c.L, w.Hkv)
+    torch.cuda.synchronize()
+    check_scores(c, s.cpu().numpy())
+    cap = c.budget()
+    s_ref = oracle.score(c.b["q"], c.b["positions"], c.summ_l, c.btl, c.b["seq_lens"], w.Hkv)
+    sel_ref, cnt_ref = oracle.select(s_ref.astype(np.float32), c.b["seq_lens"], c.b["anchor"],
+                                     c.b["recent"], c.k_mid_h, cap)
+    sel, cnt = kap.select_topk(t(s_ref.astype(np.float32)), c.L, c.anchor, c.recent, c.k_mid, cap,
+                               cap)
+    cbt, _, clen, _ = kap.compact_view(sel, cnt, c.bt, c.L, c.pos, 1)
+    lse = torch.empty((w.B, w.Hq), dtype=torch.float32, device="cuda")
+    out = kap.decode_attn(c.q, c.pos, c.K, c.V, cbt, clen, lse=lse)
+    start = np.maximum(c.b["positions"] - 9, 0).astype(np.int32)
+    vlse = torch.empty((w.B, w.q_len, w.Hq), dtype=torch.float32, device="cuda")
+    vout = kap.verify_attn(c.qv, t(start), c.K, c.V, c.bt, c.L, lse=vlse)
+    torch.cuda.synchronize()
+    np.testing.assert_array_equal(sel.cpu().numpy(), sel_ref)
+    keys = oracle.keys_selected(sel_ref, cnt_ref, c.b["seq_lens"])
+    ref, lref = oracle.attend(c.b["q"][:, None], c.b["positions"], c.Kl, c.Vl, c.btl, keys, 1,
+                              w.Hkv)
+    e1 = _check_attn(c, out, lse, ref[:, 0], lref[:, 0])
+    vref, vlref = oracle.attend(c.b["qv"], start, c.Kl, c.Vl, c.btl,
+                                oracle.keys_full(c.b["seq_lens"]), 1, w.Hkv)
+    e2 = _check_attn(c, vout, vlse, vref, vlref)
+    print(f"[Hq {Hq} Hkv {Hkv} D {D} {dtype}] decode {e1:.2e} verify {e2:.2e}", flush=True)
+
+
 def test_verify_window_k_plus_one():
     """The KAP paper's verify window is k+1 tokens (carry + k drafts): q_len 5 on the tiny case."""
     w = W.spec("tiny", q_len=5)
