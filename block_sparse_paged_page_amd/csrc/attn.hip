@@ -190,20 +190,28 @@ struct PageFrag {
   uint2 v[D / 16];
 };
 
-template <int D, int NT>
+template <int D, int NT, bool PIPE>
 __global__ __launch_bounds__(64) void attn_partial_bf16(PartArgs a) {
   const PlanIn pin{a.lens, a.B, a.Hkv, a.G, a.width, a.target};
   const bool publish = blockIdx.x == 0 && blockIdx.y == 0;
   const PlanItem it = plan_find(pin, blockIdx.x, publish ? a.row_off : nullptr, a.n_items);
   if (!it.valid) return;
   const int item = blockIdx.x;
-  const int b = it.b, g = it.g, p0 = it.p0, p1 = it.p1;
+  // the item is the same for every lane: keep it in scalar registers
+  const int b = __builtin_amdgcn_readfirstlane(it.b), g = __builtin_amdgcn_readfirstlane(it.g);
+  const int p0 = __builtin_amdgcn_readfirstlane(it.p0), p1 = __builtin_amdgcn_readfirstlane(it.p1);
   const int lane = threadIdx.x;
   const int l16 = lane & 15, q4 = lane >> 4;
   const int row0 = blockIdx.y * 16 * NT;
   const int gr = a.G == 1 ? 0 : g;
   const int len = a.lens[b * a.G + gr];
+  const int pos_b = a.pos[b];  // read once, before any page load is in flight
   const int32_t* trow = a.table + (int64_t)(b * a.G + gr) * a.width;
+  // Pipelined mode reads the (read-only) table through the constant address
+  // space: the wave-uniform entries then come through scalar memory and its
+  // own counter, so waiting for an entry never waits for K/V loads in flight.
+  const __attribute__((address_space(4))) int32_t* trow_s =
+      (const __attribute__((address_space(4))) int32_t*)trow;
   constexpr int KS = D / 32;  // QK k-steps
   constexpr int NC = D / 16;  // PV dim tiles
   const uint16_t* kpool = (const uint16_t*)a.k;
@@ -227,10 +235,19 @@ __global__ __launch_bounds__(64) void attn_partial_bf16(PartArgs a) {
       const int e = k * 64 + lane;
       const int rr = e / CPR, c = e % CPR;
       const int r = row0 + rr;
-      qraw[k] = make_uint4(0, 0, 0, 0);
-      if (r < a.R) {
-        const int i = r / a.grp, h = g * a.grp + r % a.grp;
-        qraw[k] = *(const uint4*)(q + (((int64_t)b * a.q_len + i) * a.Hq + h) * D + 8 * c);
+      if constexpr (PIPE) {
+        // straight-line: rows past R load row R - 1 and are masked to zero
+        const int rc = min(r, a.R - 1);
+        const int i = rc / a.grp, h = g * a.grp + rc % a.grp;
+        const uint4 x = *(const uint4*)(q + (((int64_t)b * a.q_len + i) * a.Hq + h) * D + 8 * c);
+        const uint32_t keep = (r < a.R) ? 0xffffffffu : 0u;
+        qraw[k] = make_uint4(x.x & keep, x.y & keep, x.z & keep, x.w & keep);
+      } else {
+        qraw[k] = make_uint4(0, 0, 0, 0);
+        if (r < a.R) {
+          const int i = r / a.grp, h = g * a.grp + r % a.grp;
+          qraw[k] = *(const uint4*)(q + (((int64_t)b * a.q_len + i) * a.Hq + h) * D + 8 * c);
+        }
       }
     }
   }
@@ -239,11 +256,15 @@ __global__ __launch_bounds__(64) void attn_partial_bf16(PartArgs a) {
   int wbase = p0;
   int tr = (p0 + lane < p1) ? trow[p0 + lane] : 0;
   auto phys_of = [&](int p) -> int64_t {
-    if (p - wbase >= 64) {  // wave-uniform refill
-      wbase += 64;
-      tr = (wbase + lane < p1) ? trow[wbase + lane] : 0;
+    if constexpr (PIPE) {
+      return (int64_t)trow_s[p];
+    } else {
+      if (p - wbase >= 64) {  // wave-uniform refill
+        wbase += 64;
+        tr = (wbase + lane < p1) ? trow[wbase + lane] : 0;
+      }
+      return (int64_t)__builtin_amdgcn_readlane(tr, p - wbase);
     }
-    return (int64_t)__builtin_amdgcn_readlane(tr, p - wbase);
   };
   auto load_page = [&](int p, PageFrag<D>& f) {
     const int64_t base = phys_of(p) * page_stride + head_off;
@@ -262,10 +283,19 @@ __global__ __launch_bounds__(64) void attn_partial_bf16(PartArgs a) {
   for (int s = 0; s < KS; ++s) buf0.k[s] = buf1.k[s] = buf2.k[s] = buf3.k[s] = make_uint4(0, 0, 0, 0);
 #pragma unroll
   for (int c = 0; c < NC; ++c) buf0.v[c] = buf1.v[c] = buf2.v[c] = buf3.v[c] = make_uint2(0, 0);
-  if (p0 < p1) load_page(p0, buf0);
-  if (p0 + 1 < p1) load_page(p0 + 1, buf1);
-  if (p0 + 2 < p1) load_page(p0 + 2, buf2);
-  if (p0 + 3 < p1) load_page(p0 + 3, buf3);
+  if constexpr (PIPE) {
+    // one pair in flight while the other is consumed; every load is
+    // straight-line (pages past the item clamp to its last page, an L2 hit
+    // whose scores are masked), so the compiler waits for exactly the pair
+    // about to be consumed
+    load_page(p0, buf0);
+    load_page(min(p0 + 1, p1 - 1), buf1);
+  } else {
+    if (p0 < p1) load_page(p0, buf0);
+    if (p0 + 1 < p1) load_page(p0 + 1, buf1);
+    if (p0 + 2 < p1) load_page(p0 + 2, buf2);
+    if (p0 + 3 < p1) load_page(p0 + 3, buf3);
+  }
 
   // This slice's query rows, rotated at their positions, as LDS fragments in
   // the B-operand layout of S^T = K Q^T (row l16, dims 32 s + 8 q4 .. + 7).
@@ -294,7 +324,7 @@ __global__ __launch_bounds__(64) void attn_partial_bf16(PartArgs a) {
       if (r < a.R) {
         const int i = r / a.grp;
         if (i != cur) {
-          rope_sincos((double)a.pos[b] + (double)i, pr, D, a.log2_theta, &sn, &cs);
+          rope_sincos((double)pos_b + (double)i, pr, D, a.log2_theta, &sn, &cs);
           cur = i;
         }
         const float2 v = rope_pair(bf16_to_f32(sraw[rr][pr]), bf16_to_f32(sraw[rr][pr + HALF]), sn, cs);
@@ -307,7 +337,7 @@ __global__ __launch_bounds__(64) void attn_partial_bf16(PartArgs a) {
 #pragma unroll
     for (int t = 0; t < NT; ++t) {
       const int r = row0 + 16 * t + l16;
-      qpos[t] = (r < a.R) ? a.pos[b] + r / a.grp : -1;
+      qpos[t] = (r < a.R) ? pos_b + r / a.grp : -1;
     }
     __syncthreads();
   }
@@ -434,14 +464,22 @@ __global__ __launch_bounds__(64) void attn_partial_bf16(PartArgs a) {
     }
   };
 
-  for (int p = p0; p < p1; p += 4) {
-    consume2(p, buf0, buf1, p + 1 < p1);
-    if (p + 4 < p1) load_page(p + 4, buf0);
-    if (p + 5 < p1) load_page(p + 5, buf1);
-    if (p + 2 < p1) {
-      consume2(p + 2, buf2, buf3, p + 3 < p1);
-      if (p + 6 < p1) load_page(p + 6, buf2);
-      if (p + 7 < p1) load_page(p + 7, buf3);
+  if constexpr (PIPE) {
+    for (int p = p0; p < p1; p += 2) {
+      consume2(p, buf0, buf1, p + 1 < p1);
+      load_page(min(p + 2, p1 - 1), buf0);
+      load_page(min(p + 3, p1 - 1), buf1);
+    }
+  } else {
+    for (int p = p0; p < p1; p += 4) {
+      consume2(p, buf0, buf1, p + 1 < p1);
+      if (p + 4 < p1) load_page(p + 4, buf0);
+      if (p + 5 < p1) load_page(p + 5, buf1);
+      if (p + 2 < p1) {
+        consume2(p + 2, buf2, buf3, p + 3 < p1);
+        if (p + 6 < p1) load_page(p + 6, buf2);
+        if (p + 7 < p1) load_page(p + 7, buf3);
+      }
     }
   }
 #pragma unroll
@@ -685,12 +723,26 @@ kap_status launch_attention(const AttnCall& c) {
     // one row slice whenever the rows fit in 64, so each page is read once per (b, g)
     const int nt = R <= 16 ? 1 : R <= 32 ? 2 : R <= 48 ? 3 : 4;
     slices = (R + 16 * nt - 1) / (16 * nt);
-    static const void* const fns[2][4] = {
-        {(const void*)attn_partial_bf16<64, 1>, (const void*)attn_partial_bf16<64, 2>,
-         (const void*)attn_partial_bf16<64, 3>, (const void*)attn_partial_bf16<64, 4>},
-        {(const void*)attn_partial_bf16<128, 1>, (const void*)attn_partial_bf16<128, 2>,
-         (const void*)attn_partial_bf16<128, 3>, (const void*)attn_partial_bf16<128, 4>}};
-    fn = fns[c.D == 128 ? 1 : 0][nt - 1];
+    static const void* const fns[2][2][4] = {
+        {{(const void*)attn_partial_bf16<64, 1, false>, (const void*)attn_partial_bf16<64, 2, false>,
+          (const void*)attn_partial_bf16<64, 3, false>, (const void*)attn_partial_bf16<64, 4, false>},
+         {(const void*)attn_partial_bf16<128, 1, false>, (const void*)attn_partial_bf16<128, 2, false>,
+          (const void*)attn_partial_bf16<128, 3, false>, (const void*)attn_partial_bf16<128, 4, false>}},
+        {{(const void*)attn_partial_bf16<64, 1, true>, (const void*)attn_partial_bf16<64, 2, true>,
+          (const void*)attn_partial_bf16<64, 3, true>, (const void*)attn_partial_bf16<64, 4, true>},
+         {(const void*)attn_partial_bf16<128, 1, true>, (const void*)attn_partial_bf16<128, 2, true>,
+          (const void*)attn_partial_bf16<128, 3, true>, (const void*)attn_partial_bf16<128, 4, true>}}};
+    const int di = c.D == 128 ? 1 : 0;
+    // Short work items (a selected view) are latency-bound: they run the
+    // pipelined variant (a pair of pages in flight).  Long items saturate HBM,
+    // where one page in flight per wave across many waves measured fastest:
+    // they run the throttled variant.  The host bounds the item length from
+    // the table width, mirroring the device plan's chunk formula.
+    const int rows = c.B * c.Hkv;
+    const int t0 = max(1, min(kTargetItems, resident_blocks(fns[0][di][nt - 1], 64) / slices));
+    const int aim = max(t0 - rows, max(t0 / 2, 1));
+    const long long chunk = max(((long long)c.width * rows + aim - 1) / aim, (long long)kMinChunk);
+    fn = fns[chunk <= kPipelinedMaxPages ? 1 : 0][di][nt - 1];
   } else {
     slices = (R + 31) / 32;
     fn = c.D == 128 ? (const void*)attn_partial_f32<128> : (const void*)attn_partial_f32<64>;
