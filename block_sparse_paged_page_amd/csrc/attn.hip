@@ -733,16 +733,18 @@ kap_status launch_attention(const AttnCall& c) {
          {(const void*)attn_partial_bf16<128, 1, true>, (const void*)attn_partial_bf16<128, 2, true>,
           (const void*)attn_partial_bf16<128, 3, true>, (const void*)attn_partial_bf16<128, 4, true>}}};
     const int di = c.D == 128 ? 1 : 0;
-    // Short work items (a selected view) are latency-bound: they run the
-    // pipelined variant (a pair of pages in flight).  Long items saturate HBM,
-    // where one page in flight per wave across many waves measured fastest:
-    // they run the throttled variant.  The host bounds the item length from
-    // the table width, mirroring the device plan's chunk formula.
+    // Short work items (a selected view) are latency-bound, and the 48/64-row
+    // tiles have enough compute per page that it must overlap the next pair's
+    // loads: both run the pipelined variant (a pair of pages in flight).  Long
+    // items with 16/32-row tiles saturate HBM, where one page in flight per
+    // wave across many waves measured fastest: they run the throttled
+    // variant.  The host bounds the item length from the table width,
+    // mirroring the device plan's chunk formula.
     const int rows = c.B * c.Hkv;
     const int t0 = max(1, min(kTargetItems, resident_blocks(fns[0][di][nt - 1], 64) / slices));
     const int aim = max(t0 - rows, max(t0 / 2, 1));
     const long long chunk = max(((long long)c.width * rows + aim - 1) / aim, (long long)kMinChunk);
-    fn = fns[chunk <= kPipelinedMaxPages ? 1 : 0][di][nt - 1];
+    fn = fns[(chunk <= kPipelinedMaxPages || nt >= 3) ? 1 : 0][di][nt - 1];
   } else {
     slices = (R + 31) / 32;
     fn = c.D == 128 ? (const void*)attn_partial_f32<128> : (const void*)attn_partial_f32<64>;
