@@ -5,7 +5,8 @@ Workload (the 128K-context, 32B-class configuration): batch B (default 4) of
 16-token pages scattered over the pool, retention s = 451/8192 pages
 (A1R2K448), 1 % needle pages.  One step is one proposal-verification cycle of
 one attention layer, every stage of the path:
-  route   : kap_score_blocks -> kap_select_topk -> kap_compact_view
+  route   : kap_score_pool_blocks (head-pooled key) -> kap_select_topk on the
+            pooled key -> kap_compact_view
   propose : k = 4 x kap_decode_attn over the compact view (tokens at P .. P+3)
   verify  : kap_verify_attn, 4 queries at 131072..131075 over all 8192 pages
 Each call reads a different layer copy of the pool (R copies, rotating), so
@@ -247,6 +248,15 @@ def _sweep(args, dev, w, label):
                                                          budget, sel=sel, cnt=cnt), args.steps, st)
     res["compact_us"] = time_call(lambda: kap.compact_view(sel, cnt, bt, L, pos, 1, out=cv),
                                   args.steps, st)
+    # the pooled route: per-head scores folded into the pooled key in the
+    # scoring launch, and the top-K reading that one row
+    pooled = torch.empty((B, 1, bt.shape[1]), dtype=torch.float32, device=dev)
+    res["score_pool_us"] = time_call(
+        lambda: kap.score_pool_blocks(q, pos, Ss[lay()], bt, L, Hkv, pooled=pooled.view(B, -1),
+                                      with_scores=False), args.steps, st)
+    res["select_pooled_us"] = time_call(lambda: kap.select_topk(pooled, L, anchor, recent, kmid,
+                                                                budget, budget, sel=sel, cnt=cnt),
+                                        args.steps, st)
     kv_tok = Hkv * 2 * D * EB
     sweep = []
     for num, den in ((1, 100), (2, 100), (55, 1000), (10, 100), (25, 100), (50, 100), (1, 1)):
@@ -534,7 +544,7 @@ def run_mixed(args, dev):
     S = torch.zeros((b["pool_pages"], Hkv, D), dtype=torch.bfloat16, device=dev)
     kap.build_summary(b["K"], bt, L, S)
     st = torch.cuda.current_stream()
-    scores = torch.empty((B, Hkv, bt.shape[1]), dtype=torch.float32, device=dev)
+    pooled = torch.empty((B, 1, bt.shape[1]), dtype=torch.float32, device=dev)
     sel = torch.empty((B, 1, cap), dtype=torch.int32, device=dev)
     cnt = torch.empty((B, 1), dtype=torch.int32, device=dev)
     cv = (torch.empty((B, 1, cap), dtype=torch.int32, device=dev),
@@ -545,8 +555,8 @@ def run_mixed(args, dev):
     out = torch.empty_like(q)
 
     def route():
-        kap.score_blocks(q, pos, S, bt, L, Hkv, scores=scores)
-        kap.select_topk(scores, L, anchor, recent, kmid, cap, cap, sel=sel, cnt=cnt)
+        kap.score_pool_blocks(q, pos, S, bt, L, Hkv, pooled=pooled.view(B, -1), with_scores=False)
+        kap.select_topk(pooled, L, anchor, recent, kmid, cap, cap, sel=sel, cnt=cnt)
         kap.compact_view(sel, cnt, bt, L, pos, 1, out=cv)
 
     route()
@@ -610,7 +620,7 @@ def run_commit(args, dev):
     for _ in range(R - 1):
         layers.append(Layer(b["K"].clone(), b["V"].clone(), S0.clone()))
     ws = torch.empty(kap.attn_workspace_bytes(B, w.q_len, Hq, Hkv, D), dtype=torch.uint8, device=dev)
-    scores = torch.empty((B, Hkv, bt.shape[1]), dtype=torch.float32, device=dev)
+    pooled = torch.empty((B, 1, bt.shape[1]), dtype=torch.float32, device=dev)
     sel = torch.empty((B, 1, cap), dtype=torch.int32, device=dev)
     cnt = torch.empty((B, 1), dtype=torch.int32, device=dev)
     cv = (torch.empty((B, 1, cap), dtype=torch.int32, device=dev),
@@ -627,8 +637,9 @@ def run_commit(args, dev):
         return layers[it[0]]
 
     def route(ly):
-        kap.score_blocks(q_route, pos, ly.S, bt, L, Hkv, scores=scores)
-        kap.select_topk(scores, L, anchor, recent, k_mid, cap, cap, sel=sel, cnt=cnt)
+        kap.score_pool_blocks(q_route, pos, ly.S, bt, L, Hkv, pooled=pooled.view(B, -1),
+                              with_scores=False)
+        kap.select_topk(pooled, L, anchor, recent, k_mid, cap, cap, sel=sel, cnt=cnt)
         kap.compact_view(sel, cnt, bt, L, pos, w.q_len, out=cv)       # slot mapping of the window
 
     def propose(ly):
@@ -784,7 +795,7 @@ def main():
 
     ws = torch.empty(kap.attn_workspace_bytes(B, w.q_len, Hq, Hkv, D), dtype=torch.uint8,
                      device=dev)
-    scores = torch.empty((B, Hkv, bt.shape[1]), dtype=torch.float32, device=dev)
+    pooled = torch.empty((B, 1, bt.shape[1]), dtype=torch.float32, device=dev)
     sel = torch.empty((B, 1, cap), dtype=torch.int32, device=dev)
     cnt = torch.empty((B, 1), dtype=torch.int32, device=dev)
     cview = (torch.empty((B, 1, cap), dtype=torch.int32, device=dev),
@@ -806,8 +817,9 @@ def main():
         if ev:
             ev[0].record(stream)
         lay = next_layer()
-        kap.score_blocks(q_route, pos, lay.S, bt, L, Hkv, scores=scores)
-        kap.select_topk(scores, L, anchor, recent, k_mid, budget, cap, sel=sel, cnt=cnt)
+        kap.score_pool_blocks(q_route, pos, lay.S, bt, L, Hkv, pooled=pooled.view(B, -1),
+                              with_scores=False)
+        kap.select_topk(pooled, L, anchor, recent, k_mid, budget, cap, sel=sel, cnt=cnt)
         kap.compact_view(sel, cnt, bt, L, pos, 1, out=cview)
         if ev:
             ev[1].record(stream)

@@ -32,6 +32,8 @@ _SIGS = {
     "kap_version": ([], ctypes.c_char_p),
     "kap_score_blocks": ([_P, _I32, _P, _F, _P, _I32, _I32, _P, _I32, _P, _I32, _I32, _I32, _I32,
                           _I32, _P, _P], _I32),
+    "kap_score_pool_blocks": ([_P, _I32, _P, _F, _P, _I32, _I32, _P, _I32, _P, _I32, _I32, _I32,
+                               _I32, _I32, _P, _P, _P], _I32),
     "kap_proxy_workspace_bytes": ([_I32, _I32, _I32], _SZ),
     "kap_proxy_query": ([_P, _P, _I32, _I32, _I32, _P, _P, _SZ, _P], _I32),
     "kap_select_topk": ([_P, _I32, _I32, _I32, _P, _I32, _I32, _P, _P, _P, _I32, _I32, _P, _P, _P],
@@ -137,6 +139,26 @@ def score_blocks(q, positions, summary, block_table, seq_lens, Hkv, theta=1e4, s
                               _p(seq_lens), B, Hq, Hkv, D, 16, _p(scores), _stream(stream))
     _check(st, "kap_score_blocks")
     return scores
+
+
+def score_pool_blocks(q, positions, summary, block_table, seq_lens, Hkv, theta=1e4,
+                      scores=None, pooled=None, with_scores=True, stream=None):
+    """kap_score_pool_blocks: per-head scores [B][Hkv][max_pages] (or None when
+    with_scores is False) and the head-pooled key [B][max_pages], float32."""
+    lib = load()
+    B, Hq, D = q.shape
+    max_pages = block_table.shape[1]
+    if scores is None and with_scores:
+        scores = torch.empty((B, Hkv, max_pages), dtype=torch.float32, device=q.device)
+    if pooled is None:
+        pooled = torch.empty((B, max_pages), dtype=torch.float32, device=q.device)
+    st = lib.kap_score_pool_blocks(_p(q), _dt(q), _p(positions), float(theta), _p(summary),
+                                   _dt(summary), summary.shape[0], _p(block_table), max_pages,
+                                   _p(seq_lens), B, Hq, Hkv, D, 16,
+                                   _p(scores), _p(pooled),
+                                   _stream(stream))
+    _check(st, "kap_score_pool_blocks")
+    return scores, pooled
 
 
 def proxy_query(hidden, w_q, q_out=None, workspace=None, stream=None):

@@ -121,6 +121,29 @@ kap_status kap_score_blocks(const void* q, int32_t q_dtype, const int32_t* posit
                       scores, (hipStream_t)stream);
 }
 
+kap_status kap_score_pool_blocks(const void* q, int32_t q_dtype, const int32_t* positions,
+                                 float rope_theta, const void* summary, int32_t sum_dtype,
+                                 int32_t num_pages, const int32_t* block_table,
+                                 int32_t max_pages, const int32_t* seq_lens, int32_t B,
+                                 int32_t Hq, int32_t Hkv, int32_t D, int32_t page_size,
+                                 float* scores, float* pooled, kap_stream stream) {
+  g_err[0] = 0;
+  if (B < 0 || max_pages < 0 || num_pages < 0)
+    return fail(KAP_ERR_INVALID_ARG, "negative size (B=%d max_pages=%d num_pages=%d)", B,
+                max_pages, num_pages);
+  kap_status st = check_heads(Hq, Hkv, D, page_size);
+  if (st != KAP_OK) return st;
+  if (!dtype_ok(q_dtype) || !dtype_ok(sum_dtype))
+    return fail(KAP_ERR_UNSUPPORTED, "dtype q=%d summary=%d", q_dtype, sum_dtype);
+  if (!(rope_theta > 1.0f)) return fail(KAP_ERR_INVALID_ARG, "rope_theta %g <= 1", rope_theta);
+  if (B == 0 || max_pages == 0) return KAP_OK;
+  if (!q || !positions || !summary || !block_table || !seq_lens || !pooled)
+    return fail(KAP_ERR_INVALID_ARG, "null pointer");
+  return launch_score_pool(q, (kap_dtype)q_dtype, positions, rope_theta, summary,
+                           (kap_dtype)sum_dtype, block_table, max_pages, seq_lens, B, Hq, Hkv,
+                           D, scores, pooled, (hipStream_t)stream);
+}
+
 size_t kap_proxy_workspace_bytes(int32_t B, int32_t d_model, int32_t n_out) {
   if (B <= 0 || d_model <= 0 || n_out <= 0) return 0;
   return (size_t)proxy_splits(d_model) * B * n_out * sizeof(float);

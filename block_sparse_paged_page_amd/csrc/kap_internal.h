@@ -67,6 +67,14 @@ __device__ __forceinline__ void rope_sincos(double pos, int pair, int D, double 
   sincos(r, s, c);
 }
 
+// Workgroup barrier that orders LDS only: global loads in flight stay in
+// flight across it (__syncthreads also waits for every outstanding load).
+__device__ __forceinline__ void lds_barrier() {
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup", "local");
+  __builtin_amdgcn_s_barrier();
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup", "local");
+}
+
 __device__ __forceinline__ float wave_max_xor(float v, int from, int to) {
   for (int m = from; m < to; m <<= 1) v = fmaxf(v, __shfl_xor(v, m));
   return v;
@@ -116,6 +124,12 @@ kap_status launch_score(const void* q, kap_dtype q_dt, const int32_t* pos, float
                         const void* summ, kap_dtype s_dt, const int32_t* bt, int32_t max_pages,
                         const int32_t* seq_lens, int32_t B, int32_t Hq, int32_t Hkv, int32_t D,
                         float* scores, hipStream_t stream);
+// All KV heads per block plus the head-pooled key (scores may be null); Hkv <= 16.
+kap_status launch_score_pool(const void* q, kap_dtype q_dt, const int32_t* pos, float theta,
+                             const void* summ, kap_dtype s_dt, const int32_t* bt,
+                             int32_t max_pages, const int32_t* seq_lens, int32_t B, int32_t Hq,
+                             int32_t Hkv, int32_t D, float* scores, float* pooled,
+                             hipStream_t stream);
 kap_status launch_select(const float* scores, int32_t B, int32_t Hkv, int32_t max_pages,
                          const int32_t* seq_lens, int32_t per_head, const int32_t* anchor,
                          const int32_t* recent, const int32_t* k_mid, int32_t capacity,

@@ -23,6 +23,7 @@ struct ScoreArgs {
   const int32_t* seq_lens;
   int32_t Hq, Hkv, grp;
   float* scores;
+  float* pooled;
 };
 
 constexpr int kScorePagesPerBlock = 256;
@@ -59,21 +60,28 @@ __global__ __launch_bounds__(256) void score_kernel(ScoreArgs a) {
   float qv[QPT];
   {
     const int64_t q0 = ((int64_t)b * a.Hq + g * a.grp) * D;  // group heads are contiguous
+    // unconditional loads at clamped indices: a load under a branch makes
+    // the compiler wait for it (and every older load) before going on
 #pragma unroll
     for (int k = 0; k < QPT; ++k) {
       const int e = k * 256 + tid;
-      qv[k] = e < a.grp * D ? (float)widen_any<QT>(a.q, q0 + e) : 0.f;
+      const float x = (float)widen_any<QT>(a.q, q0 + min(e, a.grp * D - 1));
+      qv[k] = e < a.grp * D ? x : 0.f;
     }
   }
-  const int tr = (w0 + lane < min(w1, N)) ? btrow[w0 + lane] : 0;
+  const int tr0 = btrow[min(w0 + lane, a.max_pages - 1)];
+  const int tr = (w0 + lane < min(w1, N)) ? tr0 : 0;
+  // every lane's page ids first (one LDS round trip), then all row loads
+  int phys[U];
+#pragma unroll
+  for (int u = 0; u < U; ++u) phys[u] = __shfl(tr, u * RPL + sub);
   uint4 v[U];
 #pragma unroll
   for (int u = 0; u < U; ++u) {
     const int j = u * RPL + sub;
-    const int64_t phys = __shfl(tr, j);
     v[u] = make_uint4(0, 0, 0, 0);
     if (w0 + j < N && w0 + j < w1)
-      v[u] = *(const uint4*)(summ + (phys * a.Hkv + g) * D + part * EPL);
+      v[u] = *(const uint4*)(summ + ((int64_t)phys[u] * a.Hkv + g) * D + part * EPL);
   }
 #pragma unroll
   for (int k = 0; k < QPT; ++k) sq[k * 256 + tid] = qv[k];
@@ -120,12 +128,143 @@ __global__ __launch_bounds__(256) void score_kernel(ScoreArgs a) {
   }
 }
 
+// All KV heads of a run of pages in one block, with the head-pooled key.
+// Grid (B, runs of 64 pages); one wave per KV head (Hkv <= 16).  Each wave
+// reads its head's 64 summary rows exactly as score_kernel does (same access
+// pattern and arithmetic, so the per-head scores are the same), and the waves
+// of a block read the same 64 pages, so each page's contiguous run of head
+// rows is fetched together.  The request's query heads are staged in LDS by
+// the whole block while the rows are in flight.  The run's scores are then
+// folded over the heads in head order, in fp32 with round-to-nearest adds and
+// one rounded division: the same mean the top-K forms for pooled selection,
+// so the top-K then reads one key row per request instead of Hkv.
+// Pages per block: 16 row loads in flight per wave, at most 64 pages (one
+// page-table entry per lane).
+template <int D, typename ST>
+constexpr int pool_pages_per_block() {
+  return 16 * (64 / (D / (16 / (int)sizeof(ST)))) < 64 ? 16 * (64 / (D / (16 / (int)sizeof(ST))))
+                                                        : 64;
+}
+constexpr int kPoolMaxHeads = 16;
+constexpr size_t kPoolMaxQueryLds = 64 * 1024;
+
+template <int D, typename ST, typename QT>
+__global__ __launch_bounds__(1024) void score_pool_kernel(ScoreArgs a) {
+  const int b = blockIdx.x;
+  const int tid = threadIdx.x, lane = tid & 63, g = tid >> 6;
+  const int nt = blockDim.x;  // 64 * Hkv
+  constexpr int EPL = 16 / (int)sizeof(ST);
+  constexpr int LPR = D / EPL;
+  constexpr int RPL = 64 / LPR;
+  constexpr int PPB = pool_pages_per_block<D, ST>();  // pages per block (<= 64)
+  constexpr int U = PPB / RPL;
+  constexpr int half = D / 2;
+  constexpr int QC = D * (int)sizeof(QT) / 64;  // 16-byte query chunks per thread (grp <= 16)
+  const int part = lane % LPR, sub = lane / LPR;
+  const int N = (a.seq_lens[b] + kPage - 1) / kPage;
+  const int w0 = blockIdx.y * PPB;
+  const int w1 = min(w0 + PPB, a.max_pages);
+  const int nv = max(0, min(w1, N) - w0);  // pages of the run that hold keys
+  const ST* summ = (const ST*)a.summ;
+  extern __shared__ __align__(16) unsigned char smem[];
+  QT* sq = (QT*)smem;  // the request's query heads [Hq][D] (dynamic)
+  __shared__ float su[kPoolMaxHeads][D];
+  __shared__ float sc[kPoolMaxHeads][PPB];
+
+  if (nv > 0) {  // uniform over the block
+    // Straight-line loads at clamped indices (a load under a branch makes the
+    // compiler wait for it, and for every older load, at once): the query
+    // heads, then the run's page-table entries, then the head's rows.
+    const int nchunk = a.Hq * D * (int)sizeof(QT) / 16;
+    const uint4* qsrc = (const uint4*)((const QT*)a.q + (int64_t)b * a.Hq * D);
+    uint4 qc[QC];
+#pragma unroll
+    for (int k = 0; k < QC; ++k) qc[k] = qsrc[min(k * nt + tid, nchunk - 1)];
+    const int tr0 = a.bt[(int64_t)b * a.max_pages + min(w0 + lane, a.max_pages - 1)];
+    const int tr = lane < nv ? tr0 : 0;
+    // the query chunks arrived with the table entries (loads complete in order)
+#pragma unroll
+    for (int k = 0; k < QC; ++k)  // clamped like the loads: repeats store the same chunk
+      ((uint4*)sq)[min(k * nt + tid, nchunk - 1)] = qc[k];
+    int phys[U];
+#pragma unroll
+    for (int u = 0; u < U; ++u) phys[u] = __shfl(tr, u * RPL + sub);
+    uint4 v[U];
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      const int j = u * RPL + sub;
+      v[u] = make_uint4(0, 0, 0, 0);
+      if (j < nv) v[u] = *(const uint4*)(summ + ((int64_t)phys[u] * a.Hkv + g) * D + part * EPL);
+    }
+    lds_barrier();
+    // u_g = sum over the group of RoPE(q_h, pos); lane = rotation pair
+    if (lane < half) {
+      double sn, cs;
+      rope_sincos((double)a.pos[b], lane, D, a.log2_theta, &sn, &cs);
+      double ux = 0.0, uy = 0.0;
+      const QT* qg = sq + (size_t)g * a.grp * D;
+      for (int hh = 0; hh < a.grp; ++hh) {
+        const double x = load_as_f32<QT>(qg, hh * D + lane);
+        const double y = load_as_f32<QT>(qg, hh * D + lane + half);
+        ux += x * cs - y * sn;
+        uy += y * cs + x * sn;
+      }
+      su[g][lane] = (float)ux;
+      su[g][lane + half] = (float)uy;
+    }
+    lds_barrier();
+    float ur[EPL];
+#pragma unroll
+    for (int e = 0; e < EPL; ++e) ur[e] = su[g][part * EPL + e];
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      float dot = 0.f;
+      if constexpr (sizeof(ST) == 2) {
+        const uint32_t w[4] = {v[u].x, v[u].y, v[u].z, v[u].w};
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          dot += ur[2 * e] * __uint_as_float(w[e] << 16);
+          dot += ur[2 * e + 1] * __uint_as_float(w[e] & 0xffff0000u);
+        }
+      } else {
+        dot += ur[0] * __uint_as_float(v[u].x);
+        dot += ur[1] * __uint_as_float(v[u].y);
+        dot += ur[2] * __uint_as_float(v[u].z);
+        dot += ur[3] * __uint_as_float(v[u].w);
+      }
+#pragma unroll
+      for (int m = 1; m < LPR; m <<= 1) dot += __shfl_xor(dot, m);
+      const int j = u * RPL + sub;
+      if (part == 0) sc[g][j] = (j < nv) ? dot : -INFINITY;
+    }
+    lds_barrier();
+  }
+  // per-head scores along the run (coalesced) and the pooled key
+  const int np = w1 - w0;
+  if (a.scores) {
+    for (int e = tid; e < a.Hkv * PPB; e += nt) {
+      const int gg = e / PPB, j = e % PPB;
+      if (j < np)
+        a.scores[((int64_t)b * a.Hkv + gg) * a.max_pages + w0 + j] = j < nv ? sc[gg][j] : -INFINITY;
+    }
+  }
+  if (a.pooled && tid < np) {  // np <= 64 <= 64 * Hkv threads
+    float k = -INFINITY;
+    if (tid < nv) {
+      k = sc[0][tid];
+      for (int gg = 1; gg < a.Hkv; ++gg) k = __fadd_rn(k, sc[gg][tid]);
+      k = __fdiv_rn(k, (float)a.Hkv);
+    }
+    a.pooled[(int64_t)b * a.max_pages + w0 + tid] = k;
+  }
+}
+
 kap_status launch_score(const void* q, kap_dtype q_dt, const int32_t* pos, float theta,
                         const void* summ, kap_dtype s_dt, const int32_t* bt, int32_t max_pages,
                         const int32_t* seq_lens, int32_t B, int32_t Hq, int32_t Hkv, int32_t D,
                         float* scores, hipStream_t stream) {
   ScoreArgs a{q, pos, log2((double)theta), summ, bt, max_pages, seq_lens, Hq, Hkv, Hq / Hkv,
-              scores};
+              scores, nullptr};
   dim3 grid((max_pages + kScorePagesPerBlock - 1) / kScorePagesPerBlock, Hkv, B);
 #define KAP_SCORE_LAUNCH(DD, ST, QT) \
   hipLaunchKernelGGL((score_kernel<DD, ST, QT>), grid, dim3(256), 0, stream, a)
@@ -143,6 +282,42 @@ kap_status launch_score(const void* q, kap_dtype q_dt, const int32_t* pos, float
   }
 #undef KAP_SCORE_LAUNCH
   return check_launch("score");
+}
+
+kap_status launch_score_pool(const void* q, kap_dtype q_dt, const int32_t* pos, float theta,
+                             const void* summ, kap_dtype s_dt, const int32_t* bt,
+                             int32_t max_pages, const int32_t* seq_lens, int32_t B, int32_t Hq,
+                             int32_t Hkv, int32_t D, float* scores, float* pooled,
+                             hipStream_t stream) {
+  if (Hkv > kPoolMaxHeads)
+    return fail(KAP_ERR_UNSUPPORTED, "pooled scoring with Hkv=%d > %d", Hkv, kPoolMaxHeads);
+  ScoreArgs a{q, pos, log2((double)theta), summ, bt, max_pages, seq_lens, Hq, Hkv, Hq / Hkv,
+              scores, pooled};
+  const size_t lds = (size_t)Hq * D * (q_dt == KAP_BF16 ? 2 : 4);
+  if (lds > kPoolMaxQueryLds)
+    return fail(KAP_ERR_UNSUPPORTED, "pooled scoring stages %zu query bytes (> %zu)", lds,
+                kPoolMaxQueryLds);
+  const int ppb = s_dt == KAP_BF16 ? (D == 128 ? pool_pages_per_block<128, uint16_t>()
+                                                : pool_pages_per_block<64, uint16_t>())
+                                   : (D == 128 ? pool_pages_per_block<128, float>()
+                                               : pool_pages_per_block<64, float>());
+  dim3 grid(B, (max_pages + ppb - 1) / ppb);
+#define KAP_POOL_LAUNCH(DD, ST, QT) \
+  hipLaunchKernelGGL((score_pool_kernel<DD, ST, QT>), grid, dim3(64 * Hkv), lds, stream, a)
+  const bool sb = s_dt == KAP_BF16, qb = q_dt == KAP_BF16;
+  if (D == 128) {
+    if (sb && qb) KAP_POOL_LAUNCH(128, uint16_t, uint16_t);
+    else if (sb) KAP_POOL_LAUNCH(128, uint16_t, float);
+    else if (qb) KAP_POOL_LAUNCH(128, float, uint16_t);
+    else KAP_POOL_LAUNCH(128, float, float);
+  } else {
+    if (sb && qb) KAP_POOL_LAUNCH(64, uint16_t, uint16_t);
+    else if (sb) KAP_POOL_LAUNCH(64, uint16_t, float);
+    else if (qb) KAP_POOL_LAUNCH(64, float, uint16_t);
+    else KAP_POOL_LAUNCH(64, float, float);
+  }
+#undef KAP_POOL_LAUNCH
+  return check_launch("score_pool");
 }
 
 }  // namespace kap

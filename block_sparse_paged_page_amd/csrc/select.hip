@@ -4,7 +4,7 @@
 // One 1024-thread block per selection row (request, or request x KV head).
 // Thread t owns the KPT consecutive pages [t*KPT, (t+1)*KPT) and keeps their
 // keys in registers.  Keys are mapped to order-preserving uint32 (NaN lowest,
-// -0 == +0); a 4-pass 8-bit radix select finds the k-th largest middle key T
+// -0 == +0); a 3-pass (12/10/10-bit) radix select finds the k-th largest middle key T
 // and how many of the keys equal to T are still needed; an index-ordered
 // block scan then admits those ties lowest index first, and a second scan
 // writes the chosen pages in ascending order.  Bit-exact: integer logic only,
@@ -71,8 +71,8 @@ __global__ __launch_bounds__(1024) void select_kernel(SelArgs a) {
   const int gr = blockIdx.x, b = blockIdx.y;
   const int G = a.per_head ? a.Hkv : 1;
   const int tid = threadIdx.x;
-  __shared__ int s_hist[16][256];  // one private histogram per wave
-  __shared__ int s_suf[8];  // [0..3] wave totals, [4] keys above the bin, [5] keys in the bin
+  __shared__ int s_hist[4096];
+  __shared__ int s_suf[8];  // [4] keys above the chosen bin, [5] keys in it
   __shared__ int s_wave[33];
   __shared__ uint32_t s_digit;
   const int N = min((max(a.seq_lens[b], 0) + kPage - 1) / kPage, a.max_pages);
@@ -93,7 +93,25 @@ __global__ __launch_bounds__(1024) void select_kernel(SelArgs a) {
   uint64_t cand = 0;  // bit j: page t*KPT+j is a middle candidate
   if constexpr (STAGED) {
     extern __shared__ float s_key[];  // [max_pages]
-    if (!all) {
+    if (!all && nh == 1) {
+      // one score row (per-head selection, or keys pooled beforehand): 8
+      // pages of loads in flight per thread, one round up to 8192 pages
+      constexpr int SU1 = 8;
+      const float sc = (float)a.Hkv;
+      for (int p0 = mid_lo; p0 < mid_hi; p0 += 1024 * SU1) {
+        float v[SU1];
+#pragma unroll
+        for (int u = 0; u < SU1; ++u) {
+          const int p = p0 + u * 1024 + tid;
+          v[u] = p < mid_hi ? base[p] : 0.f;
+        }
+#pragma unroll
+        for (int u = 0; u < SU1; ++u) {
+          const int p = p0 + u * 1024 + tid;
+          if (p < mid_hi) s_key[p] = a.per_head ? v[u] : __fdiv_rn(v[u], sc);
+        }
+      }
+    } else if (!all) {
       // up to 8 heads x 4 pages of loads in flight per thread (more would not
       // fit the 128 registers of a 1024-thread block), folded in head order
       constexpr int SU = 4, SG = 8;
@@ -165,50 +183,54 @@ __global__ __launch_bounds__(1024) void select_kernel(SelArgs a) {
     }
   }
 
-  // ---- radix select of the take-th largest candidate key
+  // ---- radix select of the take-th largest candidate key: three passes of
+  // 12, 10 and 10 bits.  The first digit is wide because keys of similar
+  // magnitude share their top bits: with 4096 bins the first histogram's
+  // atomics spread instead of piling onto a few bins.
   uint32_t prefix = 0, pmask = 0;
   int remaining = take;
-  int bin_count = 0;  // keys in the chosen bin of the last pass: after shift 0, those equal to T
+  int bin_count = 0;  // keys in the chosen bin of the last pass: after it, those equal to T
   if (take > 0) {
-    for (int shift = 24; shift >= 0; shift -= 8) {
-      for (int e = tid; e < 16 * 256; e += 1024) (&s_hist[0][0])[e] = 0;
+#pragma unroll
+    for (int pass = 0; pass < 3; ++pass) {
+      const int shift = pass == 0 ? 20 : (pass == 1 ? 10 : 0);
+      const int bpt = pass == 0 ? 4 : 1;  // bins per thread: 4096 or 1024 bins
+      const uint32_t dmask = pass == 0 ? 0xfffu : 0x3ffu;
+      for (int e = tid; e < 1024 * bpt; e += 1024) s_hist[e] = 0;
       __syncthreads();
-      const int wv = tid >> 6;
 #pragma unroll
       for (int j = 0; j < KPT; ++j)
         if (((cand >> j) & 1ull) && (key[j] & pmask) == prefix)
-          atomicAdd(&s_hist[wv][(key[j] >> shift) & 255u], 1);
+          atomicAdd(&s_hist[(key[j] >> shift) & dmask], 1);
       __syncthreads();
-      // bins 0..255 live in waves 0..3: suffix sums by shuffles, 3 barriers per pass
-      int h = 0;
-      if (tid < 256) {
+      // thread t owns bins [t * bpt, (t + 1) * bpt); the keys in bins above a
+      // thread's range come from a block scan over the threads
+      int hl[4];
+      int local = 0;
 #pragma unroll
-        for (int w = 0; w < 16; ++w) h += s_hist[w][tid];
+      for (int k = 0; k < 4; ++k) {
+        hl[k] = k < bpt ? s_hist[tid * bpt + k] : 0;
+        local += hl[k];
       }
-      int suf = h;  // inclusive suffix sum inside the wave (lanes above)
+      int tot;
+      const int excl = block_exclusive_scan(local, s_wave, &tot);
+      int above = tot - excl - local;
 #pragma unroll
-      for (int o = 1; o < 64; o <<= 1) {
-        const int y = __shfl_down(suf, o);
-        if ((tid & 63) + o < 64) suf += y;
-      }
-      if (tid < 256 && (tid & 63) == 0) s_suf[tid >> 6] = suf;  // wave totals
-      __syncthreads();
-      if (tid < 256) {
-        for (int w = (tid >> 6) + 1; w < 4; ++w) suf += s_suf[w];
-        const int above = suf - h;  // keys with digit > this bin
-        if (suf >= remaining && above < remaining) {
-          s_digit = tid;
+      for (int k = 3; k >= 0; --k) {
+        if (above < remaining && above + hl[k] >= remaining) {  // one bin in the block
+          s_digit = tid * bpt + k;
           s_suf[4] = above;
-          s_suf[5] = h;
+          s_suf[5] = hl[k];
         }
+        above += hl[k];
       }
       __syncthreads();
       const uint32_t d = s_digit;
       remaining -= s_suf[4];
       bin_count = s_suf[5];
       prefix |= d << shift;
-      pmask |= 0xffu << shift;
-      __syncthreads();
+      pmask |= dmask << shift;
+      // the next pass rewrites s_digit / s_suf only after two more barriers
     }
   }
   const uint32_t T = prefix;

@@ -4,6 +4,7 @@
  *
  * The path, per request and attention layer:
  *   1. kap_score_blocks  score every KV page: rotated query . block-mean K
+ *      (kap_score_pool_blocks also folds the heads into the pooled key)
  *   2. kap_select_topk   pick pages under an anchor / recent / middle split
  *   3. kap_compact_view  compact block table + slot mapping over the pick
  *   4. kap_decode_attn   q = 1 GQA decode over the compact view
@@ -98,6 +99,28 @@ KAP_API kap_status kap_score_blocks(const void* q, int32_t q_dtype, const int32_
                             int32_t num_pages, const int32_t* block_table, int32_t max_pages,
                             const int32_t* seq_lens, int32_t B, int32_t Hq, int32_t Hkv,
                             int32_t D, int32_t page_size, float* scores, kap_stream stream);
+
+/*
+ * Page scores of every KV head plus the head-pooled key in one launch, for
+ * pooled selection ([KRI] the connector mean-pools scores across heads before
+ * the per-request top-K).  scores (optional: NULL skips them) as in
+ * kap_score_blocks, bit for bit the same arithmetic per head, and
+ *   pooled[b][p] = (((S0 + S1) + S2) + ... + S_{Hkv-1}) / Hkv   for p < N_b
+ *                = -inf                                         for the other p < max_pages
+ * in fp32 with round-to-nearest adds in head order and one rounded division:
+ * exactly the key kap_select_topk forms for per_head = 0.  So kap_select_topk
+ * on (pooled, Hkv = 1) makes the same selection as on (scores, Hkv) pooled,
+ * while it reads one key row per request instead of Hkv.
+ *   pooled device out [B][max_pages] float
+ * Hkv <= 16 and Hq * D * (q element bytes) <= 64 KiB (else KAP_ERR_UNSUPPORTED);
+ * otherwise as kap_score_blocks.
+ */
+KAP_API kap_status kap_score_pool_blocks(const void* q, int32_t q_dtype, const int32_t* positions,
+                                 float rope_theta, const void* summary, int32_t sum_dtype,
+                                 int32_t num_pages, const int32_t* block_table,
+                                 int32_t max_pages, const int32_t* seq_lens, int32_t B,
+                                 int32_t Hq, int32_t Hkv, int32_t D, int32_t page_size,
+                                 float* scores, float* pooled, kap_stream stream);
 
 /*
  * Proxy query for early routing.  [ESKV] Interpretation: the side flow builds

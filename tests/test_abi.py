@@ -77,6 +77,30 @@ def test_score_validation(lib):
     assert _score(lib, B=0) == OK   # empty batch: nothing to do, no launch
 
 
+def _score_pool(lib, **kw):
+    args = dict(q=NP, q_dtype=1, positions=NP, theta=1e4, summary=NP, sum_dtype=1, num_pages=10,
+                bt=NP, max_pages=4, seq_lens=NP, B=1, Hq=8, Hkv=2, D=128, page_size=16,
+                scores=None, pooled=NP)
+    args.update(kw)
+    return lib.kap_score_pool_blocks(args["q"], args["q_dtype"], args["positions"], args["theta"],
+                                     args["summary"], args["sum_dtype"], args["num_pages"],
+                                     args["bt"], args["max_pages"], args["seq_lens"], args["B"],
+                                     args["Hq"], args["Hkv"], args["D"], args["page_size"],
+                                     args["scores"], args["pooled"], None)
+
+
+def test_score_pool_validation(lib):
+    assert _score_pool(lib, D=96) == UNSUPPORTED
+    assert _score_pool(lib, Hq=6, Hkv=4) == UNSUPPORTED
+    assert _score_pool(lib, Hq=32, Hkv=32) == UNSUPPORTED          # more than 16 KV heads
+    assert b"Hkv" in lib.kap_last_error()
+    assert _score_pool(lib, Hq=256, Hkv=16, q_dtype=0) == UNSUPPORTED  # 128 KiB of fp32 queries
+    assert _score_pool(lib, pooled=None) == INVALID                # pooled key is required
+    assert _score_pool(lib, q=None) == INVALID
+    assert _score_pool(lib, theta=0.5) == INVALID
+    assert _score_pool(lib, B=0) == OK
+
+
 def test_select_validation(lib):
     def sel(**kw):
         a = dict(scores=NP, B=2, Hkv=8, max_pages=2048, seq_lens=NP, page_size=16, per_head=0,

@@ -62,6 +62,36 @@ def test_score_parity(name):
 
 
 @pytest.mark.parametrize("name", list(CASES))
+def test_pooled_scoring(name):
+    """kap_score_pool_blocks: per-head scores within the scoring tolerance, the
+    pooled key equal to the head-order fp32 fold of those scores (bit for
+    bit), and top-K on the pooled key (one row, Hkv = 1) equal to the oracle's
+    pooled top-K on the per-head scores."""
+    c = get_case(name)
+    w = c.w
+    scores, pooled = kap.score_pool_blocks(c.q, c.pos, c.S, c.bt, c.L, w.Hkv)
+    _, pooled_only = kap.score_pool_blocks(c.q, c.pos, c.S, c.bt, c.L, w.Hkv, with_scores=False)
+    torch.cuda.synchronize()
+    s = scores.cpu().numpy()
+    check_scores(c, s)
+    fold = s[:, 0].copy()
+    for g in range(1, w.Hkv):
+        fold = fold + s[:, g]                      # float32 adds, round to nearest
+    fold = fold / np.float32(w.Hkv)
+    got = pooled.cpu().numpy()
+    np.testing.assert_array_equal(got.view(np.uint32), fold.view(np.uint32))
+    np.testing.assert_array_equal(pooled_only.cpu().numpy().view(np.uint32), got.view(np.uint32))
+    cap = c.budget() + 3
+    sel, cnt = kap.select_topk(pooled.view(w.B, 1, -1), c.L, c.anchor, c.recent, c.k_mid,
+                               c.budget(), cap)
+    sel_ref, cnt_ref = oracle.select(s, c.b["seq_lens"], c.b["anchor"], c.b["recent"], c.k_mid_h,
+                                     cap, per_head=False)
+    torch.cuda.synchronize()
+    np.testing.assert_array_equal(sel.cpu().numpy(), sel_ref)
+    np.testing.assert_array_equal(cnt.cpu().numpy(), cnt_ref)
+
+
+@pytest.mark.parametrize("name", list(CASES))
 def test_select_bit_exact_on_oracle_scores(name):
     c = get_case(name)
     cap = c.budget() + 3
