@@ -5,8 +5,8 @@ Workload (the 128K-context, 32B-class configuration): batch B (default 4) of
 16-token pages scattered over the pool, retention s = 451/8192 pages
 (A1R2K448), 1 % needle pages.  One step is one proposal-verification cycle of
 one attention layer, every stage of the path:
-  route   : kap_score_pool_blocks (head-pooled key) -> kap_select_topk on the
-            pooled key -> kap_compact_view
+  route   : kap_score_pool_blocks (head-pooled key) -> kap_select_compact (top-K on
+            the pooled key and the compact view, one launch)
   propose : k = 4 x kap_decode_attn over the compact view (tokens at P .. P+3)
   verify  : kap_verify_attn, 4 queries at 131072..131075 over all 8192 pages
 Each call reads a different layer copy of the pool (R copies, rotating), so
@@ -257,6 +257,9 @@ def _sweep(args, dev, w, label):
     res["select_pooled_us"] = time_call(lambda: kap.select_topk(pooled, L, anchor, recent, kmid,
                                                                 budget, budget, sel=sel, cnt=cnt),
                                         args.steps, st)
+    res["select_compact_pooled_us"] = time_call(
+        lambda: kap.select_compact(pooled, L, anchor, recent, kmid, budget, budget, bt, pos, 1,
+                                   cnt=cnt, out=cv), args.steps, st)
     kv_tok = Hkv * 2 * D * EB
     sweep = []
     for num, den in ((1, 100), (2, 100), (55, 1000), (10, 100), (25, 100), (50, 100), (1, 1)):
@@ -556,8 +559,7 @@ def run_mixed(args, dev):
 
     def route():
         kap.score_pool_blocks(q, pos, S, bt, L, Hkv, pooled=pooled.view(B, -1), with_scores=False)
-        kap.select_topk(pooled, L, anchor, recent, kmid, cap, cap, sel=sel, cnt=cnt)
-        kap.compact_view(sel, cnt, bt, L, pos, 1, out=cv)
+        kap.select_compact(pooled, L, anchor, recent, kmid, cap, cap, bt, pos, 1, cnt=cnt, out=cv)
 
     route()
     torch.cuda.synchronize()
@@ -639,8 +641,8 @@ def run_commit(args, dev):
     def route(ly):
         kap.score_pool_blocks(q_route, pos, ly.S, bt, L, Hkv, pooled=pooled.view(B, -1),
                               with_scores=False)
-        kap.select_topk(pooled, L, anchor, recent, k_mid, cap, cap, sel=sel, cnt=cnt)
-        kap.compact_view(sel, cnt, bt, L, pos, w.q_len, out=cv)       # slot mapping of the window
+        kap.select_compact(pooled, L, anchor, recent, k_mid, cap, cap, bt, pos, w.q_len, cnt=cnt,
+                           out=cv)                                # + slot mapping of the window
 
     def propose(ly):
         for j in range(K_PROPOSE):
@@ -819,8 +821,8 @@ def main():
         lay = next_layer()
         kap.score_pool_blocks(q_route, pos, lay.S, bt, L, Hkv, pooled=pooled.view(B, -1),
                               with_scores=False)
-        kap.select_topk(pooled, L, anchor, recent, k_mid, budget, cap, sel=sel, cnt=cnt)
-        kap.compact_view(sel, cnt, bt, L, pos, 1, out=cview)
+        kap.select_compact(pooled, L, anchor, recent, k_mid, budget, cap, bt, pos, 1, cnt=cnt,
+                           out=cview)
         if ev:
             ev[1].record(stream)
         for j in range(K_PROPOSE):

@@ -38,6 +38,8 @@ _SIGS = {
     "kap_proxy_query": ([_P, _P, _I32, _I32, _I32, _P, _P, _SZ, _P], _I32),
     "kap_select_topk": ([_P, _I32, _I32, _I32, _P, _I32, _I32, _P, _P, _P, _I32, _I32, _P, _P, _P],
                         _I32),
+    "kap_select_compact": ([_P, _I32, _I32, _I32, _P, _I32, _I32, _P, _P, _P, _I32, _I32, _P, _P,
+                            _I32, _P, _P, _P, _P, _P, _P], _I32),
     "kap_budget_from_ratio": ([_I32, _I64, _I64, _I32, _I32], _I32),
     "kap_compact_view": ([_P, _P, _I32, _I32, _I32, _P, _I32, _P, _I32, _P, _I32, _P, _P, _P, _P,
                           _P], _I32),
@@ -210,6 +212,31 @@ def compact_view(sel, cnt, block_table, seq_lens, positions, q_new, out=None, st
                               _p(clen), _p(slot), _stream(stream))
     _check(st, "kap_compact_view")
     return cbt, clog, clen, slot
+
+
+def select_compact(scores, seq_lens, anchor, recent, k_mid, max_budget, capacity, block_table,
+                   positions, q_new, per_head=False, cnt=None, out=None, stream=None):
+    """kap_select_compact -> (sel_count, (compact_bt, compact_logical, compact_len,
+    slot_mapping)); compact_logical is the selection list."""
+    lib = load()
+    B, Hkv, max_pages = scores.shape
+    G = Hkv if per_head else 1
+    dev = scores.device
+    if cnt is None:
+        cnt = torch.empty((B, G), dtype=torch.int32, device=dev)
+    if out is None:
+        out = (torch.empty((B, G, capacity), dtype=torch.int32, device=dev),
+               torch.empty((B, G, capacity), dtype=torch.int32, device=dev),
+               torch.empty((B, G), dtype=torch.int32, device=dev),
+               torch.empty((B, max(q_new, 1)), dtype=torch.int64, device=dev))
+    cbt, clog, clen, slot = out
+    st = lib.kap_select_compact(_p(scores), B, Hkv, max_pages, _p(seq_lens), 16,
+                                int(bool(per_head)), _p(anchor), _p(recent), _p(k_mid),
+                                int(max_budget), int(capacity), _p(block_table), _p(positions),
+                                int(q_new), _p(cnt), _p(cbt), _p(clog), _p(clen), _p(slot),
+                                _stream(stream))
+    _check(st, "kap_select_compact")
+    return cnt, out
 
 
 def _scale(D, scale):

@@ -198,6 +198,38 @@ int32_t kap_budget_from_ratio(int32_t n_pages, int64_t s_num, int64_t s_den, int
   return (int32_t)budget;
 }
 
+kap_status kap_select_compact(const float* scores, int32_t B, int32_t Hkv, int32_t max_pages,
+                              const int32_t* seq_lens, int32_t page_size, int32_t per_head,
+                              const int32_t* anchor, const int32_t* recent,
+                              const int32_t* k_mid, int32_t max_budget, int32_t capacity,
+                              const int32_t* block_table, const int32_t* positions,
+                              int32_t q_new, int32_t* sel_count, int32_t* compact_bt,
+                              int32_t* compact_logical, int32_t* compact_len,
+                              int64_t* slot_mapping, kap_stream stream) {
+  g_err[0] = 0;
+  if (B < 0 || Hkv <= 0 || max_pages < 0 || capacity < 0 || max_budget < 0 || q_new < 0)
+    return fail(KAP_ERR_INVALID_ARG,
+                "bad size (B=%d Hkv=%d max_pages=%d capacity=%d budget=%d q_new=%d)", B, Hkv,
+                max_pages, capacity, max_budget, q_new);
+  if (page_size != kPage) return fail(KAP_ERR_UNSUPPORTED, "page_size %d (16)", page_size);
+  if (max_pages > kMaxSelectPages)
+    return fail(KAP_ERR_UNSUPPORTED, "max_pages %d > %d", max_pages, kMaxSelectPages);
+  if (per_head != 0 && per_head != 1) return fail(KAP_ERR_INVALID_ARG, "per_head %d", per_head);
+  if (max_budget > capacity)
+    return fail(KAP_ERR_CAPACITY, "budget %d pages exceeds compact capacity %d", max_budget,
+                capacity);
+  if (B == 0) return KAP_OK;
+  if (!scores || !seq_lens || !anchor || !recent || !k_mid || !block_table || !sel_count ||
+      !compact_bt || !compact_logical || !compact_len)
+    return fail(KAP_ERR_INVALID_ARG, "null pointer");
+  if (q_new > 0 && (!slot_mapping || !positions))
+    return fail(KAP_ERR_INVALID_ARG, "slot mapping needs positions and an output");
+  return launch_select(scores, B, Hkv, max_pages, seq_lens, per_head, anchor, recent, k_mid,
+                       capacity, compact_logical, sel_count, (hipStream_t)stream, block_table,
+                       positions, q_new, compact_bt, compact_len,
+                       q_new > 0 ? slot_mapping : nullptr);
+}
+
 kap_status kap_compact_view(const int32_t* sel_pages, const int32_t* sel_count, int32_t B,
                             int32_t G, int32_t capacity, const int32_t* block_table,
                             int32_t max_pages, const int32_t* seq_lens, int32_t page_size,

@@ -133,7 +133,10 @@ kap_status launch_score_pool(const void* q, kap_dtype q_dt, const int32_t* pos, 
 kap_status launch_select(const float* scores, int32_t B, int32_t Hkv, int32_t max_pages,
                          const int32_t* seq_lens, int32_t per_head, const int32_t* anchor,
                          const int32_t* recent, const int32_t* k_mid, int32_t capacity,
-                         int32_t* sel, int32_t* cnt, hipStream_t stream);
+                         int32_t* sel, int32_t* cnt, hipStream_t stream,
+                         const int32_t* bt = nullptr, const int32_t* pos = nullptr,
+                         int32_t q_new = 0, int32_t* cbt = nullptr, int32_t* clen = nullptr,
+                         int64_t* slot = nullptr);
 kap_status launch_compact(const int32_t* sel, const int32_t* cnt, int32_t B, int32_t G,
                           int32_t cap, const int32_t* bt, int32_t max_pages,
                           const int32_t* seq_lens, const int32_t* pos, int32_t q_new,

@@ -28,6 +28,13 @@ struct SelArgs {
   int32_t cap;
   int32_t* sel;
   int32_t* cnt;
+  // compact view written by the same launch (cbt == nullptr: selection only)
+  const int32_t* bt;
+  const int32_t* pos;
+  int32_t q_new;
+  int32_t* cbt;
+  int32_t* clen;
+  int64_t* slot;
 };
 
 __device__ __forceinline__ uint32_t order_key(float f) {
@@ -75,9 +82,31 @@ __global__ __launch_bounds__(1024) void select_kernel(SelArgs a) {
   __shared__ int s_suf[8];  // [4] keys above the chosen bin, [5] keys in it
   __shared__ int s_wave[33];
   __shared__ uint32_t s_digit;
-  const int N = min((max(a.seq_lens[b], 0) + kPage - 1) / kPage, a.max_pages);
+  __shared__ int s_last;  // the row's last logical page is in its list
+  if (a.cbt) {  // uniform
+    if (tid == 0) s_last = 0;
+    __syncthreads();
+  }
+  const int L = a.seq_lens[b];
+  const int N = min((max(L, 0) + kPage - 1) / kPage, a.max_pages);
   const int na = max(a.anchor[b], 0), nr = max(a.recent[b], 0), nk = a.k_mid[b];
   int32_t* out = a.sel + ((int64_t)b * G + gr) * a.cap;
+  const int32_t* btrow = a.bt ? a.bt + (int64_t)b * a.max_pages : nullptr;
+  // slot mapping of the new tokens through the full table (first row of a request)
+  auto write_slots = [&](const int32_t* tab) {
+    if (gr != 0 || !a.slot) return;
+    const long long p0 = a.pos[b];
+    for (int i = tid; i < a.q_new; i += 1024) {
+      const long long t = p0 + i;
+      const long long p = t / kPage;
+      long long sl = -1;
+      if (t >= 0 && p < a.max_pages) {
+        const int32_t phys = tab[p];
+        if (phys >= 0) sl = (long long)phys * kPage + t % kPage;
+      }
+      a.slot[(int64_t)b * a.q_new + i] = sl;
+    }
+  };
   const bool all = (na + nr >= N);
   const int mid_lo = na, mid_hi = N - nr;
   const int take = all ? 0 : min(max(nk, 0), mid_hi - mid_lo);
@@ -91,9 +120,19 @@ __global__ __launch_bounds__(1024) void select_kernel(SelArgs a) {
   const float* base = a.scores + ((int64_t)b * a.Hkv + (a.per_head ? gr : 0)) * a.max_pages;
   uint32_t key[KPT];
   uint64_t cand = 0;  // bit j: page t*KPT+j is a middle candidate
+  extern __shared__ float s_dyn[];  // STAGED: keys [max_pages], then (compact) the table row
+  int32_t* s_bt = (int32_t*)(s_dyn + a.max_pages);
+  bool bt_lds = false;  // compact view: the table row is in s_bt (block-uniform)
   if constexpr (STAGED) {
-    extern __shared__ float s_key[];  // [max_pages]
+    float* s_key = s_dyn;
     if (!all && nh == 1) {
+      // compact view: the request's table row goes to LDS for the output
+      // gather; its loads go first, so they have landed with the keys
+      int btv[KPT];
+      if (a.cbt) {
+#pragma unroll
+        for (int u = 0; u < KPT; ++u) btv[u] = btrow[min(u * 1024 + tid, a.max_pages - 1)];
+      }
       // one score row (per-head selection, or keys pooled beforehand): 8
       // pages of loads in flight per thread, one round up to 8192 pages
       constexpr int SU1 = 8;
@@ -110,6 +149,12 @@ __global__ __launch_bounds__(1024) void select_kernel(SelArgs a) {
           const int p = p0 + u * 1024 + tid;
           if (p < mid_hi) s_key[p] = a.per_head ? v[u] : __fdiv_rn(v[u], sc);
         }
+      }
+      if (a.cbt) {
+#pragma unroll
+        for (int u = 0; u < KPT; ++u)
+          if (u * 1024 + tid < a.max_pages) s_bt[u * 1024 + tid] = btv[u];
+        bt_lds = true;
       }
     } else if (!all) {
       // up to 8 heads x 4 pages of loads in flight per thread (more would not
@@ -141,6 +186,7 @@ __global__ __launch_bounds__(1024) void select_kernel(SelArgs a) {
       }
     }
     __syncthreads();
+    if (bt_lds) write_slots(s_bt);  // from the staged row: no load at the end
 #pragma unroll
     for (int j = 0; j < KPT; ++j) {
       const int p = pbase + j;
@@ -267,30 +313,55 @@ __global__ __launch_bounds__(1024) void select_kernel(SelArgs a) {
     if (c) chosen |= 1ull << j;
   }
   const int n_ch = __popcll(chosen);
+  if (N > 0 && (N - 1) / KPT == tid && ((chosen >> ((N - 1) % KPT)) & 1ull)) s_last = 1;
   int total;
-  int pos = block_exclusive_scan(n_ch, s_wave, &total);
+  int pos = block_exclusive_scan(n_ch, s_wave, &total);  // (its barriers publish s_last)
+  const int64_t row = (int64_t)b * G + gr;
+  int gb[KPT];  // compact view without the staged row: one straight-line gather
+  if (a.cbt && !bt_lds) {
+#pragma unroll
+    for (int j = 0; j < KPT; ++j) gb[j] = btrow[min(pbase + j, a.max_pages - 1)];
+  }
 #pragma unroll
   for (int j = 0; j < KPT; ++j) {
     if ((chosen >> j) & 1ull) {
-      if (pos < a.cap) out[pos] = pbase + j;
+      if (pos < a.cap) {
+        out[pos] = pbase + j;
+        if (a.cbt) a.cbt[row * a.cap + pos] = bt_lds ? s_bt[pbase + j] : gb[j];
+      }
       ++pos;
     }
   }
   const int c = min(total, a.cap);
-  for (int j = c + tid; j < a.cap; j += 1024) out[j] = -1;
-  if (tid == 0) a.cnt[(int64_t)b * G + gr] = c;
+  for (int j = c + tid; j < a.cap; j += 1024) {
+    out[j] = -1;
+    if (a.cbt) a.cbt[row * a.cap + j] = -1;
+  }
+  if (tid == 0) a.cnt[row] = c;
+  if (a.cbt) {
+    // compact view: every listed page holds 16 tokens except the last logical
+    // page N - 1, listed last, when it made the list (total <= capacity)
+    if (tid == 0) {
+      const int deficit = (s_last && total <= a.cap) ? kPage - min(kPage, L - (N - 1) * kPage) : 0;
+      a.clen[row] = c * kPage - deficit;
+    }
+    if (!bt_lds) write_slots(btrow);
+  }
 }
 
 kap_status launch_select(const float* scores, int32_t B, int32_t Hkv, int32_t max_pages,
                          const int32_t* seq_lens, int32_t per_head, const int32_t* anchor,
                          const int32_t* recent, const int32_t* k_mid, int32_t capacity,
-                         int32_t* sel, int32_t* cnt, hipStream_t stream) {
-  SelArgs a{scores, Hkv, max_pages, seq_lens, per_head, anchor, recent, k_mid, capacity, sel, cnt};
+                         int32_t* sel, int32_t* cnt, hipStream_t stream, const int32_t* bt,
+                         const int32_t* pos, int32_t q_new, int32_t* cbt, int32_t* clen,
+                         int64_t* slot) {
+  SelArgs a{scores, Hkv, max_pages, seq_lens, per_head, anchor, recent, k_mid, capacity, sel, cnt,
+            bt, pos, q_new, cbt, clen, slot};
   const int G = per_head ? Hkv : 1;
   dim3 grid(G, B);
   const int kpt = (max_pages + 1023) / 1024;
   const bool staged = max_pages <= kSelectStagedPages;
-  const size_t lds = staged ? (size_t)max_pages * sizeof(float) : 0;
+  const size_t lds = staged ? (size_t)max_pages * sizeof(float) * (cbt ? 2 : 1) : 0;
 #define KAP_SEL(K)                                                                              \
   do {                                                                                          \
     if (staged) hipLaunchKernelGGL((select_kernel<K, true>), grid, dim3(1024), lds, stream, a); \

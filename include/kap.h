@@ -7,6 +7,7 @@
  *      (kap_score_pool_blocks also folds the heads into the pooled key)
  *   2. kap_select_topk   pick pages under an anchor / recent / middle split
  *   3. kap_compact_view  compact block table + slot mapping over the pick
+ *      (kap_select_compact does steps 2 and 3 in one launch)
  *   4. kap_decode_attn   q = 1 GQA decode over the compact view
  *   5. kap_verify_attn   short query window over the full paged KV
  * and around it: kap_append_kv writes the window's K/V through the slot
@@ -196,6 +197,24 @@ KAP_API kap_status kap_compact_view(const int32_t* sel_pages, const int32_t* sel
                             const int32_t* positions, int32_t q_new, int32_t* compact_bt,
                             int32_t* compact_logical, int32_t* compact_len,
                             int64_t* slot_mapping, kap_stream stream);
+
+/*
+ * Top-K and compact view in one launch: kap_select_topk followed by
+ * kap_compact_view over its output, with the same results ([KAP] selected-KV
+ * view: the selection is compacted in access order).  compact_logical is the
+ * selection list itself (what kap_select_topk writes to sel_pages), sel_count
+ * its length; compact_bt, compact_len and slot_mapping are as
+ * kap_compact_view writes them.  Arguments as in those two calls; capacity
+ * may be 0 (counts and lengths are still written).
+ */
+KAP_API kap_status kap_select_compact(const float* scores, int32_t B, int32_t Hkv,
+                              int32_t max_pages, const int32_t* seq_lens, int32_t page_size,
+                              int32_t per_head, const int32_t* anchor, const int32_t* recent,
+                              const int32_t* k_mid, int32_t max_budget, int32_t capacity,
+                              const int32_t* block_table, const int32_t* positions,
+                              int32_t q_new, int32_t* sel_count, int32_t* compact_bt,
+                              int32_t* compact_logical, int32_t* compact_len,
+                              int64_t* slot_mapping, kap_stream stream);
 
 /*
  * Workspace for kap_decode_attn (q_len = 1) and kap_verify_attn: the split-K

@@ -117,6 +117,24 @@ def test_select_validation(lib):
     assert sel(B=0) == OK
 
 
+def test_select_compact_validation(lib):
+    def call(**kw):
+        args = dict(scores=NP, B=2, Hkv=8, max_pages=100, L=NP, ps=16, per_head=0, a=NP, r=NP, k=NP,
+                    budget=10, cap=10, bt=NP, pos=NP, q_new=1, cnt=NP, cbt=NP, clog=NP, clen=NP,
+                    slot=NP)
+        args.update(kw)
+        return lib.kap_select_compact(*args.values(), None)
+    assert call(budget=11) == CAPACITY
+    assert call(ps=8) == UNSUPPORTED
+    assert call(max_pages=70000) == UNSUPPORTED
+    assert call(per_head=2) == INVALID
+    assert call(q_new=-1) == INVALID
+    assert call(bt=None) == INVALID
+    assert call(slot=None) == INVALID                 # q_new > 0 needs an output
+    assert b"slot" in lib.kap_last_error()
+    assert call(B=0) == OK
+
+
 def test_compact_validation(lib):
     def cv(**kw):
         a = dict(sel=NP, cnt=NP, B=1, G=1, cap=8, bt=NP, max_pages=8, seq_lens=NP, page_size=16,

@@ -61,13 +61,11 @@ def test_score_parity(name):
     check_scores(c, scores.cpu().numpy())
 
 
-@pytest.mark.parametrize("name", list(CASES))
-def test_pooled_scoring(name):
+def _check_pooled(c):
     """kap_score_pool_blocks: per-head scores within the scoring tolerance, the
     pooled key equal to the head-order fp32 fold of those scores (bit for
     bit), and top-K on the pooled key (one row, Hkv = 1) equal to the oracle's
     pooled top-K on the per-head scores."""
-    c = get_case(name)
     w = c.w
     scores, pooled = kap.score_pool_blocks(c.q, c.pos, c.S, c.bt, c.L, w.Hkv)
     _, pooled_only = kap.score_pool_blocks(c.q, c.pos, c.S, c.bt, c.L, w.Hkv, with_scores=False)
@@ -89,6 +87,11 @@ def test_pooled_scoring(name):
     torch.cuda.synchronize()
     np.testing.assert_array_equal(sel.cpu().numpy(), sel_ref)
     np.testing.assert_array_equal(cnt.cpu().numpy(), cnt_ref)
+
+
+@pytest.mark.parametrize("name", list(CASES))
+def test_pooled_scoring(name):
+    _check_pooled(get_case(name))
 
 
 @pytest.mark.parametrize("name", list(CASES))
@@ -255,9 +258,11 @@ def test_verify_row_tiles(name, q_len, D):
     (16, 1, 64, "bf16"),     # MQA, head_dim 64
     (128, 8, 128, "bf16"),   # GQA 16:1 (decode 16 rows, verify 64 rows per KV head)
     (32, 8, 64, "f32"),      # fp32 path, head_dim 64, verify 64 rows (two 32-row slices)
+    (32, 16, 128, "bf16"),   # 16 KV heads: the widest pooled-scoring block
 ])
 def test_head_layouts(Hq, Hkv, D, dtype):
-    """Score, top-K, selected decode and a 16-token verify on other head shapes."""
+    """Score (per head and pooled), top-K, selected decode and a 16-token verify on
+    other head shapes."""
     over = dict(B=2, seq_lens=[3000, 1777], Hq=Hq, Hkv=Hkv, D=D, q_len=16, dtype=dtype)
     if dtype == "f32":
         over["sigma"] = 1.0 / 8.0
@@ -266,6 +271,7 @@ def test_head_layouts(Hq, Hkv, D, dtype):
     s = kap.score_blocks(c.q, c.pos, c.S, c.bt, c.L, w.Hkv)
     torch.cuda.synchronize()
     check_scores(c, s.cpu().numpy())
+    _check_pooled(c)
     cap = c.budget()
     s_ref = oracle.score(c.b["q"], c.b["positions"], c.summ_l, c.btl, c.b["seq_lens"], w.Hkv)
     sel_ref, cnt_ref = oracle.select(s_ref.astype(np.float32), c.b["seq_lens"], c.b["anchor"],
@@ -356,6 +362,38 @@ def test_adversarial_selection_keys():
         sref, cref = oracle.select(S, L, a, r, k, cap, per_head=per_head)
         np.testing.assert_array_equal(sel.cpu().numpy(), sref)
         np.testing.assert_array_equal(cnt.cpu().numpy(), cref)
+
+
+def test_select_compact_matches_the_two_calls():
+    """kap_select_compact writes exactly what kap_select_topk then kap_compact_view
+    write (both pinned to the oracle above), on adversarial keys, ragged and
+    empty rows, unallocated table entries, a window past the table, and rows
+    the device budget truncates to the capacity."""
+    rng = np.random.default_rng(22)
+    palette = np.array([0.0, -0.0, 1.0, -1.0, 2.5, np.inf, -np.inf, np.nan, 1.0, 0.5], np.float32)
+    B, H, P = 6, 4, 3000
+    S = palette[rng.integers(0, len(palette), size=(B, H, P))]
+    L = np.array([16 * 3000, 16 * 2999 + 1, 100, 16 * 5, 1, 0], np.int32)
+    a = np.array([1, 4, 0, 2, 0, 1], np.int32)
+    r = np.array([2, 4, 3, 3, 0, 0], np.int32)
+    k = np.array([110, 1000, 2, 0, 5, 3], np.int32)
+    bt = np.stack([rng.permutation(B * P)[:P] for _ in range(B)]).astype(np.int32)
+    bt[1, 2999] = -1                                   # an unallocated last page
+    pos = L.copy()                                     # request 0's window lies past its table
+    q_new = 5
+    for per_head in (False, True):
+        for cap in (2000, 600):                        # 600: request 1's 1008 pages are cut
+            sel, cnt = kap.select_topk(t(S), t(L), t(a), t(r), t(k), cap, cap, per_head=per_head)
+            cv = kap.compact_view(sel, cnt, t(bt), t(L), t(pos), q_new)
+            cnt2, cv2 = kap.select_compact(t(S), t(L), t(a), t(r), t(k), cap, cap, t(bt), t(pos),
+                                           q_new, per_head=per_head)
+            torch.cuda.synchronize()
+            np.testing.assert_array_equal(cnt2.cpu().numpy(), cnt.cpu().numpy())
+            np.testing.assert_array_equal(cv2[1].cpu().numpy(), sel.cpu().numpy())
+            for x, y in zip(cv2, cv):
+                np.testing.assert_array_equal(x.cpu().numpy(), y.cpu().numpy())
+            if cap == 600:
+                assert int(cnt.cpu().numpy()[1].max()) == 600
 
 
 def test_empty_and_single_token_rows():
