@@ -48,6 +48,9 @@ def parse():
     ap.add_argument("--batch", type=int, default=4)
     ap.add_argument("--layers", type=int, default=0, help="layer copies (0: auto)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--graph", action="store_true",
+                    help="replay each call of the cycle from its own HIP graph (default: launch "
+                         "from Python; on this stack a graph launch adds ~7 us per call)")
     ap.add_argument("--quiet", action="store_true")
     ap.add_argument("--workload", default="qwen32b_128k",
                     choices=["qwen32b_128k", "qwen32b_128k_sweep", "qwen32b_128k_commit",
@@ -815,35 +818,67 @@ def main():
         state["layer"] += 1
         return lay
 
-    def step(ev=None):
-        if ev:
-            ev[0].record(stream)
+    def step_calls():
+        """One cycle's calls in order, each bound to the layer copy it reads."""
+        calls = []
         lay = next_layer()
-        kap.score_pool_blocks(q_route, pos, lay.S, bt, L, Hkv, pooled=pooled.view(B, -1),
-                              with_scores=False)
-        kap.select_compact(pooled, L, anchor, recent, k_mid, budget, cap, bt, pos, 1, cnt=cnt,
-                           out=cview)
-        if ev:
-            ev[1].record(stream)
+        calls.append(lambda lay=lay: (
+            kap.score_pool_blocks(q_route, pos, lay.S, bt, L, Hkv, pooled=pooled.view(B, -1),
+                                  with_scores=False),
+            kap.select_compact(pooled, L, anchor, recent, k_mid, budget, cap, bt, pos, 1,
+                               cnt=cnt, out=cview)))
         for j in range(K_PROPOSE):
             lay = next_layer()
-            kap.decode_attn(q_prop[j], pos_prop[j], lay.K, lay.V, cview[0], cview[2], G=1,
-                            out=dec_out, workspace=ws)
-            if ev:
-                ev[2 + j].record(stream)
+            calls.append(lambda lay=lay, j=j: kap.decode_attn(
+                q_prop[j], pos_prop[j], lay.K, lay.V, cview[0], cview[2], G=1, out=dec_out,
+                workspace=ws))
         lay = next_layer()
-        kap.verify_attn(qv, pos, lay.K, lay.V, bt, L, out=ver_out, workspace=ws)
-        if ev:
-            ev[2 + K_PROPOSE].record(stream)
+        calls.append(lambda lay=lay: kap.verify_attn(qv, pos, lay.K, lay.V, bt, L, out=ver_out,
+                                                     workspace=ws))
+        return calls
 
-    for _ in range(args.warmup):
-        step()
+    # The layer rotation repeats every `period` cycles.  With --graph, each
+    # call of those cycles is captured once as its own HIP graph ([KAP] shape
+    # stabilization: proposal and verification replay as graphs) and replayed;
+    # the events between the graph launches give per-call times.  Measured on
+    # MI355X with ROCm 7.2, a graph launch costs ~7 us more per call than the
+    # direct launches, whose host overhead already hides behind the GPU work.
+    period = R // math.gcd(R, 2 + K_PROPOSE)
+    cycles = [step_calls() for _ in range(period)]
+    for i in range(max(args.warmup, period)):
+        for fn in cycles[i % period]:
+            fn()
     torch.cuda.synchronize()
+    if not args.graph:
+        runs = cycles
+    else:
+        runs = []
+        for calls in cycles:
+            gs = []
+            for fn in calls:
+                g = torch.cuda.CUDAGraph()
+                with torch.cuda.graph(g):
+                    fn()
+                gs.append(g.replay)
+            runs.append(gs)
+        torch.cuda.synchronize()
+        for _ in range(2):
+            for gs in runs:
+                for r in gs:
+                    r()
+        torch.cuda.synchronize()
+
+    def step(i, ev):
+        ev[0].record(stream)
+        for c, fn in enumerate(runs[i % period]):
+            fn()
+            ev[c + 1].record(stream)
+
     evs = [[torch.cuda.Event(enable_timing=True) for _ in range(n_ev)] for _ in range(args.steps)]
     torch.cuda.synchronize()
     t_start = time.perf_counter()
     for i in range(args.steps):
-        step(evs[i])
+        step(i, evs[i])
     torch.cuda.synchronize()
     t_total = time.perf_counter() - t_start
     ms_step = 1e3 * t_total / args.steps
@@ -852,7 +887,7 @@ def main():
     ver_ms = np.mean([e[1 + K_PROPOSE].elapsed_time(e[2 + K_PROPOSE]) for e in evs])
 
     # selected pages (for byte accounting) -- read once after timing
-    sel_h = sel.cpu().numpy()[:, 0]
+    sel_h = cview[1].cpu().numpy()[:, 0]       # the compact logical table is the selection
     cnt_h = cnt.cpu().numpy()[:, 0]
     sel_pages = [sel_h[i, :cnt_h[i]] for i in range(B)]
     nbytes = algorithmic_bytes(w, b, sel_pages)
@@ -919,6 +954,7 @@ def main():
                          f"16-token pages, s=451/8192 (A1R2K448 pooled), step = route + "
                          f"{K_PROPOSE} selected-KV decodes + 4-query full-context verify"),
             "global_batch": B, "seq_len": int(w.seq_lens[0]), "layer_copies": R,
+            "launch": "hip_graph_per_call" if args.graph else "direct",
         },
         "roofline": roofline,
         "kernels": {
