@@ -92,14 +92,14 @@ def algorithmic_bytes(w, b, sel_pages):
 
 
 def kernel_source_hash():
-    """Hash of the attention kernel's code (attn.hip and its shared header) with
-    comments and blank lines removed, so that only code changes invalidate
-    counters taken earlier."""
+    """Hash of the attention kernel's code (attn.hip and the device-side header
+    it shares) with comments and blank lines removed, so that only code changes
+    invalidate counters taken earlier."""
     import hashlib
     import re
     csrc = os.path.join(ROOT, "block_sparse_paged_page_amd", "csrc")
     h = hashlib.sha256()
-    for name in ("attn.hip", "kap_internal.h"):
+    for name in ("attn.hip", "kap_device.h"):
         text = open(os.path.join(csrc, name)).read()
         text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
         text = re.sub(r"//[^\n]*", "", text)

@@ -1,84 +1,9 @@
-// Internal declarations shared by the libkap HIP sources (gfx950 only).
+// Internal host-side declarations shared by the libkap HIP sources.
 #pragma once
 
-#include <hip/hip_runtime.h>
-#include <stdint.h>
-
-#include "../../include/kap.h"
+#include "kap_device.h"
 
 namespace kap {
-
-// ---------------------------------------------------------------- constants
-constexpr int kPage = 16;            // tokens per KV page
-constexpr int kTargetItems = 1280;   // split-K work items aimed at per call (measured best at 128K, B = 4)
-constexpr int kMinChunk = 2;         // minimum pages per work item
-constexpr int kPipelinedMaxPages = 32;  // items up to this many pages run the pipelined kernel
-constexpr int kMaxSelectPages = 65536;
-constexpr int kMaxPlanRows = 4096;      // batch x KV heads per attention call
-
-// ---------------------------------------------------------------- device types
-typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
-typedef short short4v __attribute__((ext_vector_type(4)));
-typedef float floatx4 __attribute__((ext_vector_type(4)));
-
-__device__ __forceinline__ float bf16_to_f32(uint16_t x) {
-  return __uint_as_float(((uint32_t)x) << 16);
-}
-
-// round-to-nearest-even, NaN kept quiet
-__device__ __forceinline__ uint16_t f32_to_bf16(float f) {
-  uint32_t u = __float_as_uint(f);
-  if ((u & 0x7fffffffu) > 0x7f800000u) return (uint16_t)0x7fc0;
-  u += 0x7fffu + ((u >> 16) & 1u);
-  return (uint16_t)(u >> 16);
-}
-
-typedef __bf16 bf16x2v __attribute__((ext_vector_type(2)));
-typedef float float2v __attribute__((ext_vector_type(2)));
-
-// Two floats -> packed bf16 pair (low half = a), one round-to-nearest-even
-// conversion instruction on gfx950.
-__device__ __forceinline__ uint32_t pack_bf16x2(float a, float b) {
-  const float2v x = {a, b};
-  return __builtin_bit_cast(uint32_t, __builtin_convertvector(x, bf16x2v));
-}
-
-template <typename T>
-__device__ __forceinline__ float load_as_f32(const T* p, int64_t i);
-template <>
-__device__ __forceinline__ float load_as_f32<float>(const float* p, int64_t i) {
-  return p[i];
-}
-template <>
-__device__ __forceinline__ float load_as_f32<uint16_t>(const uint16_t* p, int64_t i) {
-  return bf16_to_f32(p[i]);
-}
-
-// sin and cos of pos * inv_freq, both fp64.  The angle reaches ~1.3e5 rad at
-// 128K context, so it is first reduced by 2*pi (split in two parts, Cody-Waite)
-// to keep the library call on its small-argument path.
-__device__ __forceinline__ void rope_sincos(double pos, int pair, int D, double log2_theta,
-                                            double* s, double* c) {
-  const double inv_freq = exp2(-(2.0 * pair / D) * log2_theta);
-  const double ang = pos * inv_freq;
-  const double k = rint(ang * 0.15915494309189535);       // 1 / (2 pi)
-  double r = fma(-k, 6.283185307179586, ang);             // 2 pi, high part
-  r = fma(-k, 2.4492935982947064e-16, r);                 // 2 pi, low part
-  sincos(r, s, c);
-}
-
-// Workgroup barrier that orders LDS only: global loads in flight stay in
-// flight across it (__syncthreads also waits for every outstanding load).
-__device__ __forceinline__ void lds_barrier() {
-  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup", "local");
-  __builtin_amdgcn_s_barrier();
-  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup", "local");
-}
-
-__device__ __forceinline__ float wave_max_xor(float v, int from, int to) {
-  for (int m = from; m < to; m <<= 1) v = fmaxf(v, __shfl_xor(v, m));
-  return v;
-}
 
 // ---------------------------------------------------------------- host side
 void set_error(const char* fmt, ...);
