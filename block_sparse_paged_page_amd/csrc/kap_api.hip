@@ -137,7 +137,7 @@ kap_status kap_score_pool_blocks(const void* q, int32_t q_dtype, const int32_t* 
     return fail(KAP_ERR_UNSUPPORTED, "dtype q=%d summary=%d", q_dtype, sum_dtype);
   if (!(rope_theta > 1.0f)) return fail(KAP_ERR_INVALID_ARG, "rope_theta %g <= 1", rope_theta);
   if (B == 0 || max_pages == 0) return KAP_OK;
-  if (!q || !positions || !summary || !block_table || !seq_lens || !pooled)
+  if (!q || !positions || !summary || !block_table || !seq_lens || (!pooled && !scores))
     return fail(KAP_ERR_INVALID_ARG, "null pointer");
   return launch_score_pool(q, (kap_dtype)q_dtype, positions, rope_theta, summary,
                            (kap_dtype)sum_dtype, block_table, max_pages, seq_lens, B, Hq, Hkv,

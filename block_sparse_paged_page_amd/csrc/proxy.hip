@@ -3,17 +3,17 @@
 // obtain the routing query).  q_out = hidden @ W_q, bf16 inputs, fp32 sums.
 //
 // HBM-bound GEMV (B <= 16 rows share each W_q byte).  A block (4 waves) owns a
-// tile of 512 output columns x kProxyRows rows of W_q; every wave-wide load
-// reads 1 KiB of one W_q row contiguously (lane l: columns 8l .. 8l+7), so DRAM
-// sees long contiguous runs.  Each lane accumulates B x 8 columns over its
-// rows; the four waves are added in wave order through LDS and each row split
+// tile of 256 output columns x kProxyRows rows of W_q; every wave-wide load
+// reads 512 B of one W_q row contiguously (lane l: columns 4l .. 4l+3), and a
+// wave keeps all 32 of its rows in flight.  Each lane accumulates B x 4
+// columns over its rows; the four waves are added in wave order through LDS and each row split
 // writes its partial sums; a second kernel adds the splits in split order
 // (deterministic).
 #include "kap_internal.h"
 
 namespace kap {
 
-constexpr int kProxyCols = 512;  // columns per block: 64 lanes x 8
+constexpr int kProxyCols = 256;  // columns per block: 64 lanes x 4
 constexpr int kProxyRows = 128;  // W_q rows per block (32 per wave)
 
 template <int BM>
@@ -24,44 +24,63 @@ __global__ __launch_bounds__(256) void proxy_partial_kernel(const uint16_t* hidd
   const int split = blockIdx.y;
   const int c0 = split * kProxyRows;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  constexpr int RPW = kProxyRows / 4;  // rows per wave
+  // rows in flight at once: all of the wave's rows, or 16 when the batch is 16
+  constexpr int INFL = BM >= 16 ? 16 : RPW;
+  const uint16_t* wbase = wq + (int64_t)(c0 + wave * RPW) * n_out + n0 + lane * 4;
+  // The first W_q rows go out before anything else: the hidden-state slice is
+  // staged in LDS while they are in flight (straight-line loads, and a barrier
+  // that orders LDS only).
+  uint2 wrow[INFL];
+#pragma unroll
+  for (int r = 0; r < INFL; ++r) wrow[r] = *(const uint2*)(wbase + (int64_t)r * n_out);
   __shared__ float sh[BM][kProxyRows];
-  for (int e = tid; e < BM * kProxyRows; e += 256) {
-    const int b = e / kProxyRows, c = e % kProxyRows;
-    sh[b][c] = (b < B) ? bf16_to_f32(hidden[(int64_t)b * dm + c0 + c]) : 0.f;
+  {
+    constexpr int PER = BM * kProxyRows / 256;  // hidden values per thread (BM >= 2), else 1
+    float hv[PER > 0 ? PER : 1];
+#pragma unroll
+    for (int k = 0; k < (PER > 0 ? PER : 1); ++k) {
+      const int e = k * 256 + tid;
+      const int b = e / kProxyRows, c = e % kProxyRows;
+      hv[k] = bf16_to_f32(hidden[(int64_t)min(b, B - 1) * dm + c0 + c]);
+    }
+#pragma unroll
+    for (int k = 0; k < (PER > 0 ? PER : 1); ++k) {
+      const int e = k * 256 + tid;
+      const int b = e / kProxyRows, c = e % kProxyRows;
+      if (e < BM * kProxyRows) sh[b][c] = b < B ? hv[k] : 0.f;
+    }
   }
-  __syncthreads();
-  float acc[BM][8];
+  lds_barrier();
+  float acc[BM][4];
 #pragma unroll
   for (int b = 0; b < BM; ++b)
 #pragma unroll
-    for (int e = 0; e < 8; ++e) acc[b][e] = 0.f;
-  constexpr int RPW = kProxyRows / 4;  // rows per wave
-  const uint16_t* wbase = wq + (int64_t)(c0 + wave * RPW) * n_out + n0 + lane * 8;
-  // rows in flight at once: all of the wave's rows, or 8 when the batch is 16
-  constexpr int INFL = BM >= 16 ? 8 : RPW;
+    for (int e = 0; e < 4; ++e) acc[b][e] = 0.f;
 #pragma unroll
   for (int r0 = 0; r0 < RPW; r0 += INFL) {
-  uint4 wrow[INFL];
+    if (r0 > 0) {
 #pragma unroll
-  for (int r = 0; r < INFL; ++r) wrow[r] = *(const uint4*)(wbase + (int64_t)(r0 + r) * n_out);
-#pragma unroll
-  for (int rr = 0; rr < INFL; ++rr) {
-    const int r = r0 + rr;
-    const uint4 w = wrow[rr];
-    const uint32_t ww[4] = {w.x, w.y, w.z, w.w};
-    float wf[8];
-#pragma unroll
-    for (int e = 0; e < 4; ++e) {
-      wf[2 * e] = __uint_as_float(ww[e] << 16);
-      wf[2 * e + 1] = __uint_as_float(ww[e] & 0xffff0000u);
+      for (int r = 0; r < INFL; ++r)
+        wrow[r] = *(const uint2*)(wbase + (int64_t)(r0 + r) * n_out);
     }
 #pragma unroll
-    for (int b = 0; b < BM; ++b) {
-      const float h = sh[b][wave * RPW + r];
+    for (int rr = 0; rr < INFL; ++rr) {
+      const int r = r0 + rr;
+      const uint32_t ww[2] = {wrow[rr].x, wrow[rr].y};
+      float wf[4];
 #pragma unroll
-      for (int e = 0; e < 8; ++e) acc[b][e] += h * wf[e];
+      for (int e = 0; e < 2; ++e) {
+        wf[2 * e] = __uint_as_float(ww[e] << 16);
+        wf[2 * e + 1] = __uint_as_float(ww[e] & 0xffff0000u);
+      }
+#pragma unroll
+      for (int b = 0; b < BM; ++b) {
+        const float h = sh[b][wave * RPW + r];
+#pragma unroll
+        for (int e = 0; e < 4; ++e) acc[b][e] += h * wf[e];
+      }
     }
-  }
   }
   // waves 1..3 hand their sums to wave 0 through LDS, added in wave order,
   // eight batch rows at a time
@@ -73,34 +92,46 @@ __global__ __launch_bounds__(256) void proxy_partial_kernel(const uint16_t* hidd
 #pragma unroll
       for (int bb = 0; bb < BC; ++bb)
 #pragma unroll
-        for (int e = 0; e < 8; ++e) red[wave - 1][bb][lane * 8 + e] = acc[b0 + bb][e];
+        for (int e = 0; e < 4; ++e) red[wave - 1][bb][lane * 4 + e] = acc[b0 + bb][e];
     }
-    __syncthreads();
+    lds_barrier();
     if (wave == 0) {
 #pragma unroll
       for (int bb = 0; bb < BC; ++bb) {
         const int b = b0 + bb;
         if (b < B) {
-          float* dst = partial + ((int64_t)split * B + b) * n_out + n0 + lane * 8;
+          float* dst = partial + ((int64_t)split * B + b) * n_out + n0 + lane * 4;
+          floatx4 o;
 #pragma unroll
-          for (int e = 0; e < 8; ++e) {
-            const int col = lane * 8 + e;
-            dst[e] = ((acc[b][e] + red[0][bb][col]) + red[1][bb][col]) + red[2][bb][col];
+          for (int e = 0; e < 4; ++e) {
+            const int col = lane * 4 + e;
+            o[e] = ((acc[b][e] + red[0][bb][col]) + red[1][bb][col]) + red[2][bb][col];
           }
+          *(floatx4*)dst = o;
         }
       }
     }
-    __syncthreads();
+    lds_barrier();
   }
 }
 
+// Adds the row splits in split order.  Each thread's splits are loaded 32 at a
+// time with straight-line loads (indices clamped, extra copies masked), so a
+// d_model of 4096 costs one memory round trip instead of one per few splits.
 __global__ __launch_bounds__(256) void proxy_reduce_kernel(const float* partial, int splits,
                                                            int total, float* out) {
   const int i = blockIdx.x * 256 + threadIdx.x;
   if (i >= total) return;
+  constexpr int SB = 32;
   float s = 0.f;
-#pragma unroll 8
-  for (int k = 0; k < splits; ++k) s += partial[(int64_t)k * total + i];
+  for (int k0 = 0; k0 < splits; k0 += SB) {
+    float v[SB];
+#pragma unroll
+    for (int k = 0; k < SB; ++k) v[k] = partial[(int64_t)min(k0 + k, splits - 1) * total + i];
+#pragma unroll
+    for (int k = 0; k < SB; ++k)
+      if (k0 + k < splits) s += v[k];
+  }
   out[i] = s;
 }
 

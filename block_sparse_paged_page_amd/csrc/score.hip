@@ -263,6 +263,12 @@ kap_status launch_score(const void* q, kap_dtype q_dt, const int32_t* pos, float
                         const void* summ, kap_dtype s_dt, const int32_t* bt, int32_t max_pages,
                         const int32_t* seq_lens, int32_t B, int32_t Hq, int32_t Hkv, int32_t D,
                         float* scores, hipStream_t stream) {
+  // Up to 16 KV heads the all-heads kernel computes the same per-head scores
+  // (same loads and arithmetic per head) and reads each page's head rows
+  // together, which measured faster; this kernel serves the other shapes.
+  if (Hkv <= kPoolMaxHeads && (size_t)Hq * D * (q_dt == KAP_BF16 ? 2 : 4) <= kPoolMaxQueryLds)
+    return launch_score_pool(q, q_dt, pos, theta, summ, s_dt, bt, max_pages, seq_lens, B, Hq, Hkv,
+                             D, scores, nullptr, stream);
   ScoreArgs a{q, pos, log2((double)theta), summ, bt, max_pages, seq_lens, Hq, Hkv, Hq / Hkv,
               scores, nullptr};
   dim3 grid((max_pages + kScorePagesPerBlock - 1) / kScorePagesPerBlock, Hkv, B);

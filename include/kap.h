@@ -104,8 +104,8 @@ KAP_API kap_status kap_score_blocks(const void* q, int32_t q_dtype, const int32_
 /*
  * Page scores of every KV head plus the head-pooled key in one launch, for
  * pooled selection ([KRI] the connector mean-pools scores across heads before
- * the per-request top-K).  scores (optional: NULL skips them) as in
- * kap_score_blocks, bit for bit the same arithmetic per head, and
+ * the per-request top-K).  scores as in kap_score_blocks, bit for bit the
+ * same arithmetic per head, and
  *   pooled[b][p] = (((S0 + S1) + S2) + ... + S_{Hkv-1}) / Hkv   for p < N_b
  *                = -inf                                         for the other p < max_pages
  * in fp32 with round-to-nearest adds in head order and one rounded division:
@@ -113,6 +113,7 @@ KAP_API kap_status kap_score_blocks(const void* q, int32_t q_dtype, const int32_
  * on (pooled, Hkv = 1) makes the same selection as on (scores, Hkv) pooled,
  * while it reads one key row per request instead of Hkv.
  *   pooled device out [B][max_pages] float
+ * Either output may be NULL (not both): it is then not written.
  * Hkv <= 16 and Hq * D * (q element bytes) <= 64 KiB (else KAP_ERR_UNSUPPORTED);
  * otherwise as kap_score_blocks.
  */

@@ -95,7 +95,7 @@ def test_score_pool_validation(lib):
     assert _score_pool(lib, Hq=32, Hkv=32) == UNSUPPORTED          # more than 16 KV heads
     assert b"Hkv" in lib.kap_last_error()
     assert _score_pool(lib, Hq=256, Hkv=16, q_dtype=0) == UNSUPPORTED  # 128 KiB of fp32 queries
-    assert _score_pool(lib, pooled=None) == INVALID                # pooled key is required
+    assert _score_pool(lib, pooled=None) == INVALID                # neither output given
     assert _score_pool(lib, q=None) == INVALID
     assert _score_pool(lib, theta=0.5) == INVALID
     assert _score_pool(lib, B=0) == OK
