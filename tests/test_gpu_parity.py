@@ -259,6 +259,7 @@ def test_verify_row_tiles(name, q_len, D):
     (128, 8, 128, "bf16"),   # GQA 16:1 (decode 16 rows, verify 64 rows per KV head)
     (32, 8, 64, "f32"),      # fp32 path, head_dim 64, verify 64 rows (two 32-row slices)
     (32, 16, 128, "bf16"),   # 16 KV heads: the widest pooled-scoring block
+    (32, 32, 64, "bf16"),    # 32 KV heads: per-head scores from the one-head-per-block kernel
 ])
 def test_head_layouts(Hq, Hkv, D, dtype):
     """Score (per head and pooled), top-K, selected decode and a 16-token verify on
@@ -271,7 +272,12 @@ def test_head_layouts(Hq, Hkv, D, dtype):
     s = kap.score_blocks(c.q, c.pos, c.S, c.bt, c.L, w.Hkv)
     torch.cuda.synchronize()
     check_scores(c, s.cpu().numpy())
-    _check_pooled(c)
+    if w.Hkv <= 16:
+        _check_pooled(c)
+    else:
+        with pytest.raises(kap.KapError) as ei:
+            kap.score_pool_blocks(c.q, c.pos, c.S, c.bt, c.L, w.Hkv)
+        assert ei.value.status == 2
     cap = c.budget()
     s_ref = oracle.score(c.b["q"], c.b["positions"], c.summ_l, c.btl, c.b["seq_lens"], w.Hkv)
     sel_ref, cnt_ref = oracle.select(s_ref.astype(np.float32), c.b["seq_lens"], c.b["anchor"],
@@ -366,19 +372,28 @@ def test_adversarial_selection_keys():
 
 def test_select_compact_matches_the_two_calls():
     """kap_select_compact writes exactly what kap_select_topk then kap_compact_view
-    write (both pinned to the oracle above), on adversarial keys, ragged and
-    empty rows, unallocated table entries, a window past the table, and rows
-    the device budget truncates to the capacity."""
-    rng = np.random.default_rng(22)
+    write, and what the oracle's selection then compaction give, on adversarial
+    keys, ragged and empty rows, unallocated table entries, a window past the
+    table, and rows the device budget truncates to the capacity."""
+    _select_compact_case(22, 3000)
+
+
+def test_select_compact_on_a_long_table():
+    """Past 11264 pages the keys are not staged in LDS: the other load path."""
+    _select_compact_case(23, 12500)
+
+
+def _select_compact_case(seed, P):
+    rng = np.random.default_rng(seed)
     palette = np.array([0.0, -0.0, 1.0, -1.0, 2.5, np.inf, -np.inf, np.nan, 1.0, 0.5], np.float32)
-    B, H, P = 6, 4, 3000
+    B, H = 6, 4
     S = palette[rng.integers(0, len(palette), size=(B, H, P))]
-    L = np.array([16 * 3000, 16 * 2999 + 1, 100, 16 * 5, 1, 0], np.int32)
+    L = np.array([16 * P, 16 * (P - 1) + 1, 100, 16 * 5, 1, 0], np.int32)
     a = np.array([1, 4, 0, 2, 0, 1], np.int32)
     r = np.array([2, 4, 3, 3, 0, 0], np.int32)
     k = np.array([110, 1000, 2, 0, 5, 3], np.int32)
     bt = np.stack([rng.permutation(B * P)[:P] for _ in range(B)]).astype(np.int32)
-    bt[1, 2999] = -1                                   # an unallocated last page
+    bt[1, P - 1] = -1                                  # an unallocated last page
     pos = L.copy()                                     # request 0's window lies past its table
     q_new = 5
     for per_head in (False, True):
@@ -392,6 +407,12 @@ def test_select_compact_matches_the_two_calls():
             np.testing.assert_array_equal(cv2[1].cpu().numpy(), sel.cpu().numpy())
             for x, y in zip(cv2, cv):
                 np.testing.assert_array_equal(x.cpu().numpy(), y.cpu().numpy())
+            # and the oracle's selection then compaction, on the same host arrays
+            sref, cref = oracle.select(S, L, a, r, k, cap, per_head=per_head)
+            ref = oracle.compact(sref, cref, bt, L, pos, q_new)
+            np.testing.assert_array_equal(cnt2.cpu().numpy(), cref)
+            for x, y in zip(cv2, ref):
+                np.testing.assert_array_equal(x.cpu().numpy(), y)
             if cap == 600:
                 assert int(cnt.cpu().numpy()[1].max()) == 600
 
