@@ -121,6 +121,31 @@ def _routing(big):
     r = oracle.compact(sel_ref, cnt_ref, b["bt"], b["seq_lens"], b["positions"], 1)
     for got, want in zip(cv, r):
         np.testing.assert_array_equal(got.cpu().numpy(), want)
+    # the one-launch top-K + compact view on the same scores
+    cnt2, cv2 = kap.select_compact(torch.from_numpy(s32).cuda(), big.L, big.anchor, big.recent,
+                                   big.k_mid, cap, cap, big.bt, big.pos, 1, per_head=w.per_head)
+    torch.cuda.synchronize()
+    np.testing.assert_array_equal(cnt2.cpu().numpy(), cnt_ref)
+    for got, want in zip(cv2, r):
+        np.testing.assert_array_equal(got.cpu().numpy(), want)
+    if not w.per_head:
+        # the bench's route: pooled key folded in the scoring launch, top-K on it
+        s2, pooled = kap.score_pool_blocks(big.q, big.pos, S_o, big.bt, big.L, w.Hkv)
+        cnt3, cv3 = kap.select_compact(pooled.view(w.B, 1, -1), big.L, big.anchor, big.recent,
+                                       big.k_mid, cap, cap, big.bt, big.pos, 1)
+        torch.cuda.synchronize()
+        s2h = s2.cpu().numpy()
+        np.testing.assert_array_equal(s2h.view(np.uint32), s_gpu.view(np.uint32))
+        fold = s2h[:, 0].copy()
+        for g in range(1, w.Hkv):
+            fold = fold + s2h[:, g]
+        fold = fold / np.float32(w.Hkv)
+        np.testing.assert_array_equal(pooled.cpu().numpy().view(np.uint32), fold.view(np.uint32))
+        sel4, cnt4 = oracle.select(s2h, b["seq_lens"], b["anchor"], b["recent"], big.k_mid_h, cap)
+        r4 = oracle.compact(sel4, cnt4, b["bt"], b["seq_lens"], b["positions"], 1)
+        np.testing.assert_array_equal(cnt3.cpu().numpy(), cnt4)
+        for got, want in zip(cv3, r4):
+            np.testing.assert_array_equal(got.cpu().numpy(), want)
     return sel_ref, cnt_ref, cv
 
 
