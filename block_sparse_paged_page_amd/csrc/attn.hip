@@ -65,17 +65,17 @@ struct PlanIn {
   int32_t target;  // items aimed at: the kernel's resident-wave capacity (<= kTargetItems)
 };
 
-__device__ __forceinline__ int plan_row_pages(const PlanIn& p, int r) {
+// Visible tokens of row r, clamped to the table width.
+__device__ __forceinline__ int plan_row_len(const PlanIn& p, int r) {
   const int b = r / p.Hkv, g = r % p.Hkv;
   const int gr = p.G == 1 ? 0 : g;
-  const int len = min(max(p.lens[b * p.G + gr], 0), p.width * kPage);
-  return (len + kPage - 1) / kPage;
+  return min(max(p.lens[b * p.G + gr], 0), p.width * kPage);
 }
 
-constexpr int kPlanCachedTiles = 8;  // rows <= 512 keep their page counts in registers
+constexpr int kPlanCachedTiles = 8;  // rows <= 512 keep their lengths in registers
 
 struct PlanItem {
-  int b, g, p0, p1;
+  int b, g, p0, p1, len;
   bool valid;
 };
 
@@ -84,32 +84,37 @@ struct PlanItem {
 __device__ PlanItem plan_find(const PlanIn& p, int item, int32_t* row_off, int32_t* n_items) {
   const int lane = threadIdx.x & 63;
   const int rows = p.B * p.Hkv;
-  int npc[kPlanCachedTiles];
+  // every cached length in one round trip: straight-line loads at clamped
+  // rows (a load under a branch would be waited for on the spot)
+  int lenc[kPlanCachedTiles];
+#pragma unroll
+  for (int t = 0; t < kPlanCachedTiles; ++t) lenc[t] = plan_row_len(p, min(t * 64 + lane, rows - 1));
   long long local = 0;
 #pragma unroll
   for (int t = 0; t < kPlanCachedTiles; ++t) {
-    const int r = t * 64 + lane;
-    npc[t] = (r < rows) ? plan_row_pages(p, r) : 0;
-    local += npc[t];
+    if (t * 64 + lane >= rows) lenc[t] = 0;
+    local += (lenc[t] + kPage - 1) / kPage;
   }
-  for (int r = kPlanCachedTiles * 64 + lane; r < rows; r += 64) local += plan_row_pages(p, r);
+  for (int r = kPlanCachedTiles * 64 + lane; r < rows; r += 64)
+    local += (plan_row_len(p, r) + kPage - 1) / kPage;
   for (int o = 32; o > 0; o >>= 1) local += __shfl_xor(local, o);
   // every row may end in a partial item, so aim at target - rows full items
   // (at least target / 2) to keep the whole plan within one resident round
   const int aim = max(p.target - rows, max(p.target / 2, 1));
   const int chunk = max((int)((local + aim - 1) / aim), kMinChunk);
-  PlanItem it{0, 0, 0, 0, false};
+  PlanItem it{0, 0, 0, 0, 0, false};
   int carry = 0;
   for (int base = 0, t = 0; base < rows; base += 64, ++t) {
     const int r = base + lane;
-    int np = 0;
+    int ln = 0;
     if (t < kPlanCachedTiles) {
 #pragma unroll
       for (int u = 0; u < kPlanCachedTiles; ++u)
-        if (u == t) np = npc[u];
+        if (u == t) ln = lenc[u];
     } else if (r < rows) {
-      np = plan_row_pages(p, r);
+      ln = plan_row_len(p, r);
     }
+    const int np = (ln + kPage - 1) / kPage;
     const int n = (np + chunk - 1) / chunk;
     int incl = n;
 #pragma unroll
@@ -128,6 +133,7 @@ __device__ PlanItem plan_find(const PlanIn& p, int item, int32_t* row_off, int32
       it.g = rr % p.Hkv;
       it.p0 = j * chunk;
       it.p1 = min(__shfl(np, src), it.p0 + chunk);
+      it.len = __shfl(ln, src);
       it.valid = true;
     }
     carry += __shfl(incl, 63);
@@ -204,7 +210,7 @@ __global__ __launch_bounds__(64) void attn_partial_bf16(PartArgs a) {
   const int l16 = lane & 15, q4 = lane >> 4;
   const int row0 = blockIdx.y * 16 * NT;
   const int gr = a.G == 1 ? 0 : g;
-  const int len = a.lens[b * a.G + gr];
+  const int len = __builtin_amdgcn_readfirstlane(it.len);
   const int pos_b = a.pos[b];  // read once, before any page load is in flight
   const int32_t* trow = a.table + (int64_t)(b * a.G + gr) * a.width;
   // Pipelined mode reads the (read-only) table through the constant address
@@ -235,33 +241,26 @@ __global__ __launch_bounds__(64) void attn_partial_bf16(PartArgs a) {
       const int e = k * 64 + lane;
       const int rr = e / CPR, c = e % CPR;
       const int r = row0 + rr;
-      if constexpr (PIPE) {
-        // straight-line: rows past R load row R - 1 and are masked to zero
-        const int rc = min(r, a.R - 1);
-        const int i = rc / a.grp, h = g * a.grp + rc % a.grp;
-        const uint4 x = *(const uint4*)(q + (((int64_t)b * a.q_len + i) * a.Hq + h) * D + 8 * c);
-        const uint32_t keep = (r < a.R) ? 0xffffffffu : 0u;
-        qraw[k] = make_uint4(x.x & keep, x.y & keep, x.z & keep, x.w & keep);
-      } else {
-        qraw[k] = make_uint4(0, 0, 0, 0);
-        if (r < a.R) {
-          const int i = r / a.grp, h = g * a.grp + r % a.grp;
-          qraw[k] = *(const uint4*)(q + (((int64_t)b * a.q_len + i) * a.Hq + h) * D + 8 * c);
-        }
-      }
+      // straight-line (a load under a branch would be waited for on the
+      // spot): rows past R load row R - 1 and are masked to zero
+      const int rc = min(r, a.R - 1);
+      const int i = rc / a.grp, h = g * a.grp + rc % a.grp;
+      const uint4 x = *(const uint4*)(q + (((int64_t)b * a.q_len + i) * a.Hq + h) * D + 8 * c);
+      const uint32_t keep = (r < a.R) ? 0xffffffffu : 0u;
+      qraw[k] = make_uint4(x.x & keep, x.y & keep, x.z & keep, x.w & keep);
     }
   }
 
   // page-table window: lane j holds trow[wbase + j]
   int wbase = p0;
-  int tr = (p0 + lane < p1) ? trow[p0 + lane] : 0;
+  int tr = trow[min(p0 + lane, p1 - 1)];  // entries past the item are never used
   auto phys_of = [&](int p) -> int64_t {
     if constexpr (PIPE) {
       return (int64_t)trow_s[p];
     } else {
       if (p - wbase >= 64) {  // wave-uniform refill
         wbase += 64;
-        tr = (wbase + lane < p1) ? trow[wbase + lane] : 0;
+        tr = trow[min(wbase + lane, p1 - 1)];
       }
       return (int64_t)__builtin_amdgcn_readlane(tr, p - wbase);
     }
@@ -512,7 +511,7 @@ __global__ __launch_bounds__(64) void attn_partial_f32(PartArgs a) {
   const int row0 = blockIdx.y * RS;
   const int nr = min(RS, a.R - row0);
   const int gr = a.G == 1 ? 0 : g;
-  const int len = a.lens[b * a.G + gr];
+  const int len = it.len;
   const int32_t* trow = a.table + (int64_t)(b * a.G + gr) * a.width;
   const float* qin = (const float*)a.q;
   const float* kpool = (const float*)a.k;
