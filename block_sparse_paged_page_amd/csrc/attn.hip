@@ -53,9 +53,9 @@ AttnWorkspace carve_attn_workspace(void* base, int32_t B, int32_t q_len, int32_t
 
 // ------------------------------------------------------------------ work plan
 // Rows are (request b, KV head g); row r reads table row (b, g or 0).  A row
-// of np pages is cut into ceil(np / chunk) items of chunk pages, with
-// chunk = max(kMinChunk, ceil(total pages / max(target - rows, target / 2)));
-// items are numbered row by row.  target is the number of waves the partial kernel keeps resident on the
+// of np pages is cut into ceil(np / chunk) items of chunk pages, with chunk
+// the smallest (at least kMinChunk) for which the items number at most
+// target (see plan_find); items are numbered row by row.  target is the number of waves the partial kernel keeps resident on the
 // device (CUs x resident blocks per CU), so a call runs as one round of equal
 // items.  Every wave evaluates this closed form for its own item id, so no
 // separate planning launch is needed.  At most target + rows items.
@@ -98,10 +98,27 @@ __device__ PlanItem plan_find(const PlanIn& p, int item, int32_t* row_off, int32
   for (int r = kPlanCachedTiles * 64 + lane; r < rows; r += 64)
     local += (plan_row_len(p, r) + kPage - 1) / kPage;
   for (int o = 32; o > 0; o >>= 1) local += __shfl_xor(local, o);
-  // every row may end in a partial item, so aim at target - rows full items
-  // (at least target / 2) to keep the whole plan within one resident round
+  // The chunk is the smallest with sum over rows of ceil(pages / chunk) <=
+  // target, so that the plan fills one resident round without leaving a
+  // wave's worth of slots empty.  Every row may end in a partial item, so
+  // total / (target - rows) always satisfies it (at least target / 2 as the
+  // divisor); up to 512 rows the exact value is then found by bisection
+  // between that bound and total / target (a few steps: the two are close).
   const int aim = max(p.target - rows, max(p.target / 2, 1));
-  const int chunk = max((int)((local + aim - 1) / aim), kMinChunk);
+  int chunk = max((int)((local + aim - 1) / aim), kMinChunk);
+  if (rows <= kPlanCachedTiles * 64) {
+    int lo = max((int)((local + p.target - 1) / p.target), kMinChunk);
+    while (lo < chunk) {  // wave-uniform
+      const int mid = (lo + chunk) >> 1;
+      int cnt = 0;
+#pragma unroll
+      for (int t = 0; t < kPlanCachedTiles; ++t)
+        if (t * 64 < rows) cnt += ((lenc[t] + kPage - 1) / kPage + mid - 1) / mid;
+      for (int o = 32; o > 0; o >>= 1) cnt += __shfl_xor(cnt, o);
+      if (cnt <= p.target) chunk = mid;
+      else lo = mid + 1;
+    }
+  }
   PlanItem it{0, 0, 0, 0, 0, false};
   int carry = 0;
   for (int base = 0, t = 0; base < rows; base += 64, ++t) {
