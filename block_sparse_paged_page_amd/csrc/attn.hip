@@ -54,8 +54,8 @@ AttnWorkspace carve_attn_workspace(void* base, int32_t B, int32_t q_len, int32_t
 // ------------------------------------------------------------------ work plan
 // Rows are (request b, KV head g); row r reads table row (b, g or 0).  A row
 // of np pages is cut into ceil(np / chunk) items of chunk pages, with chunk
-// the smallest (at least kMinChunk) for which the items number at most
-// target (see plan_find); items are numbered row by row.  target is the number of waves the partial kernel keeps resident on the
+// chosen so that the items number at most target (see plan_find); items are
+// numbered row by row.  target is the number of waves the partial kernel keeps resident on the
 // device (CUs x resident blocks per CU), so a call runs as one round of equal
 // items.  Every wave evaluates this closed form for its own item id, so no
 // separate planning launch is needed.  At most target + rows items.
@@ -89,35 +89,37 @@ __device__ PlanItem plan_find(const PlanIn& p, int item, int32_t* row_off, int32
   int lenc[kPlanCachedTiles];
 #pragma unroll
   for (int t = 0; t < kPlanCachedTiles; ++t) lenc[t] = plan_row_len(p, min(t * 64 + lane, rows - 1));
-  long long local = 0;
+  // total pages (< 2^28: rows <= 4096, width <= 65536) and the longest row
+  int local = 0, longest = 0;
 #pragma unroll
   for (int t = 0; t < kPlanCachedTiles; ++t) {
     if (t * 64 + lane >= rows) lenc[t] = 0;
-    local += (lenc[t] + kPage - 1) / kPage;
+    const int np = (lenc[t] + kPage - 1) / kPage;
+    local += np;
+    longest = max(longest, np);
   }
-  for (int r = kPlanCachedTiles * 64 + lane; r < rows; r += 64)
-    local += (plan_row_len(p, r) + kPage - 1) / kPage;
-  for (int o = 32; o > 0; o >>= 1) local += __shfl_xor(local, o);
+  for (int r = kPlanCachedTiles * 64 + lane; r < rows; r += 64) {
+    const int np = (plan_row_len(p, r) + kPage - 1) / kPage;
+    local += np;
+    longest = max(longest, np);
+  }
+  for (int o = 32; o > 0; o >>= 1) {
+    local += __shfl_xor(local, o);
+    longest = max(longest, __shfl_xor(longest, o));
+  }
   // The chunk is the smallest with sum over rows of ceil(pages / chunk) <=
   // target, so that the plan fills one resident round without leaving a
-  // wave's worth of slots empty.  Every row may end in a partial item, so
-  // total / (target - rows) always satisfies it (at least target / 2 as the
-  // divisor); up to 512 rows the exact value is then found by bisection
-  // between that bound and total / target (a few steps: the two are close).
-  const int aim = max(p.target - rows, max(p.target / 2, 1));
-  int chunk = max((int)((local + aim - 1) / aim), kMinChunk);
-  if (rows <= kPlanCachedTiles * 64) {
-    int lo = max((int)((local + p.target - 1) / p.target), kMinChunk);
-    while (lo < chunk) {  // wave-uniform
-      const int mid = (lo + chunk) >> 1;
-      int cnt = 0;
-#pragma unroll
-      for (int t = 0; t < kPlanCachedTiles; ++t)
-        if (t * 64 < rows) cnt += ((lenc[t] + kPage - 1) / kPage + mid - 1) / mid;
-      for (int o = 32; o > 0; o >>= 1) cnt += __shfl_xor(cnt, o);
-      if (cnt <= p.target) chunk = mid;
-      else lo = mid + 1;
-    }
+  // wave's worth of slots empty.  When every row has the same length n (a
+  // full table, or a pooled selection) that is ceil(n / floor(target / rows)).
+  // Otherwise every row may end in a partial item, and total / (target -
+  // rows) satisfies it (at least target / 2 as the divisor).
+  int chunk;
+  if (local == longest * rows && p.target >= rows && longest > 0) {
+    const int per_row = p.target / rows;
+    chunk = max((longest + per_row - 1) / per_row, kMinChunk);
+  } else {
+    const int aim = max(p.target - rows, max(p.target / 2, 1));
+    chunk = max((local + aim - 1) / aim, kMinChunk);
   }
   PlanItem it{0, 0, 0, 0, 0, false};
   int carry = 0;
@@ -307,10 +309,14 @@ __global__ __launch_bounds__(64) void attn_partial_bf16(PartArgs a) {
     load_page(p0, buf0);
     load_page(min(p0 + 1, p1 - 1), buf1);
   } else {
-    if (p0 < p1) load_page(p0, buf0);
-    if (p0 + 1 < p1) load_page(p0 + 1, buf1);
-    if (p0 + 2 < p1) load_page(p0 + 2, buf2);
-    if (p0 + 3 < p1) load_page(p0 + 3, buf3);
+    // the first four pages go out together (straight-line, past the item
+    // clamped to its last page: never consumed unmasked), so they arrive in
+    // one round trip and the query rotation below runs while they are in
+    // flight; the main loop then throttles to about one page per wave
+    load_page(p0, buf0);
+    load_page(min(p0 + 1, p1 - 1), buf1);
+    load_page(min(p0 + 2, p1 - 1), buf2);
+    load_page(min(p0 + 3, p1 - 1), buf3);
   }
 
   // This slice's query rows, rotated at their positions, as LDS fragments in
