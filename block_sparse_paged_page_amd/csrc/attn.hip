@@ -310,13 +310,22 @@ __global__ __launch_bounds__(64) void attn_partial_bf16(PartArgs a) {
     load_page(min(p0 + 1, p1 - 1), buf1);
   } else {
     // the first four pages go out together (straight-line, past the item
-    // clamped to its last page: never consumed unmasked), so they arrive in
+    // clamped to its last page: never consumed unmasked; their table entries
+    // read straight from the window, which holds them), so they arrive in
     // one round trip and the query rotation below runs while they are in
     // flight; the main loop then throttles to about one page per wave
-    load_page(p0, buf0);
-    load_page(min(p0 + 1, p1 - 1), buf1);
-    load_page(min(p0 + 2, p1 - 1), buf2);
-    load_page(min(p0 + 3, p1 - 1), buf3);
+    auto load_first = [&](int k, PageFrag<D>& f) {
+      const int p = min(p0 + k, p1 - 1);
+      const int64_t base = (int64_t)__builtin_amdgcn_readlane(tr, p - p0) * page_stride + head_off;
+#pragma unroll
+      for (int s = 0; s < KS; ++s) f.k[s] = *(const uint4*)(kpool + base + k_lane + 32 * s);
+#pragma unroll
+      for (int c = 0; c < NC; ++c) f.v[c] = *(const uint2*)(vpool + base + v_lane + 16 * kPage * c);
+    };
+    load_first(0, buf0);
+    load_first(1, buf1);
+    load_first(2, buf2);
+    load_first(3, buf3);
   }
 
   // This slice's query rows, rotated at their positions, as LDS fragments in
@@ -330,7 +339,7 @@ __global__ __launch_bounds__(64) void attn_partial_bf16(PartArgs a) {
       const int e = k * 64 + lane;
       *(uint4*)&sraw[e / CPR][8 * (e % CPR)] = qraw[k];
     }
-    __syncthreads();
+    lds_barrier();  // LDS only: the first pages stay in flight
     constexpr int HALF = D / 2, LPP = 64 / HALF;
     const int pr = lane % HALF, rsub = lane / HALF;
     uint16_t* sqh = (uint16_t*)&sq[0][0][0];
@@ -361,7 +370,7 @@ __global__ __launch_bounds__(64) void attn_partial_bf16(PartArgs a) {
       const int r = row0 + 16 * t + l16;
       qpos[t] = (r < a.R) ? pos_b + r / a.grp : -1;
     }
-    __syncthreads();
+    lds_barrier();
   }
 
   floatx4 o[NT][NC];
