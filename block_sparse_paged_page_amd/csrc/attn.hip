@@ -193,10 +193,12 @@ struct PartArgs {
 // NT row tiles of 16 query rows per wave (rows = GQA group x window, row r is
 // query r / grp of head g*grp + r % grp).
 //
-// Memory pipeline: four page buffers (two pairs) in a ring, so one pair's K/V
-// loads are in flight while the other pair is consumed; the item's page-table
-// entries are fetched 64 at a time into one lane register each and broadcast
-// with readlane.  The query fragments live in LDS (re-read per pair) to keep
+// Memory pipeline, two disciplines (PIPE selects): throttled, a four-page
+// register ring whose loads sit under branches, so that about one page per
+// wave is in flight (page-table entries fetched 64 at a time into one lane
+// register each and broadcast with readlane); pipelined, straight-line loads
+// of one pair at a time, requested as soon as the previous pair is consumed
+// (page-table entries through scalar loads).  The query fragments live in LDS (re-read per pair) to keep
 // the register footprint in budget: at D = 128, NT = 1 runs two waves per SIMD
 // and NT = 2..4 one, with no spills.  NT = 3 and 4 let a (b, g) row group of up to
 // 64 rows (e.g. a 5..8-token window under GQA 8:1) read each page once.
@@ -294,18 +296,16 @@ __global__ __launch_bounds__(64) void attn_partial_bf16(PartArgs a) {
     for (int c = 0; c < NC; ++c) f.v[c] = *(const uint2*)(vp + 16 * kPage * c);
   };
 
-  // four page buffers: two pairs, one pair's loads in flight while the other
-  // pair is consumed
+  // page buffers: the throttled ring uses four, the pipelined loop two
   PageFrag<D> buf0, buf1, buf2, buf3;
 #pragma unroll
   for (int s = 0; s < KS; ++s) buf0.k[s] = buf1.k[s] = buf2.k[s] = buf3.k[s] = make_uint4(0, 0, 0, 0);
 #pragma unroll
   for (int c = 0; c < NC; ++c) buf0.v[c] = buf1.v[c] = buf2.v[c] = buf3.v[c] = make_uint2(0, 0);
   if constexpr (PIPE) {
-    // one pair in flight while the other is consumed; every load is
-    // straight-line (pages past the item clamp to its last page, an L2 hit
-    // whose scores are masked), so the compiler waits for exactly the pair
-    // about to be consumed
+    // every load is straight-line (pages past the item clamp to its last
+    // page, an L2 hit whose scores are masked), so the compiler waits for
+    // exactly the pair about to be consumed
     load_page(p0, buf0);
     load_page(min(p0 + 1, p1 - 1), buf1);
   } else {
@@ -765,11 +765,10 @@ kap_status launch_attention(const AttnCall& c) {
           (const void*)attn_partial_bf16<128, 3, true>, (const void*)attn_partial_bf16<128, 4, true>}}};
     const int di = c.D == 128 ? 1 : 0;
     // Short work items (a selected view) are latency-bound, and the 48/64-row
-    // tiles have enough compute per page that it must overlap the next pair's
-    // loads: both run the pipelined variant (a pair of pages in flight).  Long
-    // items with 16/32-row tiles saturate HBM, where one page in flight per
-    // wave across many waves measured fastest: they run the throttled
-    // variant.  The host bounds the item length from the table width,
+    // tiles measured faster with a pair of pages requested at a time: both run
+    // the pipelined variant.  Long items with 16/32-row tiles saturate HBM,
+    // where about one page in flight per wave across many waves measured
+    // fastest: they run the throttled variant.  The host bounds the item length from the table width,
     // mirroring the device plan's chunk formula.
     const int rows = c.B * c.Hkv;
     const int t0 = max(1, min(kTargetItems, resident_blocks(fns[0][di][nt - 1], 64) / slices));
