@@ -765,10 +765,10 @@ def run_workspace(args, dev):
 def main():
     args = parse()
     if args.gpus != 1:
-        print(json.dumps({"error": "this build runs on one GPU only; --gpus must be 1",
+        print(json.dumps({"error": "the library runs on one GPU; --gpus must be 1",
                           "n_gpus": args.gpus}))
-        print("bench.py: multi-GPU runs are not part of this build (one GPU per box); "
-              "see DESIGN.md for how the path would shard.", file=sys.stderr)
+        print("bench.py: only single-GPU runs are implemented; the figures are one GPU's "
+              "share of the work, and the path has no collectives.", file=sys.stderr)
         sys.exit(2)
     q = args.quiet
     dev = torch.device("cuda:0")
