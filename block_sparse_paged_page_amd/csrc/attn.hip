@@ -198,9 +198,16 @@ struct PartArgs {
 // wave is in flight (page-table entries fetched 64 at a time into one lane
 // register each and broadcast with readlane); pipelined, straight-line loads
 // of one pair at a time, requested as soon as the previous pair is consumed
-// (page-table entries through scalar loads).  The query fragments live in LDS (re-read per pair) to keep
-// the register footprint in budget: at D = 128, NT = 1 runs two waves per SIMD
-// and NT = 2..4 one, with no spills.  NT = 3 and 4 let a (b, g) row group of up to
+// (page-table entries through scalar loads).
+// Load policy, measured at 128K: items that stream long page runs (the
+// throttled discipline, and the 48/64-row tiles) read V with the non-temporal
+// policy and K with the default one (each K fragment load covers half of a
+// 128-byte line whose other half the next load takes, and early eviction
+// between the two costs more than it saves); the short items of a selected
+// view read both with the default policy, which measured faster there.
+// The query fragments live in LDS (re-read per pair) to keep the register
+// footprint in budget: at D = 128, NT = 1 runs two waves per SIMD and
+// NT = 2..4 one, with no spills.  NT = 3 and 4 let a (b, g) row group of up to
 // 64 rows (e.g. a 5..8-token window under GQA 8:1) read each page once.
 // Online softmax with a lazy reference max: a row's reference only moves
 // when its running max exceeds it by more than 2^8 (log2 units), so the
@@ -208,8 +215,6 @@ struct PartArgs {
 // below 2^8, well inside bf16/fp32 range.  The final (m, l) pair uses the
 // reference, so the merged result is the same softmax.
 constexpr float kLazyRescale = 8.0f;
-
-typedef unsigned int u32x2v __attribute__((ext_vector_type(2)));
 
 template <int D>
 struct PageFrag {
@@ -245,6 +250,7 @@ __global__ __launch_bounds__(64) void attn_partial_bf16(PartArgs a) {
   const uint16_t* vpool = (const uint16_t*)a.v;
   const int64_t head_off = (int64_t)g * (kPage * D);
   const int64_t page_stride = (int64_t)a.Hkv * (kPage * D);
+  constexpr bool kStreamV = !PIPE || NT >= 3;  // long page runs: V by streaming loads
   const int k_lane = l16 * D + 8 * q4;
   const int v_lane = l16 * kPage + 4 * q4;
 
@@ -293,7 +299,8 @@ __global__ __launch_bounds__(64) void attn_partial_bf16(PartArgs a) {
 #pragma unroll
     for (int s = 0; s < KS; ++s) f.k[s] = *(const uint4*)(kp + 32 * s);
 #pragma unroll
-    for (int c = 0; c < NC; ++c) f.v[c] = *(const uint2*)(vp + 16 * kPage * c);
+    for (int c = 0; c < NC; ++c)
+      f.v[c] = kStreamV ? ld_stream8(vp + 16 * kPage * c) : *(const uint2*)(vp + 16 * kPage * c);
   };
 
   // page buffers: the throttled ring uses four, the pipelined loop two
@@ -320,7 +327,7 @@ __global__ __launch_bounds__(64) void attn_partial_bf16(PartArgs a) {
 #pragma unroll
       for (int s = 0; s < KS; ++s) f.k[s] = *(const uint4*)(kpool + base + k_lane + 32 * s);
 #pragma unroll
-      for (int c = 0; c < NC; ++c) f.v[c] = *(const uint2*)(vpool + base + v_lane + 16 * kPage * c);
+      for (int c = 0; c < NC; ++c) f.v[c] = ld_stream8(vpool + base + v_lane + 16 * kPage * c);
     };
     load_first(0, buf0);
     load_first(1, buf1);

@@ -68,6 +68,22 @@ __device__ __forceinline__ void rope_sincos(double pos, int pair, int D, double 
   sincos(r, s, c);
 }
 
+// Streaming loads with the non-temporal policy, which marks the lines for
+// early eviction instead of keeping them cached.  On MI355X it raises the
+// sustained read rate of a plain stream from about 6.3 to 7.2 TB/s, and of
+// random 8 KiB page tiles by about 10 %, when every load covers whole 128-byte
+// lines.  For data a call reads once; not for page tables or queries.
+typedef unsigned int u32x4v __attribute__((ext_vector_type(4)));
+typedef unsigned int u32x2v __attribute__((ext_vector_type(2)));
+__device__ __forceinline__ uint4 ld_stream16(const void* p) {
+  const u32x4v v = __builtin_nontemporal_load((const u32x4v*)p);
+  return make_uint4(v.x, v.y, v.z, v.w);
+}
+__device__ __forceinline__ uint2 ld_stream8(const void* p) {
+  const u32x2v v = __builtin_nontemporal_load((const u32x2v*)p);
+  return make_uint2(v.x, v.y);
+}
+
 // Workgroup barrier that orders LDS only: global loads in flight stay in
 // flight across it (__syncthreads also waits for every outstanding load).
 __device__ __forceinline__ void lds_barrier() {

@@ -86,14 +86,15 @@ __global__ __launch_bounds__(256) void materialize_kernel(MaterializeArgs a) {
   uint4* kd = a.kws + (dst * a.Hkv + g) * a.tile;
   uint4* vd = a.vws + (dst * a.Hkv + g) * a.tile;
   constexpr int U = 2;  // words per thread in flight (a bf16 D = 128 tile is 256 words)
+  // source tiles are read once: streaming loads
   for (int w0 = threadIdx.x; w0 < a.tile; w0 += 256 * U) {
     uint4 kw[U], vw[U];
 #pragma unroll
     for (int u = 0; u < U; ++u) {
       const int w = w0 + u * 256;
       if (w < a.tile) {
-        kw[u] = ks[w];
-        vw[u] = vs[w];
+        kw[u] = ld_stream16(ks + w);
+        vw[u] = ld_stream16(vs + w);
       }
     }
 #pragma unroll

@@ -30,10 +30,10 @@ __global__ __launch_bounds__(256) void proxy_partial_kernel(const uint16_t* hidd
   const uint16_t* wbase = wq + (int64_t)(c0 + wave * RPW) * n_out + n0 + lane * 4;
   // The first W_q rows go out before anything else: the hidden-state slice is
   // staged in LDS while they are in flight (straight-line loads, and a barrier
-  // that orders LDS only).
+  // that orders LDS only).  W_q is read once per call: streaming loads.
   uint2 wrow[INFL];
 #pragma unroll
-  for (int r = 0; r < INFL; ++r) wrow[r] = *(const uint2*)(wbase + (int64_t)r * n_out);
+  for (int r = 0; r < INFL; ++r) wrow[r] = ld_stream8(wbase + (int64_t)r * n_out);
   __shared__ float sh[BM][kProxyRows];
   {
     constexpr int PER = BM * kProxyRows / 256;  // hidden values per thread (BM >= 2), else 1
@@ -62,7 +62,7 @@ __global__ __launch_bounds__(256) void proxy_partial_kernel(const uint16_t* hidd
     if (r0 > 0) {
 #pragma unroll
       for (int r = 0; r < INFL; ++r)
-        wrow[r] = *(const uint2*)(wbase + (int64_t)(r0 + r) * n_out);
+        wrow[r] = ld_stream8(wbase + (int64_t)(r0 + r) * n_out);
     }
 #pragma unroll
     for (int rr = 0; rr < INFL; ++rr) {

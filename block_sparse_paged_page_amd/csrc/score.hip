@@ -75,13 +75,13 @@ __global__ __launch_bounds__(256) void score_kernel(ScoreArgs a) {
   int phys[U];
 #pragma unroll
   for (int u = 0; u < U; ++u) phys[u] = __shfl(tr, u * RPL + sub);
-  uint4 v[U];
+  uint4 v[U];  // summary rows are read once per call: streaming loads
 #pragma unroll
   for (int u = 0; u < U; ++u) {
     const int j = u * RPL + sub;
     v[u] = make_uint4(0, 0, 0, 0);
     if (w0 + j < N && w0 + j < w1)
-      v[u] = *(const uint4*)(summ + ((int64_t)phys[u] * a.Hkv + g) * D + part * EPL);
+      v[u] = ld_stream16(summ + ((int64_t)phys[u] * a.Hkv + g) * D + part * EPL);
   }
 #pragma unroll
   for (int k = 0; k < QPT; ++k) sq[k * 256 + tid] = qv[k];
@@ -194,7 +194,7 @@ __global__ __launch_bounds__(1024) void score_pool_kernel(ScoreArgs a) {
     for (int u = 0; u < U; ++u) {
       const int j = u * RPL + sub;
       v[u] = make_uint4(0, 0, 0, 0);
-      if (j < nv) v[u] = *(const uint4*)(summ + ((int64_t)phys[u] * a.Hkv + g) * D + part * EPL);
+      if (j < nv) v[u] = ld_stream16(summ + ((int64_t)phys[u] * a.Hkv + g) * D + part * EPL);
     }
     lds_barrier();
     // u_g = sum over the group of RoPE(q_h, pos); lane = rotation pair
