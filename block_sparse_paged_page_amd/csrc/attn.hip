@@ -193,18 +193,25 @@ struct PartArgs {
 // NT row tiles of 16 query rows per wave (rows = GQA group x window, row r is
 // query r / grp of head g*grp + r % grp).
 //
-// Memory pipeline, two disciplines (PIPE selects): throttled, a four-page
-// register ring whose loads sit under branches, so that about one page per
-// wave is in flight (page-table entries fetched 64 at a time into one lane
-// register each and broadcast with readlane); pipelined, straight-line loads
-// of one pair at a time, requested as soon as the previous pair is consumed
-// (page-table entries through scalar loads).
-// Load policy, measured at 128K: items that stream long page runs (the
-// throttled discipline, and the 48/64-row tiles) read V with the non-temporal
-// policy and K with the default one (each K fragment load covers half of a
-// 128-byte line whose other half the next load takes, and early eviction
-// between the two costs more than it saves); the short items of a selected
-// view read both with the default policy, which measured faster there.
+// Memory pipeline, three disciplines (MODE selects), measured at 128K:
+//  * throttled (long page runs, 16-row tiles): a four-page register ring whose
+//    loads sit under branches, so each wave waits for every load in flight
+//    before it computes and has about one page outstanding (page-table entries
+//    fetched 64 at a time into one lane register each, broadcast with
+//    readlane).  Two waves per SIMD hide each other's compute.
+//  * staggered (long page runs, 32-row tiles): straight-line loads one page
+//    ahead of the pair being consumed, so about one page stays in flight while
+//    the single wave per SIMD computes.
+//  * pairs (short items of a selected view, and 48/64-row tiles at any
+//    length): straight-line loads of one pair at a time, requested as soon as
+//    the previous pair is consumed.
+// The straight-line disciplines read page-table entries through scalar loads
+// and clamp pages past the item to its last page (an L2 hit whose scores are
+// masked), so the compiler waits for exactly the loads about to be consumed.
+// V is read with the non-temporal policy (each byte once per call) and K with
+// the default one: each K fragment load covers half of a 128-byte line whose
+// other half the next load takes, and early eviction between the two costs
+// more than it saves.
 // The query fragments live in LDS (re-read per pair) to keep the register
 // footprint in budget: at D = 128, NT = 1 runs two waves per SIMD and
 // NT = 2..4 one, with no spills.  NT = 3 and 4 let a (b, g) row group of up to
@@ -222,7 +229,9 @@ struct PageFrag {
   uint2 v[D / 16];
 };
 
-template <int D, int NT, bool PIPE>
+enum { kThrottled = 0, kPairs = 1, kStaggered = 2 };
+
+template <int D, int NT, int MODE>
 __global__ __launch_bounds__(64) void attn_partial_bf16(PartArgs a) {
   const PlanIn pin{a.lens, a.B, a.Hkv, a.G, a.width, a.target};
   const bool publish = blockIdx.x == 0 && blockIdx.y == 0;
@@ -239,7 +248,7 @@ __global__ __launch_bounds__(64) void attn_partial_bf16(PartArgs a) {
   const int len = __builtin_amdgcn_readfirstlane(it.len);
   const int pos_b = a.pos[b];  // read once, before any page load is in flight
   const int32_t* trow = a.table + (int64_t)(b * a.G + gr) * a.width;
-  // Pipelined mode reads the (read-only) table through the constant address
+  // The straight-line modes read the (read-only) table through the constant address
   // space: the wave-uniform entries then come through scalar memory and its
   // own counter, so waiting for an entry never waits for K/V loads in flight.
   const __attribute__((address_space(4))) int32_t* trow_s =
@@ -250,7 +259,7 @@ __global__ __launch_bounds__(64) void attn_partial_bf16(PartArgs a) {
   const uint16_t* vpool = (const uint16_t*)a.v;
   const int64_t head_off = (int64_t)g * (kPage * D);
   const int64_t page_stride = (int64_t)a.Hkv * (kPage * D);
-  constexpr bool kStreamV = !PIPE || NT >= 3;  // long page runs: V by streaming loads
+  constexpr bool STRAIGHT = MODE != kThrottled;  // straight-line loads, scalar table reads
   const int k_lane = l16 * D + 8 * q4;
   const int v_lane = l16 * kPage + 4 * q4;
 
@@ -282,7 +291,7 @@ __global__ __launch_bounds__(64) void attn_partial_bf16(PartArgs a) {
   int wbase = p0;
   int tr = trow[min(p0 + lane, p1 - 1)];  // entries past the item are never used
   auto phys_of = [&](int p) -> int64_t {
-    if constexpr (PIPE) {
+    if constexpr (STRAIGHT) {
       return (int64_t)trow_s[p];
     } else {
       if (p - wbase >= 64) {  // wave-uniform refill
@@ -300,19 +309,19 @@ __global__ __launch_bounds__(64) void attn_partial_bf16(PartArgs a) {
     for (int s = 0; s < KS; ++s) f.k[s] = *(const uint4*)(kp + 32 * s);
 #pragma unroll
     for (int c = 0; c < NC; ++c)
-      f.v[c] = kStreamV ? ld_stream8(vp + 16 * kPage * c) : *(const uint2*)(vp + 16 * kPage * c);
+      f.v[c] = ld_stream8(vp + 16 * kPage * c);
   };
 
-  // page buffers: the throttled ring uses four, the pipelined loop two
+  // page buffers: the throttled ring and the staggered loop use four, the
+  // pair loop two
   PageFrag<D> buf0, buf1, buf2, buf3;
 #pragma unroll
   for (int s = 0; s < KS; ++s) buf0.k[s] = buf1.k[s] = buf2.k[s] = buf3.k[s] = make_uint4(0, 0, 0, 0);
 #pragma unroll
   for (int c = 0; c < NC; ++c) buf0.v[c] = buf1.v[c] = buf2.v[c] = buf3.v[c] = make_uint2(0, 0);
-  if constexpr (PIPE) {
-    // every load is straight-line (pages past the item clamp to its last
-    // page, an L2 hit whose scores are masked), so the compiler waits for
-    // exactly the pair about to be consumed
+  if constexpr (STRAIGHT) {
+    // straight-line: the first pair (the staggered loop requests the next
+    // page itself before consuming it)
     load_page(p0, buf0);
     load_page(min(p0 + 1, p1 - 1), buf1);
   } else {
@@ -502,7 +511,19 @@ __global__ __launch_bounds__(64) void attn_partial_bf16(PartArgs a) {
     }
   };
 
-  if constexpr (PIPE) {
+  if constexpr (MODE == kStaggered) {
+    // one page ahead: while a pair is consumed, the first page of the next
+    // pair is in flight, and its second page is requested right after
+    for (int p = p0; p < p1; p += 4) {
+      load_page(min(p + 2, p1 - 1), buf2);
+      consume2(p, buf0, buf1, p + 1 < p1);
+      load_page(min(p + 3, p1 - 1), buf3);
+      if (p + 2 >= p1) break;
+      load_page(min(p + 4, p1 - 1), buf0);
+      consume2(p + 2, buf2, buf3, p + 3 < p1);
+      load_page(min(p + 5, p1 - 1), buf1);
+    }
+  } else if constexpr (MODE == kPairs) {
     for (int p = p0; p < p1; p += 2) {
       consume2(p, buf0, buf1, p + 1 < p1);
       load_page(min(p + 2, p1 - 1), buf0);
@@ -761,27 +782,28 @@ kap_status launch_attention(const AttnCall& c) {
     // one row slice whenever the rows fit in 64, so each page is read once per (b, g)
     const int nt = R <= 16 ? 1 : R <= 32 ? 2 : R <= 48 ? 3 : 4;
     slices = (R + 16 * nt - 1) / (16 * nt);
-    static const void* const fns[2][2][4] = {
-        {{(const void*)attn_partial_bf16<64, 1, false>, (const void*)attn_partial_bf16<64, 2, false>,
-          (const void*)attn_partial_bf16<64, 3, false>, (const void*)attn_partial_bf16<64, 4, false>},
-         {(const void*)attn_partial_bf16<128, 1, false>, (const void*)attn_partial_bf16<128, 2, false>,
-          (const void*)attn_partial_bf16<128, 3, false>, (const void*)attn_partial_bf16<128, 4, false>}},
-        {{(const void*)attn_partial_bf16<64, 1, true>, (const void*)attn_partial_bf16<64, 2, true>,
-          (const void*)attn_partial_bf16<64, 3, true>, (const void*)attn_partial_bf16<64, 4, true>},
-         {(const void*)attn_partial_bf16<128, 1, true>, (const void*)attn_partial_bf16<128, 2, true>,
-          (const void*)attn_partial_bf16<128, 3, true>, (const void*)attn_partial_bf16<128, 4, true>}}};
+#define KAP_PARTIALS(D, M)                                                            \
+  {(const void*)attn_partial_bf16<D, 1, M>, (const void*)attn_partial_bf16<D, 2, M>,      \
+   (const void*)attn_partial_bf16<D, 3, M>, (const void*)attn_partial_bf16<D, 4, M>}
+    static const void* const fns[3][2][4] = {
+        {KAP_PARTIALS(64, kThrottled), KAP_PARTIALS(128, kThrottled)},
+        {KAP_PARTIALS(64, kPairs), KAP_PARTIALS(128, kPairs)},
+        {KAP_PARTIALS(64, kStaggered), KAP_PARTIALS(128, kStaggered)}};
+#undef KAP_PARTIALS
     const int di = c.D == 128 ? 1 : 0;
     // Short work items (a selected view) are latency-bound, and the 48/64-row
-    // tiles measured faster with a pair of pages requested at a time: both run
-    // the pipelined variant.  Long items with 16/32-row tiles saturate HBM,
-    // where about one page in flight per wave across many waves measured
-    // fastest: they run the throttled variant.  The host bounds the item length from the table width,
-    // mirroring the device plan's chunk formula.
+    // tiles need their per-page compute to overlap the next pair's loads: both
+    // run the pair loop.  Long items saturate HBM, where about one page in
+    // flight per wave measured fastest: with 16-row tiles (two waves per SIMD)
+    // the throttled ring, with 32-row tiles (one wave per SIMD, so nothing else
+    // hides its compute) the staggered loop.  The host bounds the item length
+    // from the table width, mirroring the device plan's chunk formula.
     const int rows = c.B * c.Hkv;
     const int t0 = max(1, min(kTargetItems, resident_blocks(fns[0][di][nt - 1], 64) / slices));
     const int aim = max(t0 - rows, max(t0 / 2, 1));
     const long long chunk = max(((long long)c.width * rows + aim - 1) / aim, (long long)kMinChunk);
-    fn = fns[(chunk <= kPipelinedMaxPages || nt >= 3) ? 1 : 0][di][nt - 1];
+    const int mode = (chunk <= kShortItemPages || nt >= 3) ? kPairs : nt == 1 ? kThrottled : kStaggered;
+    fn = fns[mode][di][nt - 1];
   } else {
     slices = (R + 31) / 32;
     fn = c.D == 128 ? (const void*)attn_partial_f32<128> : (const void*)attn_partial_f32<64>;

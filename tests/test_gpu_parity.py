@@ -253,6 +253,44 @@ def test_verify_row_tiles(name, q_len, D):
     print(f"[{name} q_len {q_len} D {D}] verify max rel err {err:.2e}", flush=True)
 
 
+_long_cache = {}
+
+
+@pytest.mark.parametrize("q_len", [4, 2])
+def test_long_ragged_items(q_len):
+    """Work items longer than 32 pages, whose length is not a multiple of the
+    kernel's 4-page step, and a shorter last item in every row: the disciplines
+    for long page runs (the staggered loop for 32-row tiles, the throttled ring
+    for 16-row tiles and the q = 1 decode).  4 requests of 33K-52K tokens under
+    GQA 8:1 with 4 KV heads make 16 rows of 2084-3251 pages; on MI355X the plan
+    splits them into items of 41 pages (32-row tiles, 1024 resident waves) or 33
+    pages (16-row tiles, 1280 items)."""
+    if q_len not in _long_cache:
+        _long_cache.clear()
+        w = W.spec("qwen32b_128k", B=4, seq_lens=[52001, 41111, 36000, 33333], Hq=32, Hkv=4,
+                   q_len=q_len)
+        _long_cache[q_len] = Case(w)
+    c = _long_cache[q_len]
+    w = c.w
+    start = np.maximum(c.b["positions"] - 3, 0).astype(np.int32)
+    lse = torch.empty((w.B, q_len, w.Hq), dtype=torch.float32, device="cuda")
+    out = kap.verify_attn(c.qv, t(start), c.K, c.V, c.bt, c.L, lse=lse)
+    torch.cuda.synchronize()
+    ref, lref = oracle.attend(c.b["qv"], start, c.Kl, c.Vl, c.btl,
+                              oracle.keys_full(c.b["seq_lens"]), 1, w.Hkv)
+    err = _check_attn(c, out, lse, ref, lref)
+    print(f"[long items, q_len {q_len}] verify max rel err {err:.2e}", flush=True)
+    if q_len == 2:
+        lse1 = torch.empty((w.B, w.Hq), dtype=torch.float32, device="cuda")
+        out1 = kap.decode_attn(c.q, c.pos, c.K, c.V, c.bt, c.L, G=1, lse=lse1)
+        torch.cuda.synchronize()
+        ref1, lref1 = oracle.attend(c.b["q"][:, None], c.b["positions"], c.Kl, c.Vl, c.btl,
+                                    oracle.keys_full(c.b["seq_lens"]), 1, w.Hkv)
+        err1 = _check_attn(c, out1, lse1, ref1[:, 0], lref1[:, 0])
+        print(f"[long items] full decode max rel err {err1:.2e}", flush=True)
+    _long_cache.clear()
+
+
 @pytest.mark.parametrize("Hq,Hkv,D,dtype", [
     (8, 8, 128, "bf16"),     # MHA: one query row per KV head
     (16, 1, 64, "bf16"),     # MQA, head_dim 64
