@@ -112,6 +112,7 @@ def test_select_validation(lib):
     assert sel(budget=129) == CAPACITY          # the fallback cue
     assert b"capacity" in lib.kap_last_error()
     assert sel(max_pages=70000) == UNSUPPORTED
+    assert sel(max_pages=65537) == UNSUPPORTED  # one past the widest row the top-K takes
     assert sel(per_head=2) == INVALID
     assert sel(k_mid=None) == INVALID
     assert sel(B=0) == OK
@@ -177,6 +178,9 @@ def test_attention_validation(lib):
         assert _attn(lib, fn, scale=0.0) == INVALID
         assert _attn(lib, fn, B=0) == OK
     assert _attn(lib, "verify", q_len=17) == UNSUPPORTED
+    for fn in ("decode", "verify"):                            # more than 4096 (request, KV head) rows
+        assert _attn(lib, fn, B=513, Hkv=8, Hq=64) == UNSUPPORTED
+        assert _attn(lib, fn, B=4097, Hkv=1, Hq=8) == UNSUPPORTED
     assert _attn(lib, "decode", G=3) == INVALID
 
 

@@ -421,6 +421,50 @@ def test_select_compact_on_a_long_table():
     _select_compact_case(23, 12500)
 
 
+def test_select_compact_at_the_widest_table():
+    """65536 pages (a 1M-token context), the widest row the top-K takes."""
+    _select_compact_case(24, 65536)
+
+
+def test_attention_at_the_row_limit():
+    """4096 (request, KV head) rows, the most one attention call takes: past 512
+    rows the plan reads row lengths outside its register cache, and the rows
+    outnumber the work-item target, so most rows are one item.  512 ragged
+    requests of 0-399 tokens (empty, 1- and 16-token rows among them), GQA 2:1,
+    8 KV heads, D 64: full-table decode, selected decode over per-head compact
+    tables, and a 2-token verify."""
+    rng = np.random.default_rng(31)
+    L = rng.integers(0, 400, size=512)
+    L[:3] = [0, 1, 16]
+    w = W.spec("llama8b_32k", B=512, seq_lens=[int(x) for x in L], Hq=16, D=64, needles=0,
+               q_len=2, per_head=True, k_mid=5)
+    c = Case(w)
+    b = c.b
+    lse = torch.empty((w.B, w.Hq), dtype=torch.float32, device="cuda")
+    out = kap.decode_attn(c.q, c.pos, c.K, c.V, c.bt, c.L, G=1, lse=lse)
+    torch.cuda.synchronize()
+    ref, lref = oracle.attend(b["q"][:, None], b["positions"], c.Kl, c.Vl, c.btl,
+                              oracle.keys_full(b["seq_lens"]), 1, w.Hkv)
+    e_full = _check_attn(c, out, lse, ref[:, 0], lref[:, 0])
+    cap = c.budget()
+    _, sel_ref, cnt_ref = _oracle_chain(c, cap)
+    cbt, clog, clen, slot = kap.compact_view(t(sel_ref), t(cnt_ref), c.bt, c.L, c.pos, 1)
+    out = kap.decode_attn(c.q, c.pos, c.K, c.V, cbt, clen, G=w.Hkv, lse=lse)
+    torch.cuda.synchronize()
+    keys = oracle.keys_selected(sel_ref, cnt_ref, b["seq_lens"])
+    ref, lref = oracle.attend(b["q"][:, None], b["positions"], c.Kl, c.Vl, c.btl, keys, w.Hkv, w.Hkv)
+    e_sel = _check_attn(c, out, lse, ref[:, 0], lref[:, 0])
+    start = np.maximum(b["positions"] - 1, 0).astype(np.int32)
+    vlse = torch.empty((w.B, w.q_len, w.Hq), dtype=torch.float32, device="cuda")
+    vout = kap.verify_attn(c.qv, t(start), c.K, c.V, c.bt, c.L, lse=vlse)
+    torch.cuda.synchronize()
+    vref, vlref = oracle.attend(b["qv"], start, c.Kl, c.Vl, c.btl,
+                                oracle.keys_full(b["seq_lens"]), 1, w.Hkv)
+    e_ver = _check_attn(c, vout, vlse, vref, vlref)
+    print(f"[4096 rows] max rel err: full {e_full:.2e} selected {e_sel:.2e} verify {e_ver:.2e}",
+          flush=True)
+
+
 def _select_compact_case(seed, P):
     rng = np.random.default_rng(seed)
     palette = np.array([0.0, -0.0, 1.0, -1.0, 2.5, np.inf, -np.inf, np.nan, 1.0, 0.5], np.float32)
