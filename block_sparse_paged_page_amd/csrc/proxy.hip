@@ -28,28 +28,32 @@ __global__ __launch_bounds__(256) void proxy_partial_kernel(const uint16_t* hidd
   // rows in flight at once: all of the wave's rows, or 16 when the batch is 16
   constexpr int INFL = BM >= 16 ? 16 : RPW;
   const uint16_t* wbase = wq + (int64_t)(c0 + wave * RPW) * n_out + n0 + lane * 4;
-  // The first W_q rows go out before anything else: the hidden-state slice is
-  // staged in LDS while they are in flight (straight-line loads, and a barrier
-  // that orders LDS only).  W_q is read once per call: streaming loads.
+  // The hidden-state slice is requested first and the W_q rows right after.
+  // Loads complete in issue order, so staging the slice in LDS waits only for
+  // its own few loads, and the row loop below waits for one W_q row at a time:
+  // each row's FMAs run while the later rows are still in flight.  (Issued the
+  // other way round, staging the slice waited for every W_q row, and all of
+  // the arithmetic ran after the whole burst had arrived.)  W_q is read once
+  // per call: streaming loads.
+  __shared__ float sh[BM][kProxyRows];
+  constexpr int PER = BM * kProxyRows / 256 > 0 ? BM * kProxyRows / 256 : 1;  // values per thread
+  uint16_t hraw[PER];
+#pragma unroll
+  for (int k = 0; k < PER; ++k) {
+    const int e = k * 256 + tid;
+    const int b = e / kProxyRows, c = e % kProxyRows;
+    hraw[k] = hidden[(int64_t)min(b, B - 1) * dm + c0 + c];
+  }
+  __builtin_amdgcn_sched_barrier(0);  // keep the slice's loads ahead of the rows
   uint2 wrow[INFL];
 #pragma unroll
   for (int r = 0; r < INFL; ++r) wrow[r] = ld_stream8(wbase + (int64_t)r * n_out);
-  __shared__ float sh[BM][kProxyRows];
-  {
-    constexpr int PER = BM * kProxyRows / 256;  // hidden values per thread (BM >= 2), else 1
-    float hv[PER > 0 ? PER : 1];
+  __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
-    for (int k = 0; k < (PER > 0 ? PER : 1); ++k) {
-      const int e = k * 256 + tid;
-      const int b = e / kProxyRows, c = e % kProxyRows;
-      hv[k] = bf16_to_f32(hidden[(int64_t)min(b, B - 1) * dm + c0 + c]);
-    }
-#pragma unroll
-    for (int k = 0; k < (PER > 0 ? PER : 1); ++k) {
-      const int e = k * 256 + tid;
-      const int b = e / kProxyRows, c = e % kProxyRows;
-      if (e < BM * kProxyRows) sh[b][c] = b < B ? hv[k] : 0.f;
-    }
+  for (int k = 0; k < PER; ++k) {
+    const int e = k * 256 + tid;
+    const int b = e / kProxyRows, c = e % kProxyRows;
+    if (e < BM * kProxyRows) sh[b][c] = b < B ? bf16_to_f32(hraw[k]) : 0.f;
   }
   lds_barrier();
   float acc[BM][4];
