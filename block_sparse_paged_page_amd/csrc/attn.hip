@@ -114,9 +114,20 @@ __device__ PlanItem plan_find(const PlanIn& p, int item, int32_t* row_off, int32
   // Otherwise every row may end in a partial item, and total / (target -
   // rows) satisfies it (at least target / 2 as the divisor).
   int chunk;
+  int shift = 0;  // pages moved from each odd item to the even item before it
   if (local == longest * rows && p.target >= rows && longest > 0) {
     const int per_row = p.target / rows;
     chunk = max((longest + per_row - 1) / per_row, kMinChunk);
+    // Consecutive block ids go to consecutive XCDs, and on MI355X the waves
+    // of the odd-numbered ones stream HBM about 5 % slower (per-wave
+    // timelines, random page placement).  With an even item count per row,
+    // item parity is block-id parity, so odd items give chunk / 40 pages to
+    // the even item before them: the two halves then end together (measured:
+    // chunk / 64 and chunk / 20 both gain less).  The last item (odd) keeps at
+    // least one page.
+    const int n_row = (longest + chunk - 1) / chunk;
+    const int last_len = longest - (n_row - 1) * chunk;
+    if ((n_row & 1) == 0 && last_len > chunk / 40) shift = chunk / 40;
   } else {
     const int aim = max(p.target - rows, max(p.target / 2, 1));
     chunk = max((local + aim - 1) / aim, kMinChunk);
@@ -152,6 +163,8 @@ __device__ PlanItem plan_find(const PlanIn& p, int item, int32_t* row_off, int32
       it.g = rr % p.Hkv;
       it.p0 = j * chunk;
       it.p1 = min(__shfl(np, src), it.p0 + chunk);
+      if (j & 1) it.p0 += shift;
+      else if (it.p1 < __shfl(np, src)) it.p1 += shift;
       it.len = __shfl(ln, src);
       it.valid = true;
     }
