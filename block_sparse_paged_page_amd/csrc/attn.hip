@@ -537,11 +537,15 @@ __global__ __launch_bounds__(64) void attn_partial_bf16(PartArgs a) {
       load_page(min(p + 5, p1 - 1), buf1);
     }
   } else if constexpr (MODE == kPairs) {
-    for (int p = p0; p < p1; p += 2) {
-      consume2(p, buf0, buf1, p + 1 < p1);
-      load_page(min(p + 2, p1 - 1), buf0);
+    // the last pair is consumed after the loop, so no pages past the item are
+    // requested (clamped copies would be fetched again: V streams)
+    int p = p0;
+    for (; p + 2 < p1; p += 2) {
+      consume2(p, buf0, buf1, true);
+      load_page(p + 2, buf0);
       load_page(min(p + 3, p1 - 1), buf1);
     }
+    consume2(p, buf0, buf1, p + 1 < p1);
   } else {
     for (int p = p0; p < p1; p += 4) {
       consume2(p, buf0, buf1, p + 1 < p1);
