@@ -219,8 +219,10 @@ struct PartArgs {
 //    length): straight-line loads of one pair at a time, requested as soon as
 //    the previous pair is consumed.
 // The straight-line disciplines read page-table entries through scalar loads
-// and clamp pages past the item to its last page (an L2 hit whose scores are
-// masked), so the compiler waits for exactly the loads about to be consumed.
+// and make every page load unconditional, so the compiler waits for exactly
+// the loads about to be consumed: the staggered loop clamps pages past the
+// item to its last page (scores masked; at most two such loads per item), and
+// the pair loop consumes its last pair after the loop and requests none.
 // V is read with the non-temporal policy (each byte once per call) and K with
 // the default one: each K fragment load covers half of a 128-byte line whose
 // other half the next load takes, and early eviction between the two costs
