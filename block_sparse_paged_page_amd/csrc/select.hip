@@ -276,9 +276,13 @@ __global__ __launch_bounds__(1024) void select_kernel(SelArgs a) {
       bin_count = s_suf[5];
       prefix |= d << shift;
       pmask |= dmask << shift;
+      // every key of the chosen bin is taken: the digits below cannot change
+      // the selection (block-uniform; the usual case after the second pass)
+      if (bin_count == remaining) break;
       // the next pass rewrites s_digit / s_suf only after two more barriers
     }
   }
+  // threshold on the digits fixed so far (all 32 bits unless a pass ended early)
   const uint32_t T = prefix;
 
   // ---- ties at T: lowest indices first.  When every key equal to T is taken
@@ -289,7 +293,7 @@ __global__ __launch_bounds__(1024) void select_kernel(SelArgs a) {
     int n_eq = 0;
 #pragma unroll
     for (int j = 0; j < KPT; ++j)
-      if (((cand >> j) & 1ull) && key[j] == T) ++n_eq;
+      if (((cand >> j) & 1ull) && (key[j] & pmask) == T) ++n_eq;
     int tot;
     eq_rank = block_exclusive_scan(n_eq, s_wave, &tot);
   }
@@ -303,8 +307,9 @@ __global__ __launch_bounds__(1024) void select_kernel(SelArgs a) {
       if (all || p < mid_lo || p >= mid_hi) {
         c = true;
       } else if (take > 0 && ((cand >> j) & 1ull)) {
-        if (key[j] > T) c = true;
-        else if (key[j] == T) {
+        const uint32_t km = key[j] & pmask;
+        if (km > T) c = true;
+        else if (km == T) {
           c = eq_rank < remaining;
           ++eq_rank;
         }
