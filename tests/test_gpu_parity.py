@@ -408,6 +408,36 @@ def test_adversarial_selection_keys():
         np.testing.assert_array_equal(cnt.cpu().numpy(), cref)
 
 
+def test_select_radix_exits():
+    """The top-K's radix passes stop once the chosen bin holds exactly the keys
+    still needed.  Three key families reach each exit: one key per power of two
+    (decided by the first 12-bit digit), normal draws (usually decided by the
+    second digit), and a threshold inside a run of equal keys (all three
+    digits, then the tie ranks).  Bit-exact against the oracle, per head and
+    pooled."""
+    rng = np.random.default_rng(25)
+    B, H, P = 3, 2, 4096
+    S = np.empty((B, H, P), np.float32)
+    # row 0: 4000 keys with distinct top 12 bits (sign, exponent, 3 mantissa
+    # bits), then -inf
+    sgn, ex, m3 = np.meshgrid([-1.0, 1.0], np.arange(-124, 126), np.arange(8), indexing="ij")
+    vals = (sgn * np.exp2(ex.astype(np.float64)) * (1.0 + m3 / 8.0)).ravel().astype(np.float32)
+    for h in range(H):
+        S[0, h] = np.concatenate([rng.permutation(vals), np.full(P - vals.size, -np.inf, np.float32)])
+    S[1] = rng.standard_normal((H, P)).astype(np.float32)
+    S[2] = np.where(rng.random((H, P)) < 0.3, np.float32(1.5), rng.standard_normal((H, P)).astype(np.float32))
+    L = np.full(B, 16 * P, np.int32)
+    a, r = np.full(B, 1, np.int32), np.full(B, 2, np.int32)
+    k = np.array([300, 448, 700], np.int32)
+    cap = 1024
+    for per_head in (True, False):
+        sel, cnt = kap.select_topk(t(S), t(L), t(a), t(r), t(k), cap, cap, per_head=per_head)
+        torch.cuda.synchronize()
+        sref, cref = oracle.select(S, L, a, r, k, cap, per_head=per_head)
+        np.testing.assert_array_equal(sel.cpu().numpy(), sref)
+        np.testing.assert_array_equal(cnt.cpu().numpy(), cref)
+
+
 def test_select_compact_matches_the_two_calls():
     """kap_select_compact writes exactly what kap_select_topk then kap_compact_view
     write, and what the oracle's selection then compaction give, on adversarial
