@@ -131,6 +131,24 @@ __device__ PlanItem plan_find(const PlanIn& p, int item, int32_t* row_off, int32
   } else {
     const int aim = max(p.target - rows, max(p.target / 2, 1));
     chunk = max((local + aim - 1) / aim, kMinChunk);
+    if (rows <= kPlanCachedTiles * 64) {
+      // Ragged rows: that bound can leave the longest items far above the
+      // average, and the call lasts as long as its longest items.  Search
+      // for the smallest chunk whose items still fit the target, between the
+      // even split and the bound (every wave computes the same value from
+      // the cached lengths).
+      int lo = max((local + p.target - 1) / p.target, kMinChunk), hi = chunk;
+      while (lo < hi) {
+        const int mid = (lo + hi) >> 1;
+        int n = 0;
+#pragma unroll
+        for (int t = 0; t < kPlanCachedTiles; ++t) n += ((lenc[t] + kPage - 1) / kPage + mid - 1) / mid;
+        for (int o = 32; o > 0; o >>= 1) n += __shfl_xor(n, o);
+        if (n <= p.target) hi = mid;
+        else lo = mid + 1;
+      }
+      chunk = lo;
+    }
   }
   PlanItem it{0, 0, 0, 0, 0, false};
   int carry = 0;
