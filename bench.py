@@ -959,6 +959,9 @@ def main():
                 "mfma": {"flops_per_launch": ver_flops, "tflops": round(ver_tflops, 1),
                          "frac_of_bf16_dense_peak": round(ver_tflops / 2500.0, 4)}}
     s_meas = nbytes["decode_selected"] / nbytes["decode_full"]
+    # the same ratio with the route's summary reads charged to the proposal step
+    summ_bytes = int(((b["seq_lens"].astype(np.int64) + 15) // 16).sum()) * Hkv * D * EB
+    s_meas_route = (nbytes["decode_selected"] + summ_bytes) / nbytes["decode_full"]
     h = 0.952  # KAP paper Table 5 at 128K: s + (h - s) = 0.055 + 0.897
     result = {
         "metric": METRIC,
@@ -996,6 +999,9 @@ def main():
             "selected_vs_full_decode_speedup": round(full_ms / dec_ms, 3),
             "s_meas_bytes": round(s_meas, 5),
             "phase_boundary_break_even_W_over_KV": round((h - s_meas) / (1 - h), 3),
+            "s_meas_bytes_with_summary_reads": round(s_meas_route, 5),
+            "phase_boundary_break_even_W_over_KV_with_summary_reads":
+                round((h - s_meas_route) / (1 - h), 3),
         },
     }
     if not args.no_cpu_baseline:
