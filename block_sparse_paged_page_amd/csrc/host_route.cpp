@@ -106,6 +106,12 @@ void proxy_tile(const float* h, int nb, int dm, const uint16_t* w, size_t ldw, i
   float wf[kProxyCols];
   for (int k = 0; k < dm; ++k) {
     const uint16_t* row = w + (size_t)k * ldw;
+    // rows are ldw elements apart, each in its own 4 KiB page, where the
+    // hardware's stride prefetch does not follow: prefetch 8 rows ahead
+    if (k + 8 < dm) {
+      const char* ahead = (const char*)(row + 8 * ldw);
+      for (int off = 0; off < nc * 2; off += 64) __builtin_prefetch(ahead + off);
+    }
     for (int c = 0; c < nc; ++c) wf[c] = bf16_bits_to_f32(row[c]);
     for (int c = nc; c < kProxyCols; ++c) wf[c] = 0.f;
     for (int b = 0; b < nb; ++b) {
@@ -193,6 +199,7 @@ kap_status kap_host_score_blocks(const float* q, const int32_t* positions, float
   // tasks: (request, run of 64 pages); a page's Hkv summary rows are one
   // contiguous block, read once for all KV heads
   constexpr int kRun = 64;
+  constexpr int kAhead = 4;  // pages prefetched ahead
   const int runs = (max_pages + kRun - 1) / kRun;
   parallel_for(B * runs, pick_threads(threads, B * runs), [&](int task) {
     const int b = task / runs, p0 = (task % runs) * kRun, p1 = std::min(p0 + kRun, max_pages);
@@ -203,8 +210,13 @@ kap_status kap_host_score_blocks(const float* q, const int32_t* positions, float
         for (int g = 0; g < Hkv; ++g) scores[((size_t)b * Hkv + g) * max_pages + p] = -INFINITY;
         continue;
       }
-      if (p + 2 < N)
-        __builtin_prefetch(summary + (size_t)block_table[(size_t)b * max_pages + p + 2] * Hkv * D);
+      // the whole summary block of the page kAhead ahead (one prefetch per
+      // 64-byte line: a block is Hkv * D * 2 bytes, 2 KiB at Hkv 8, D 128)
+      if (p + kAhead < N) {
+        const char* nb =
+            (const char*)(summary + (size_t)block_table[(size_t)b * max_pages + p + kAhead] * Hkv * D);
+        for (int off = 0; off < Hkv * D * 2; off += 64) __builtin_prefetch(nb + off);
+      }
       const int64_t phys = block_table[(size_t)b * max_pages + p];
       const uint16_t* blk = summary + (size_t)phys * Hkv * D;
       for (int g = 0; g < Hkv; ++g)
