@@ -256,21 +256,21 @@ def test_verify_row_tiles(name, q_len, D):
 _long_cache = {}
 
 
-@pytest.mark.parametrize("q_len", [4, 2])
-def test_long_ragged_items(q_len):
+@pytest.mark.parametrize("q_len,D", [(4, 128), (2, 128), (4, 64)])
+def test_long_ragged_items(q_len, D):
     """Work items longer than 32 pages, whose length is not a multiple of the
     kernel's 4-page step, and a shorter last item in every row: the disciplines
     for long page runs (the staggered loop for 32-row tiles, the throttled ring
     for 16-row tiles and the q = 1 decode).  4 requests of 33K-52K tokens under
     GQA 8:1 with 4 KV heads make 16 rows of 2084-3251 pages; on MI355X the plan
     splits them into items of 41 pages (32-row tiles, 1024 resident waves) or 33
-    pages (16-row tiles, 1280 items)."""
-    if q_len not in _long_cache:
+    pages (16-row tiles, 1280 items).  Head dim 128 and 64."""
+    if (q_len, D) not in _long_cache:
         _long_cache.clear()
         w = W.spec("qwen32b_128k", B=4, seq_lens=[52001, 41111, 36000, 33333], Hq=32, Hkv=4,
-                   q_len=q_len)
-        _long_cache[q_len] = Case(w)
-    c = _long_cache[q_len]
+                   q_len=q_len, D=D)
+        _long_cache[(q_len, D)] = Case(w)
+    c = _long_cache[(q_len, D)]
     w = c.w
     start = np.maximum(c.b["positions"] - 3, 0).astype(np.int32)
     lse = torch.empty((w.B, q_len, w.Hq), dtype=torch.float32, device="cuda")
@@ -279,7 +279,7 @@ def test_long_ragged_items(q_len):
     ref, lref = oracle.attend(c.b["qv"], start, c.Kl, c.Vl, c.btl,
                               oracle.keys_full(c.b["seq_lens"]), 1, w.Hkv)
     err = _check_attn(c, out, lse, ref, lref)
-    print(f"[long items, q_len {q_len}] verify max rel err {err:.2e}", flush=True)
+    print(f"[long items, q_len {q_len}, D {D}] verify max rel err {err:.2e}", flush=True)
     if q_len == 2:
         lse1 = torch.empty((w.B, w.Hq), dtype=torch.float32, device="cuda")
         out1 = kap.decode_attn(c.q, c.pos, c.K, c.V, c.bt, c.L, G=1, lse=lse1)
