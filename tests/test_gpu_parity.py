@@ -263,8 +263,9 @@ def test_long_ragged_items(q_len, D):
     for long page runs (the staggered loop for 32-row tiles, the throttled ring
     for 16-row tiles and the q = 1 decode).  4 requests of 33K-52K tokens under
     GQA 8:1 with 4 KV heads make 16 rows of 2084-3251 pages; on MI355X the plan
-    splits them into items of 41 pages (32-row tiles, 1024 resident waves) or 33
-    pages (16-row tiles, 1280 items).  Head dim 128 and 64."""
+    splits them into items of 41 pages (32-row tiles, 1024 resident waves) or 32
+    pages (16-row tiles, 1280 items), every row ending in a shorter item.  Head
+    dim 128 and 64."""
     if (q_len, D) not in _long_cache:
         _long_cache.clear()
         w = W.spec("qwen32b_128k", B=4, seq_lens=[52001, 41111, 36000, 33333], Hq=32, Hkv=4,
