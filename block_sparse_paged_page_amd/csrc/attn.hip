@@ -103,10 +103,8 @@ __device__ PlanItem plan_find(const PlanIn& p, int item, int32_t* row_off, int32
     local += np;
     longest = max(longest, np);
   }
-  for (int o = 32; o > 0; o >>= 1) {
-    local += __shfl_xor(local, o);
-    longest = max(longest, __shfl_xor(longest, o));
-  }
+  local = wave_sum(local);
+  longest = wave_max_nonneg(longest);
   // The chunk is the smallest with sum over rows of ceil(pages / chunk) <=
   // target, so that the plan fills one resident round without leaving a
   // wave's worth of slots empty.  When every row has the same length n (a
@@ -143,7 +141,7 @@ __device__ PlanItem plan_find(const PlanIn& p, int item, int32_t* row_off, int32
         int n = 0;
 #pragma unroll
         for (int t = 0; t < kPlanCachedTiles; ++t) n += ((lenc[t] + kPage - 1) / kPage + mid - 1) / mid;
-        for (int o = 32; o > 0; o >>= 1) n += __shfl_xor(n, o);
+        n = wave_sum(n);
         if (n <= p.target) hi = mid;
         else lo = mid + 1;
       }
@@ -164,29 +162,25 @@ __device__ PlanItem plan_find(const PlanIn& p, int item, int32_t* row_off, int32
     }
     const int np = (ln + kPage - 1) / kPage;
     const int n = (np + chunk - 1) / chunk;
-    int incl = n;
-#pragma unroll
-    for (int o = 1; o < 64; o <<= 1) {
-      const int y = __shfl_up(incl, o);
-      if (lane >= o) incl += y;
-    }
+    const int incl = wave_incl_scan(n);
     const int excl = carry + incl - n;
     if (row_off && r < rows) row_off[r] = excl;
     const uint64_t hit = __ballot(r < rows && item >= excl && item < excl + n);
     if (hit && !it.valid) {
-      const int src = __ffsll((unsigned long long)hit) - 1;
+      const int src = __ffsll((unsigned long long)hit) - 1;  // wave-uniform
       const int rr = base + src;
-      const int j = item - __shfl(excl, src);
+      const int j = item - __builtin_amdgcn_readlane(excl, src);
+      const int np_src = __builtin_amdgcn_readlane(np, src);
       it.b = rr / p.Hkv;
       it.g = rr % p.Hkv;
       it.p0 = j * chunk;
-      it.p1 = min(__shfl(np, src), it.p0 + chunk);
+      it.p1 = min(np_src, it.p0 + chunk);
       if (j & 1) it.p0 += shift;
-      else if (it.p1 < __shfl(np, src)) it.p1 += shift;
-      it.len = __shfl(ln, src);
+      else if (it.p1 < np_src) it.p1 += shift;
+      it.len = __builtin_amdgcn_readlane(ln, src);
       it.valid = true;
     }
-    carry += __shfl(incl, 63);
+    carry += __builtin_amdgcn_readlane(incl, 63);
     if (it.valid && !row_off) break;
   }
   if (row_off && lane == 0) {

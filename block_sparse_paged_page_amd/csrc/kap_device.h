@@ -84,6 +84,33 @@ __device__ __forceinline__ uint2 ld_stream8(const void* p) {
   return make_uint2(v.x, v.y);
 }
 
+// Wave-wide integer prefix sums and reductions on DPP lane moves (row shifts
+// within each 16-lane row, then row broadcasts), a few VALU cycles per step
+// instead of an LDS round trip per step for shuffles.  Inclusive scan over the
+// 64 lanes in lane order; the total is lane 63's value.
+__device__ __forceinline__ int wave_incl_scan(int x) {
+  x += __builtin_amdgcn_update_dpp(0, x, 0x111, 0xf, 0xf, true);   // row_shr:1
+  x += __builtin_amdgcn_update_dpp(0, x, 0x112, 0xf, 0xf, true);   // row_shr:2
+  x += __builtin_amdgcn_update_dpp(0, x, 0x114, 0xf, 0xf, true);   // row_shr:4
+  x += __builtin_amdgcn_update_dpp(0, x, 0x118, 0xf, 0xf, true);   // row_shr:8
+  x += __builtin_amdgcn_update_dpp(0, x, 0x142, 0xa, 0xf, false);  // row_bcast:15 -> rows 1, 3
+  x += __builtin_amdgcn_update_dpp(0, x, 0x143, 0xc, 0xf, false);  // row_bcast:31 -> rows 2, 3
+  return x;
+}
+__device__ __forceinline__ int wave_sum(int x) {
+  return __builtin_amdgcn_readlane(wave_incl_scan(x), 63);
+}
+// maximum over the wave of values >= 0 (0 is the identity of the steps)
+__device__ __forceinline__ int wave_max_nonneg(int x) {
+  x = max(x, __builtin_amdgcn_update_dpp(0, x, 0x111, 0xf, 0xf, true));
+  x = max(x, __builtin_amdgcn_update_dpp(0, x, 0x112, 0xf, 0xf, true));
+  x = max(x, __builtin_amdgcn_update_dpp(0, x, 0x114, 0xf, 0xf, true));
+  x = max(x, __builtin_amdgcn_update_dpp(0, x, 0x118, 0xf, 0xf, true));
+  x = max(x, __builtin_amdgcn_update_dpp(0, x, 0x142, 0xa, 0xf, false));
+  x = max(x, __builtin_amdgcn_update_dpp(0, x, 0x143, 0xc, 0xf, false));
+  return __builtin_amdgcn_readlane(x, 63);
+}
+
 // Workgroup barrier that orders LDS only: global loads in flight stay in
 // flight across it (__syncthreads also waits for every outstanding load).
 __device__ __forceinline__ void lds_barrier() {

@@ -47,22 +47,12 @@ __device__ __forceinline__ uint32_t order_key(float f) {
 // Exclusive prefix of v over the block (1024 threads, thread order); *total gets the sum.
 __device__ __forceinline__ int block_exclusive_scan(int v, int* s_wave, int* total) {
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  int x = v;
-#pragma unroll
-  for (int o = 1; o < 64; o <<= 1) {
-    const int y = __shfl_up(x, o);
-    if (lane >= o) x += y;
-  }
+  const int x = wave_incl_scan(v);
   if (lane == 63) s_wave[wave] = x;
   __syncthreads();
   if (tid < 64) {
-    int w = tid < 16 ? s_wave[tid] : 0;
-    int inc = w;
-#pragma unroll
-    for (int o = 1; o < 16; o <<= 1) {
-      const int y = __shfl_up(inc, o);
-      if (lane >= o) inc += y;
-    }
+    const int w = tid < 16 ? s_wave[tid] : 0;
+    const int inc = wave_incl_scan(w);
     if (tid < 16) s_wave[16 + tid] = inc - w;  // exclusive wave offsets
     if (tid == 15) s_wave[32] = inc;
   }
