@@ -491,7 +491,7 @@ __global__ __launch_bounds__(64) void attn_partial_bf16(PartArgs a) {
       }
     }
 #pragma unroll
-    for (int t = 0; t < NT; ++t) mx[t] = wave_max_xor(mx[t], 16, 64);
+    for (int t = 0; t < NT; ++t) mx[t] = rows_max(mx[t]);
     // move a row's reference only when its running max clears it by kLazyRescale
     bool bump[NT];
     bool any = false;
@@ -574,8 +574,7 @@ __global__ __launch_bounds__(64) void attn_partial_bf16(PartArgs a) {
   }
 #pragma unroll
   for (int t = 0; t < NT; ++t) {
-    l[t] += __shfl_xor(l[t], 16);
-    l[t] += __shfl_xor(l[t], 32);
+    l[t] = rows_sum(l[t]);
     const int r = row0 + 16 * t + l16;
     if (r < a.R) {
       float* dst = a.part_o + ((int64_t)item * a.R + r) * D + 4 * q4;

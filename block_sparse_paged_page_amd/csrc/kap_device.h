@@ -119,9 +119,31 @@ __device__ __forceinline__ void lds_barrier() {
   __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup", "local");
 }
 
-__device__ __forceinline__ float wave_max_xor(float v, int from, int to) {
-  for (int m = from; m < to; m <<= 1) v = fmaxf(v, __shfl_xor(v, m));
-  return v;
+// Max and sum over the four lanes i, i ^ 16, i ^ 32, i ^ 48 (the same lane of
+// each 16-lane row) with gfx950's row-swap moves (one VALU instruction per
+// exchange).  The sum adds in the order (x_i + x_{i^16}) + (x_{i^32} + x_{i^48})
+// for every lane, as an xor butterfly does.
+__device__ __forceinline__ void rows_exchange16(float v, float& a, float& b) {
+  const auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+  a = __uint_as_float(r[0]);
+  b = __uint_as_float(r[1]);
+}
+__device__ __forceinline__ void rows_exchange32(float v, float& a, float& b) {
+  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+  a = __uint_as_float(r[0]);
+  b = __uint_as_float(r[1]);
+}
+__device__ __forceinline__ float rows_max(float v) {
+  float a, b;
+  rows_exchange16(v, a, b);
+  rows_exchange32(fmaxf(a, b), a, b);
+  return fmaxf(a, b);
+}
+__device__ __forceinline__ float rows_sum(float v) {
+  float a, b;
+  rows_exchange16(v, a, b);
+  rows_exchange32(a + b, a, b);
+  return a + b;
 }
 
 }  // namespace kap
