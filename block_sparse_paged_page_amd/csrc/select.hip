@@ -45,6 +45,8 @@ __device__ __forceinline__ uint32_t order_key(float f) {
 }
 
 // Exclusive prefix of v over the block (1024 threads, thread order); *total gets the sum.
+// s_wave (33 ints) must not be reused by a later call: there is no trailing
+// barrier, so each call site has its own region.
 __device__ __forceinline__ int block_exclusive_scan(int v, int* s_wave, int* total) {
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int x = wave_incl_scan(v);
@@ -59,7 +61,6 @@ __device__ __forceinline__ int block_exclusive_scan(int v, int* s_wave, int* tot
   __syncthreads();
   const int excl = s_wave[16 + wave] + x - v;
   *total = s_wave[32];
-  __syncthreads();
   return excl;
 }
 
@@ -68,9 +69,9 @@ __global__ __launch_bounds__(1024) void select_kernel(SelArgs a) {
   const int gr = blockIdx.x, b = blockIdx.y;
   const int G = a.per_head ? a.Hkv : 1;
   const int tid = threadIdx.x;
-  __shared__ int s_hist[4096];
+  __shared__ int s_hist[2][4096];  // radix histograms, alternating by pass
   __shared__ int s_suf[8];  // [4] keys above the chosen bin, [5] keys in it
-  __shared__ int s_wave[33];
+  __shared__ int s_wave[5][33];  // one region per block scan (three passes, ties, output)
   __shared__ uint32_t s_digit;
   __shared__ int s_last;  // the row's last logical page is in its list
   if (a.cbt) {  // uniform
@@ -227,17 +228,22 @@ __global__ __launch_bounds__(1024) void select_kernel(SelArgs a) {
   int remaining = take;
   int bin_count = 0;  // keys in the chosen bin of the last pass: after it, those equal to T
   if (take > 0) {
+    // the first pass's 4096 bins and the second's 1024; each pass clears the
+    // histogram the pass after it uses, before its last barrier
+#pragma unroll
+    for (int k = 0; k < 4; ++k) s_hist[0][k * 1024 + tid] = 0;
+    s_hist[1][tid] = 0;
+    __syncthreads();
 #pragma unroll
     for (int pass = 0; pass < 3; ++pass) {
       const int shift = pass == 0 ? 20 : (pass == 1 ? 10 : 0);
       const int bpt = pass == 0 ? 4 : 1;  // bins per thread: 4096 or 1024 bins
       const uint32_t dmask = pass == 0 ? 0xfffu : 0x3ffu;
-      for (int e = tid; e < 1024 * bpt; e += 1024) s_hist[e] = 0;
-      __syncthreads();
+      int* hist = s_hist[pass & 1];
 #pragma unroll
       for (int j = 0; j < KPT; ++j)
         if (((cand >> j) & 1ull) && (key[j] & pmask) == prefix)
-          atomicAdd(&s_hist[(key[j] >> shift) & dmask], 1);
+          atomicAdd(&hist[(key[j] >> shift) & dmask], 1);
       __syncthreads();
       // thread t owns bins [t * bpt, (t + 1) * bpt); the keys in bins above a
       // thread's range come from a block scan over the threads
@@ -245,11 +251,11 @@ __global__ __launch_bounds__(1024) void select_kernel(SelArgs a) {
       int local = 0;
 #pragma unroll
       for (int k = 0; k < 4; ++k) {
-        hl[k] = k < bpt ? s_hist[tid * bpt + k] : 0;
+        hl[k] = k < bpt ? hist[tid * bpt + k] : 0;
         local += hl[k];
       }
       int tot;
-      const int excl = block_exclusive_scan(local, s_wave, &tot);
+      const int excl = block_exclusive_scan(local, s_wave[pass], &tot);
       int above = tot - excl - local;
 #pragma unroll
       for (int k = 3; k >= 0; --k) {
@@ -260,6 +266,9 @@ __global__ __launch_bounds__(1024) void select_kernel(SelArgs a) {
         }
         above += hl[k];
       }
+      // the third pass's histogram is the first pass's, last read above in
+      // the first pass (before its final barrier)
+      if (pass == 1) s_hist[0][tid] = 0;
       __syncthreads();
       const uint32_t d = s_digit;
       remaining -= s_suf[4];
@@ -269,7 +278,7 @@ __global__ __launch_bounds__(1024) void select_kernel(SelArgs a) {
       // every key of the chosen bin is taken: the digits below cannot change
       // the selection (block-uniform; the usual case after the second pass)
       if (bin_count == remaining) break;
-      // the next pass rewrites s_digit / s_suf only after two more barriers
+      // the next pass rewrites s_digit / s_suf only after three more barriers
     }
   }
   // threshold on the digits fixed so far (all 32 bits unless a pass ended early)
@@ -285,7 +294,7 @@ __global__ __launch_bounds__(1024) void select_kernel(SelArgs a) {
     for (int j = 0; j < KPT; ++j)
       if (((cand >> j) & 1ull) && (key[j] & pmask) == T) ++n_eq;
     int tot;
-    eq_rank = block_exclusive_scan(n_eq, s_wave, &tot);
+    eq_rank = block_exclusive_scan(n_eq, s_wave[3], &tot);
   }
 
   uint64_t chosen = 0;
@@ -310,7 +319,7 @@ __global__ __launch_bounds__(1024) void select_kernel(SelArgs a) {
   const int n_ch = __popcll(chosen);
   if (N > 0 && (N - 1) / KPT == tid && ((chosen >> ((N - 1) % KPT)) & 1ull)) s_last = 1;
   int total;
-  int pos = block_exclusive_scan(n_ch, s_wave, &total);  // (its barriers publish s_last)
+  int pos = block_exclusive_scan(n_ch, s_wave[4], &total);  // (its barriers publish s_last)
   const int64_t row = (int64_t)b * G + gr;
   int gb[KPT];  // compact view without the staged row: one straight-line gather
   if (a.cbt && !bt_lds) {
