@@ -79,6 +79,38 @@ static kap_status check_heads(int32_t Hq, int32_t Hkv, int32_t D, int32_t page_s
 
 }  // namespace kap
 
+// ------------------------------------------------------------------ allocation-free decode
+// The attention workspace of kap_decode_attn_noalloc lives in this array, one
+// copy per GPU, held until the process ends.  Host code never passes the
+// array's name to a kernel (on the host it is a stand-in, not a device
+// address): each device's address comes from hipGetSymbolAddress, taken once
+// with that device current, and only that address is used.
+static __device__ __align__(256) unsigned char scratch[KAP_NOALLOC_SCRATCH_BYTES];
+
+namespace kap {
+namespace {
+constexpr int kMaxDevices = 64;
+std::atomic<void*> g_scratch_ptr[kMaxDevices];
+
+// Device address of the current device's scratch array (NULL on failure,
+// with the error recorded).
+void* scratch_address(int dev) {
+  void* p = g_scratch_ptr[dev].load(std::memory_order_acquire);
+  if (p) return p;
+  void* q = nullptr;
+  const hipError_t e = hipGetSymbolAddress(&q, HIP_SYMBOL(scratch));
+  if (e != hipSuccess || q == nullptr) {
+    (void)hipGetLastError();
+    set_error("scratch address on device %d: %s", dev, hipGetErrorString(e));
+    return nullptr;
+  }
+  // two threads may both look it up: they find the same address
+  g_scratch_ptr[dev].store(q, std::memory_order_release);
+  return q;
+}
+}  // namespace
+}  // namespace kap
+
 using namespace kap;
 
 extern "C" {
@@ -320,6 +352,40 @@ kap_status kap_decode_attn(const void* q, int32_t q_dtype, const int32_t* positi
   return attn_common(q, q_dtype, positions, 1, rope_theta, scale, k_pool, v_pool, kv_dtype,
                      num_pages, Hkv, D, page_size, block_table, table_width, G, lens, B, Hq, out,
                      lse, workspace, workspace_bytes, stream);
+}
+
+kap_status kap_decode_attn_noalloc(const void* q, int32_t q_dtype, const int32_t* positions,
+                                   float rope_theta, float scale, const void* k_pool,
+                                   const void* v_pool, int32_t kv_dtype, int32_t num_pages,
+                                   int32_t Hkv, int32_t D, int32_t page_size,
+                                   const int32_t* block_table, int32_t table_width, int32_t G,
+                                   const int32_t* lens, int32_t B, int32_t Hq, void* out,
+                                   float* lse, kap_stream stream) {
+  g_err[0] = 0;
+  // size check first, before any HIP call
+  if (B > 0 && Hq > 0 && Hkv > 0 && Hq % Hkv == 0) {
+    const size_t need = kap_attn_workspace_bytes(B, 1, Hq, Hkv, D);
+    if (need > (size_t)KAP_NOALLOC_SCRATCH_BYTES)
+      return fail(KAP_ERR_WORKSPACE,
+                  "decode needs %zu bytes of scratch (B=%d Hq=%d Hkv=%d D=%d); the static "
+                  "scratch holds %zu: use kap_decode_attn with a caller workspace",
+                  need, B, Hq, Hkv, D, (size_t)KAP_NOALLOC_SCRATCH_BYTES);
+  }
+  if (B <= 0) {  // nothing to launch; validate the rest as kap_decode_attn does
+    return attn_common(q, q_dtype, positions, 1, rope_theta, scale, k_pool, v_pool, kv_dtype,
+                       num_pages, Hkv, D, page_size, block_table, table_width, G, lens, B, Hq,
+                       out, lse, nullptr, 0, stream);
+  }
+  int dev = 0;
+  const hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return fail(KAP_ERR_HIP, "hipGetDevice: %s", hipGetErrorString(e));
+  if (dev < 0 || dev >= kMaxDevices)
+    return fail(KAP_ERR_UNSUPPORTED, "device %d (at most %d devices)", dev, kMaxDevices);
+  void* ws = scratch_address(dev);
+  if (!ws) return KAP_ERR_HIP;
+  return attn_common(q, q_dtype, positions, 1, rope_theta, scale, k_pool, v_pool, kv_dtype,
+                     num_pages, Hkv, D, page_size, block_table, table_width, G, lens, B, Hq, out,
+                     lse, ws, (size_t)KAP_NOALLOC_SCRATCH_BYTES, stream);
 }
 
 kap_status kap_verify_attn(const void* q, int32_t q_dtype, const int32_t* start_positions,

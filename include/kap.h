@@ -25,7 +25,9 @@
  *
  * Conventions shared by every entry point
  *   - Pointers named *device* are device memory owned by the caller; the
- *     library never frees, keeps or allocates memory.  Scalars are host values.
+ *     library never frees, keeps or allocates memory (the one exception is the
+ *     static per-GPU scratch of kap_decode_attn_noalloc, part of the loaded
+ *     code object).  Scalars are host values.
  *   - Every call enqueues kernels on `stream` (a hipStream_t; NULL = default
  *     stream) and returns without synchronizing, so a sequence of calls can be
  *     captured in a HIP graph ([KAP] stabilizes shapes, tables and metadata so
@@ -255,6 +257,32 @@ KAP_API kap_status kap_decode_attn(const void* q, int32_t q_dtype, const int32_t
                            int32_t G, const int32_t* lens, int32_t B, int32_t Hq, void* out,
                            float* lse, void* workspace, size_t workspace_bytes,
                            kap_stream stream);
+
+/*
+ * Allocation-free variant of kap_decode_attn, for callers that cannot
+ * allocate device memory (code under HIP graph capture, tight serving loops,
+ * harnesses that forbid allocation): the same arguments without the
+ * workspace, the same kernels and the same results bit for bit.  The split-K
+ * workspace is a static device array of KAP_NOALLOC_SCRATCH_BYTES inside the
+ * library, one per GPU, held until the process ends; its address is looked up
+ * once per device on the first call with that device current.  No call
+ * allocates or frees memory.
+ *   Returns KAP_ERR_WORKSPACE, before any HIP call, when the call needs more
+ *   than KAP_NOALLOC_SCRATCH_BYTES (kap_attn_workspace_bytes(B, 1, Hq, Hkv, D)
+ *   is the need); use kap_decode_attn with a workspace then.
+ *   Every call on one GPU shares that GPU's array and overwrites what the last
+ *   call left there (nothing in it needs to start at zero).  Calls that
+ *   overlap on one GPU (other streams, other threads) race: serialize them.
+ */
+#define KAP_NOALLOC_SCRATCH_BYTES (16u << 20)
+KAP_API kap_status kap_decode_attn_noalloc(const void* q, int32_t q_dtype,
+                                           const int32_t* positions, float rope_theta,
+                                           float scale, const void* k_pool, const void* v_pool,
+                                           int32_t kv_dtype, int32_t num_pages, int32_t Hkv,
+                                           int32_t D, int32_t page_size,
+                                           const int32_t* block_table, int32_t table_width,
+                                           int32_t G, const int32_t* lens, int32_t B, int32_t Hq,
+                                           void* out, float* lse, kap_stream stream);
 
 /*
  * Full-context verification window ([KAP] verifier: a short contiguous query

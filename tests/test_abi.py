@@ -236,3 +236,19 @@ def test_product_binding_never_imports_oracle():
                 text = open(os.path.join(dirpath, fn)).read()
                 assert "import oracle" not in text and "from oracle" not in text, fn
                 assert "kap_oracle" not in text and "liboracle" not in text, fn
+
+
+def test_noalloc_decode_rejects_oversize_before_any_hip_call(lib):
+    """The allocation-free decode holds its split-K partials in a static
+    scratch of KAP_NOALLOC_SCRATCH_BYTES; a call that needs more is refused
+    with KAP_ERR_WORKSPACE before any HIP call (so this runs without a GPU)."""
+    text = open(HEADER).read()
+    m = re.search(r"#define KAP_NOALLOC_SCRATCH_BYTES \((\d+)u << (\d+)\)", text)
+    cap = int(m.group(1)) << int(m.group(2))
+    B, Hq, Hkv, D = 512, 128, 8, 128
+    assert kap.attn_workspace_bytes(B, 1, Hq, Hkv, D) > cap
+    st = lib.kap_decode_attn_noalloc(NP, 1, NP, 1e4, 0.088, NP, NP, 1, 100, Hkv, D, 16, NP, 64, 1,
+                                     NP, B, Hq, NP, None, None)
+    assert st == WORKSPACE
+    assert b"scratch" in lib.kap_last_error()
+    assert kap.attn_workspace_bytes(4, 1, 64, 8, 128) <= cap   # the 128K, B = 4 decode fits
