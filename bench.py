@@ -271,7 +271,7 @@ def _sweep(args, dev, w, label):
         sl, ct = kap.select_topk(scores, L, anchor, recent, km, bud, bud)
         cb = kap.compact_view(sl, ct, bt, L, pos, 1)
         us = time_call(lambda: kap.decode_attn(q, pos, Ks[lay()], Vs[lay()], cb[0], cb[2], out=out,
-                                               workspace=ws), args.steps, st)
+                                               workspace=ws, logical=cb[1]), args.steps, st)
         nbytes = B * bud * 16 * kv_tok
         sweep.append({"s": round(num / den, 4), "pages": bud, "us": round(us, 2),
                       "GBps": round(nbytes / (us * 1e-6) / 1e9, 1)})
@@ -342,7 +342,7 @@ def run_early_route(args, dev):
 
     def decode(l, s):
         kap.decode_attn(qreal[l], pos, Ks[l], Vs[l], views[l][0], views[l][2], G=Hkv, out=out,
-                        workspace=aws, stream=s)
+                        workspace=aws, stream=s, logical=views[l][1])
 
     main = torch.cuda.current_stream()
     side = torch.cuda.Stream(device=dev)  # default priority
@@ -506,7 +506,8 @@ def run_early_route_cpu(args, dev):
         sel_d.copy_(sel_pin[l], non_blocking=True)
         cnt_d.copy_(cnt_pin[l], non_blocking=True)
         kap.compact_view(sel_d, cnt_d, bt, L, pos, 1, out=view)
-        kap.decode_attn(qreal[l], pos, Ks[l], Vs[l], view[0], view[2], G=Hkv, out=out, workspace=aws)
+        kap.decode_attn(qreal[l], pos, Ks[l], Vs[l], view[0], view[2], G=Hkv, out=out, workspace=aws,
+                        logical=view[1])
 
     def run_overlapped():
         ready = [threading.Event() for _ in range(layers)]
@@ -535,7 +536,8 @@ def run_early_route_cpu(args, dev):
     st = torch.cuda.current_stream()
     t_gpu_layer = time_call(lambda: gpu_layer(5), args.steps, st)
     t_dec = time_call(lambda: kap.decode_attn(qreal[5], pos, Ks[5], Vs[5], view[0], view[2], G=Hkv,
-                                              out=out, workspace=aws), args.steps, st)
+                                              out=out, workspace=aws, logical=view[1]),
+                      args.steps, st)
     med = {k: float(np.median(v)) * 1e6 for k, v in t_parts.items()}
     t_cpu = sum(med.values())
     import os as _os
@@ -592,7 +594,7 @@ def run_mixed(args, dev):
     torch.cuda.synchronize()
     t_route = time_call(route, args.steps, st)
     t_sel = time_call(lambda: kap.decode_attn(q, pos, b["K"], b["V"], cv[0], cv[2], out=out,
-                                              workspace=ws), args.steps, st)
+                                              workspace=ws, logical=cv[1]), args.steps, st)
     t_full = time_call(lambda: kap.decode_attn(q, pos, b["K"], b["V"], bt, L, out=out,
                                                workspace=ws), args.steps, st)
     clen = cv[2].cpu().numpy()[:, 0].astype(np.int64)
@@ -673,7 +675,8 @@ def run_commit(args, dev):
 
     def propose(ly):
         for j in range(K_PROPOSE):
-            kap.decode_attn(q_prop[j], pos_prop[j], ly.K, ly.V, cv[0], cv[2], out=out1, workspace=ws)
+            kap.decode_attn(q_prop[j], pos_prop[j], ly.K, ly.V, cv[0], cv[2], out=out1, workspace=ws,
+                            logical=cv[1])
 
     def commit(ly):
         kap.append_kv(kn, vn, cv[3], ly.K, ly.V)
@@ -732,7 +735,7 @@ def run_workspace(args, dev):
     kap.build_summary(b["K"], bt, L, S)
     scores = kap.score_blocks(q, pos, S, bt, L, Hkv)
     sel, cnt = kap.select_topk(scores, L, anchor, recent, k_mid, cap, cap)
-    cbt, _, clen, _ = kap.compact_view(sel, cnt, bt, L, pos, 1)
+    cbt, clog, clen, _ = kap.compact_view(sel, cnt, bt, L, pos, 1)
     R = args.layers or 8
     pools = [(b["K"], b["V"])] + [(b["K"].clone(), b["V"].clone()) for _ in range(R - 1)]
     wss = [kap.materialize_view(K, V, cbt) for K, V in pools]
@@ -751,11 +754,13 @@ def run_workspace(args, dev):
 
     def dec_pool():
         i = nxt()
-        kap.decode_attn(q, pos, pools[i][0], pools[i][1], cbt, clen, out=out, workspace=ws)
+        kap.decode_attn(q, pos, pools[i][0], pools[i][1], cbt, clen, out=out, workspace=ws,
+                        logical=clog)
 
     def dec_ws():
         i = nxt()
-        kap.decode_attn(q, pos, wss[i][0], wss[i][1], wss[i][2], clen, out=out, workspace=ws)
+        kap.decode_attn(q, pos, wss[i][0], wss[i][1], wss[i][2], clen, out=out, workspace=ws,
+                        logical=clog)
 
     t_mat = time_call(mat, args.steps, st)
     t_pool = time_call(dec_pool, args.steps, st)
@@ -855,7 +860,7 @@ def main():
             lay = next_layer()
             calls.append(lambda lay=lay, j=j: kap.decode_attn(
                 q_prop[j], pos_prop[j], lay.K, lay.V, cview[0], cview[2], G=1, out=dec_out,
-                workspace=ws))
+                workspace=ws, logical=cview[1]))
         lay = next_layer()
         calls.append(lambda lay=lay: kap.verify_attn(qv, pos, lay.K, lay.V, bt, L, out=ver_out,
                                                      workspace=ws))

@@ -44,10 +44,10 @@ _SIGS = {
     "kap_compact_view": ([_P, _P, _I32, _I32, _I32, _P, _I32, _P, _I32, _P, _I32, _P, _P, _P, _P,
                           _P], _I32),
     "kap_attn_workspace_bytes": ([_I32, _I32, _I32, _I32, _I32], _SZ),
-    "kap_decode_attn": ([_P, _I32, _P, _F, _F, _P, _P, _I32, _I32, _I32, _I32, _I32, _P, _I32, _I32,
-                         _P, _I32, _I32, _P, _P, _P, _SZ, _P], _I32),
+    "kap_decode_attn": ([_P, _I32, _P, _F, _F, _P, _P, _I32, _I32, _I32, _I32, _I32, _P, _P, _I32,
+                         _I32, _P, _I32, _I32, _P, _P, _P, _SZ, _P], _I32),
     "kap_decode_attn_noalloc": ([_P, _I32, _P, _F, _F, _P, _P, _I32, _I32, _I32, _I32, _I32, _P,
-                                 _I32, _I32, _P, _I32, _I32, _P, _P, _P], _I32),
+                                 _P, _I32, _I32, _P, _I32, _I32, _P, _P, _P], _I32),
     "kap_verify_attn": ([_P, _I32, _P, _I32, _F, _F, _P, _P, _I32, _I32, _I32, _I32, _I32, _P, _I32,
                          _P, _I32, _I32, _P, _P, _P, _SZ, _P], _I32),
     "kap_diag_stream_read": ([_P, _SZ, _P, _P], _I32),
@@ -246,8 +246,10 @@ def _scale(D, scale):
 
 
 def decode_attn(q, positions, k_pool, v_pool, table, lens, G=1, theta=1e4, scale=None, out=None,
-                lse=None, workspace=None, stream=None):
-    """kap_decode_attn: q [B][Hq][D] over a paged view table [B][G][width] with lens [B][G]."""
+                lse=None, workspace=None, stream=None, logical=None):
+    """kap_decode_attn: q [B][Hq][D] over a paged view table [B][G][width] with lens [B][G];
+    logical [B][G][width] holds each entry's logical page (a compact view), None for a
+    full block table."""
     lib = load()
     B, Hq, D = q.shape
     num_pages, Hkv = k_pool.shape[0], k_pool.shape[1]
@@ -259,14 +261,14 @@ def decode_attn(q, positions, k_pool, v_pool, table, lens, G=1, theta=1e4, scale
                                 device=q.device)
     st = lib.kap_decode_attn(_p(q), _dt(q), _p(positions), float(theta), _scale(D, scale),
                              _p(k_pool), _p(v_pool), _dt(k_pool), num_pages, Hkv, D, 16, _p(table),
-                             width, int(G), _p(lens), B, Hq, _p(out), _p(lse), _p(workspace),
-                             workspace.numel(), _stream(stream))
+                             _p(logical), width, int(G), _p(lens), B, Hq, _p(out), _p(lse),
+                             _p(workspace), workspace.numel(), _stream(stream))
     _check(st, "kap_decode_attn")
     return out
 
 
 def decode_attn_noalloc(q, positions, k_pool, v_pool, table, lens, G=1, theta=1e4, scale=None,
-                        out=None, lse=None, stream=None):
+                        out=None, lse=None, stream=None, logical=None):
     """kap_decode_attn_noalloc: kap_decode_attn without a workspace argument (the
     library's static per-GPU scratch holds the split-K partials)."""
     lib = load()
@@ -276,8 +278,8 @@ def decode_attn_noalloc(q, positions, k_pool, v_pool, table, lens, G=1, theta=1e
         out = torch.empty_like(q)
     st = lib.kap_decode_attn_noalloc(_p(q), _dt(q), _p(positions), float(theta), _scale(D, scale),
                                      _p(k_pool), _p(v_pool), _dt(k_pool), num_pages, Hkv, D, 16,
-                                     _p(table), table.shape[-1], int(G), _p(lens), B, Hq, _p(out),
-                                     _p(lse), _stream(stream))
+                                     _p(table), _p(logical), table.shape[-1], int(G), _p(lens), B,
+                                     Hq, _p(out), _p(lse), _stream(stream))
     _check(st, "kap_decode_attn_noalloc")
     return out
 

@@ -200,6 +200,7 @@ struct PartArgs {
   const void* k;
   const void* v;
   const int32_t* table;
+  const int32_t* logical;  // logical page of each table entry, or null: entry j is page j
   int32_t width, G;
   const int32_t* lens;
   const int32_t* pos;
@@ -254,6 +255,7 @@ template <int D>
 struct PageFrag {
   uint4 k[D / 32];
   uint2 v[D / 16];
+  int lp;  // logical page (the causal mask compares logical positions)
 };
 
 enum { kThrottled = 0, kPairs = 1, kStaggered = 2 };
@@ -275,11 +277,16 @@ __global__ __launch_bounds__(64) void attn_partial_bf16(PartArgs a) {
   const int len = __builtin_amdgcn_readfirstlane(it.len);
   const int pos_b = a.pos[b];  // read once, before any page load is in flight
   const int32_t* trow = a.table + (int64_t)(b * a.G + gr) * a.width;
-  // The straight-line modes read the (read-only) table through the constant address
+  // logical pages of the entries (a compact view), or none: entry p is page p
+  const bool has_lg = a.logical != nullptr;
+  const int32_t* lrow = has_lg ? a.logical + (int64_t)(b * a.G + gr) * a.width : trow;
+  // The straight-line modes read the (read-only) tables through the constant address
   // space: the wave-uniform entries then come through scalar memory and its
   // own counter, so waiting for an entry never waits for K/V loads in flight.
   const __attribute__((address_space(4))) int32_t* trow_s =
       (const __attribute__((address_space(4))) int32_t*)trow;
+  const __attribute__((address_space(4))) int32_t* lrow_s =
+      (const __attribute__((address_space(4))) int32_t*)lrow;
   constexpr int KS = D / 32;  // QK k-steps
   constexpr int NC = D / 16;  // PV dim tiles
   const uint16_t* kpool = (const uint16_t*)a.k;
@@ -314,9 +321,10 @@ __global__ __launch_bounds__(64) void attn_partial_bf16(PartArgs a) {
     }
   }
 
-  // page-table window: lane j holds trow[wbase + j]
+  // page-table window: lane j holds trow[wbase + j] (and its logical page)
   int wbase = p0;
   int tr = trow[min(p0 + lane, p1 - 1)];  // entries past the item are never used
+  int tl = has_lg ? lrow[min(p0 + lane, p1 - 1)] : 0;
   auto phys_of = [&](int p) -> int64_t {
     if constexpr (STRAIGHT) {
       return (int64_t)trow_s[p];
@@ -324,12 +332,20 @@ __global__ __launch_bounds__(64) void attn_partial_bf16(PartArgs a) {
       if (p - wbase >= 64) {  // wave-uniform refill
         wbase += 64;
         tr = trow[min(wbase + lane, p1 - 1)];
+        if (has_lg) tl = lrow[min(wbase + lane, p1 - 1)];
       }
       return (int64_t)__builtin_amdgcn_readlane(tr, p - wbase);
     }
   };
+  // logical page of entry p; for the ring, after phys_of(p) has set the window
+  auto logical_of = [&](int p) -> int {
+    if (!has_lg) return p;
+    if constexpr (STRAIGHT) return lrow_s[p];
+    else return __builtin_amdgcn_readlane(tl, p - wbase);
+  };
   auto load_page = [&](int p, PageFrag<D>& f) {
     const int64_t base = phys_of(p) * page_stride + head_off;
+    f.lp = logical_of(p);
     const uint16_t* kp = kpool + base + k_lane;
     const uint16_t* vp = vpool + base + v_lane;
 #pragma unroll
@@ -346,6 +362,7 @@ __global__ __launch_bounds__(64) void attn_partial_bf16(PartArgs a) {
   for (int s = 0; s < KS; ++s) buf0.k[s] = buf1.k[s] = buf2.k[s] = buf3.k[s] = make_uint4(0, 0, 0, 0);
 #pragma unroll
   for (int c = 0; c < NC; ++c) buf0.v[c] = buf1.v[c] = buf2.v[c] = buf3.v[c] = make_uint2(0, 0);
+  buf0.lp = buf1.lp = buf2.lp = buf3.lp = 0;
   if constexpr (STRAIGHT) {
     // straight-line: the first pair (the staggered loop requests the next
     // page itself before consuming it)
@@ -360,6 +377,7 @@ __global__ __launch_bounds__(64) void attn_partial_bf16(PartArgs a) {
     auto load_first = [&](int k, PageFrag<D>& f) {
       const int p = min(p0 + k, p1 - 1);
       const int64_t base = (int64_t)__builtin_amdgcn_readlane(tr, p - p0) * page_stride + head_off;
+      f.lp = has_lg ? __builtin_amdgcn_readlane(tl, p - p0) : p;
 #pragma unroll
       for (int s = 0; s < KS; ++s) f.k[s] = *(const uint4*)(kpool + base + k_lane + 32 * s);
 #pragma unroll
@@ -477,7 +495,9 @@ __global__ __launch_bounds__(64) void attn_partial_bf16(PartArgs a) {
         sb[t] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, fb.k[s]), qf,
                                                        sb[t], 0, 0, 0);
       }
+    // length test on the entry index, causal test on the logical position
     const int tok0 = p * kPage + 4 * q4;
+    const int la0 = fa.lp * kPage + 4 * q4, lb0 = fb.lp * kPage + 4 * q4;
     float za[NT][4], zb[NT][4], mx[NT];
 #pragma unroll
     for (int t = 0; t < NT; ++t) {
@@ -485,8 +505,8 @@ __global__ __launch_bounds__(64) void attn_partial_bf16(PartArgs a) {
 #pragma unroll
       for (int j = 0; j < 4; ++j) {
         const int ta = tok0 + j, tb = tok0 + kPage + j;
-        za[t][j] = (ta < len && ta <= qpos[t]) ? sa[t][j] * a.scale_log2 : -INFINITY;
-        zb[t][j] = (hb && tb < len && tb <= qpos[t]) ? sb[t][j] * a.scale_log2 : -INFINITY;
+        za[t][j] = (ta < len && la0 + j <= qpos[t]) ? sa[t][j] * a.scale_log2 : -INFINITY;
+        zb[t][j] = (hb && tb < len && lb0 + j <= qpos[t]) ? sb[t][j] * a.scale_log2 : -INFINITY;
         mx[t] = fmaxf(mx[t], fmaxf(za[t][j], zb[t][j]));
       }
     }
@@ -635,8 +655,10 @@ __global__ __launch_bounds__(64) void attn_partial_f32(PartArgs a) {
 #pragma unroll
     for (int u = 0; u < DPL; ++u) acc[rr][u] = 0.f;
   __syncthreads();
+  const int32_t* ltab = a.logical ? a.logical + (int64_t)(b * a.G + gr) * a.width : nullptr;
   for (int p = p0; p < p1; ++p) {
     const int64_t phys = trow[p];
+    const int lpos0 = (ltab ? ltab[p] : p) * kPage;  // logical position of the page's slot 0
     const float* kp = kpool + (phys * a.Hkv + g) * (int64_t)(kPage * D);
     const float* vp = vpool + (phys * a.Hkv + g) * (int64_t)(D * kPage);
     const int nvalid = min(kPage, len - p * kPage);
@@ -652,7 +674,7 @@ __global__ __launch_bounds__(64) void attn_partial_f32(PartArgs a) {
       const int rr = e / kPage, t = e % kPage;
       const int tok = p * kPage + t;
       float z = -INFINITY;
-      if (tok < len && tok <= s_qpos[rr]) {
+      if (tok < len && lpos0 + t <= s_qpos[rr]) {
         float dot = 0.f;
         for (int d = 0; d < D; ++d) dot += sq[rr][d] * sk[t][d];
         z = dot * a.scale_log2;
@@ -790,6 +812,7 @@ kap_status launch_attention(const AttnCall& c) {
   a.k = c.k;
   a.v = c.v;
   a.table = c.table;
+  a.logical = c.logical;
   a.width = c.width;
   a.G = c.G;
   a.lens = c.lens;

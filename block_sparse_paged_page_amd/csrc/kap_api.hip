@@ -293,7 +293,8 @@ static kap_status attn_common(const void* q, int32_t q_dtype, const int32_t* pos
                               int32_t q_len, float theta, float scale, const void* k_pool,
                               const void* v_pool, int32_t kv_dtype, int32_t num_pages,
                               int32_t Hkv, int32_t D, int32_t page_size, const int32_t* table,
-                              int32_t width, int32_t G, const int32_t* lens, int32_t B,
+                              const int32_t* logical, int32_t width, int32_t G,
+                              const int32_t* lens, int32_t B,
                               int32_t Hq, void* out, float* lse, void* workspace,
                               size_t workspace_bytes, kap_stream stream) {
   if (B < 0 || width < 0 || num_pages < 0)
@@ -329,6 +330,7 @@ static kap_status attn_common(const void* q, int32_t q_dtype, const int32_t* pos
   c.Hkv = Hkv;
   c.D = D;
   c.table = table;
+  c.logical = logical;
   c.width = width;
   c.G = G;
   c.lens = lens;
@@ -344,23 +346,23 @@ static kap_status attn_common(const void* q, int32_t q_dtype, const int32_t* pos
 kap_status kap_decode_attn(const void* q, int32_t q_dtype, const int32_t* positions,
                            float rope_theta, float scale, const void* k_pool, const void* v_pool,
                            int32_t kv_dtype, int32_t num_pages, int32_t Hkv, int32_t D,
-                           int32_t page_size, const int32_t* block_table, int32_t table_width,
-                           int32_t G, const int32_t* lens, int32_t B, int32_t Hq, void* out,
-                           float* lse, void* workspace, size_t workspace_bytes,
-                           kap_stream stream) {
+                           int32_t page_size, const int32_t* block_table,
+                           const int32_t* logical_table, int32_t table_width, int32_t G,
+                           const int32_t* lens, int32_t B, int32_t Hq, void* out, float* lse,
+                           void* workspace, size_t workspace_bytes, kap_stream stream) {
   g_err[0] = 0;
   return attn_common(q, q_dtype, positions, 1, rope_theta, scale, k_pool, v_pool, kv_dtype,
-                     num_pages, Hkv, D, page_size, block_table, table_width, G, lens, B, Hq, out,
-                     lse, workspace, workspace_bytes, stream);
+                     num_pages, Hkv, D, page_size, block_table, logical_table, table_width, G,
+                     lens, B, Hq, out, lse, workspace, workspace_bytes, stream);
 }
 
 kap_status kap_decode_attn_noalloc(const void* q, int32_t q_dtype, const int32_t* positions,
                                    float rope_theta, float scale, const void* k_pool,
                                    const void* v_pool, int32_t kv_dtype, int32_t num_pages,
                                    int32_t Hkv, int32_t D, int32_t page_size,
-                                   const int32_t* block_table, int32_t table_width, int32_t G,
-                                   const int32_t* lens, int32_t B, int32_t Hq, void* out,
-                                   float* lse, kap_stream stream) {
+                                   const int32_t* block_table, const int32_t* logical_table,
+                                   int32_t table_width, int32_t G, const int32_t* lens, int32_t B,
+                                   int32_t Hq, void* out, float* lse, kap_stream stream) {
   g_err[0] = 0;
   // size check first, before any HIP call
   if (B > 0 && Hq > 0 && Hkv > 0 && Hq % Hkv == 0) {
@@ -373,8 +375,8 @@ kap_status kap_decode_attn_noalloc(const void* q, int32_t q_dtype, const int32_t
   }
   if (B <= 0) {  // nothing to launch; validate the rest as kap_decode_attn does
     return attn_common(q, q_dtype, positions, 1, rope_theta, scale, k_pool, v_pool, kv_dtype,
-                       num_pages, Hkv, D, page_size, block_table, table_width, G, lens, B, Hq,
-                       out, lse, nullptr, 0, stream);
+                       num_pages, Hkv, D, page_size, block_table, logical_table, table_width, G,
+                       lens, B, Hq, out, lse, nullptr, 0, stream);
   }
   int dev = 0;
   const hipError_t e = hipGetDevice(&dev);
@@ -384,8 +386,8 @@ kap_status kap_decode_attn_noalloc(const void* q, int32_t q_dtype, const int32_t
   void* ws = scratch_address(dev);
   if (!ws) return KAP_ERR_HIP;
   return attn_common(q, q_dtype, positions, 1, rope_theta, scale, k_pool, v_pool, kv_dtype,
-                     num_pages, Hkv, D, page_size, block_table, table_width, G, lens, B, Hq, out,
-                     lse, ws, (size_t)KAP_NOALLOC_SCRATCH_BYTES, stream);
+                     num_pages, Hkv, D, page_size, block_table, logical_table, table_width, G,
+                     lens, B, Hq, out, lse, ws, (size_t)KAP_NOALLOC_SCRATCH_BYTES, stream);
 }
 
 kap_status kap_verify_attn(const void* q, int32_t q_dtype, const int32_t* start_positions,
@@ -397,8 +399,8 @@ kap_status kap_verify_attn(const void* q, int32_t q_dtype, const int32_t* start_
                            kap_stream stream) {
   g_err[0] = 0;
   return attn_common(q, q_dtype, start_positions, q_len, rope_theta, scale, k_pool, v_pool,
-                     kv_dtype, num_pages, Hkv, D, page_size, block_table, max_pages, 1, seq_lens,
-                     B, Hq, out, lse, workspace, workspace_bytes, stream);
+                     kv_dtype, num_pages, Hkv, D, page_size, block_table, nullptr, max_pages, 1,
+                     seq_lens, B, Hq, out, lse, workspace, workspace_bytes, stream);
 }
 
 kap_status kap_build_summary(const void* k_pool, int32_t kv_dtype, int32_t num_pages,

@@ -35,6 +35,7 @@ struct AttnCall {
   const void* v;
   int32_t Hkv, D;
   const int32_t* table;
+  const int32_t* logical;  // logical page per table entry, or null (entry j is page j)
   int32_t width, G;
   const int32_t* lens;
   int32_t B, Hq;

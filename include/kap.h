@@ -232,31 +232,43 @@ KAP_API size_t kap_attn_workspace_bytes(int32_t B, int32_t q_len, int32_t Hq, in
  * q = 1 GQA decode attention over a paged view ([KAP] executor: each proposal
  * step is a decode-like forward with one query token at its full-sequence
  * logical position, over the compact block table and compact metadata).
- * For request b and query head h (KV head g = g(h), table row gr = G == 1 ? 0 : g):
- *   keys   = the first lens[b][gr] tokens of table row (b, gr): token t lives at
- *            page block_table[(b*G + gr)*table_width + t/16], slot t%16
+ * For request b and query head h (KV head g = g(h), table row gr = G == 1 ? 0 : g),
+ * with j = (b*G + gr)*table_width + t/16:
+ *   view   = the first lens[b][gr] tokens of table row (b, gr): token t lives at
+ *            page block_table[j], slot t%16, and sits at logical position
+ *            lambda(t) = logical_table[j]*16 + t%16 (lambda(t) = t when
+ *            logical_table is NULL: a full block table, entry p = logical page p)
+ *   keys   = the tokens t of the view with lambda(t) <= positions[b] (logical
+ *            positions are kept in the compact view, [KAP] selected-KV view, so
+ *            the causal rule is the full-context one)
  *   z_t    = scale * RoPE(q[b][h], positions[b]) . K(t)
  *   out    = sum_t e^{z_t - m} V(t) / sum_t e^{z_t - m};  lse = m + ln sum_t e^{z_t - m}
  * Work is split over page chunks (split-K) and merged with a log-sum-exp
- * combine in fixed order.  Use (block_table, max_pages, G = 1, seq_lens) for
- * full-context decode and (compact_bt, capacity, G, compact_len) for the
- * selected view.  A row with no key yields out = 0 and lse = -inf.
+ * combine in fixed order.  Use (block_table, NULL, max_pages, G = 1, seq_lens)
+ * for full-context decode and (compact_bt, compact_logical, capacity, G,
+ * compact_len) for the selected view.  A row with no key yields out = 0 and
+ * lse = -inf.
+ * The view holds the context only: tokens proposed after positions[b] are not
+ * in a compact view built over seq_lens, so proposal step j > 0 does not see
+ * the drafts of steps 0 .. j-1 (their KV is written by kap_append_kv before
+ * the verify, which reads the full table).
  * Precision: bf16 K/V run on the matrix cores with the rotated query and the
  * probabilities rounded to bf16 and fp32 accumulation, softmax and merge;
  * fp32 K/V run in fp32 throughout.
  *   q        device [B][Hq][D], q_dtype; out device [B][Hq][D], same dtype as q
  *   lse      device out [B][Hq] float, natural log, or NULL
  *   k_pool, v_pool device, kv_dtype, layouts above; q_dtype must equal kv_dtype
+ *   logical_table device [B][G][table_width] int32 or NULL (see above)
  *   lens     device [B][G] int32 (lens <= 16 * table_width)
  *   workspace device, >= kap_attn_workspace_bytes(B, 1, Hq, Hkv, D)
  */
 KAP_API kap_status kap_decode_attn(const void* q, int32_t q_dtype, const int32_t* positions,
                            float rope_theta, float scale, const void* k_pool, const void* v_pool,
                            int32_t kv_dtype, int32_t num_pages, int32_t Hkv, int32_t D,
-                           int32_t page_size, const int32_t* block_table, int32_t table_width,
-                           int32_t G, const int32_t* lens, int32_t B, int32_t Hq, void* out,
-                           float* lse, void* workspace, size_t workspace_bytes,
-                           kap_stream stream);
+                           int32_t page_size, const int32_t* block_table,
+                           const int32_t* logical_table, int32_t table_width, int32_t G,
+                           const int32_t* lens, int32_t B, int32_t Hq, void* out, float* lse,
+                           void* workspace, size_t workspace_bytes, kap_stream stream);
 
 /*
  * Allocation-free variant of kap_decode_attn, for callers that cannot
@@ -280,7 +292,8 @@ KAP_API kap_status kap_decode_attn_noalloc(const void* q, int32_t q_dtype,
                                            float scale, const void* k_pool, const void* v_pool,
                                            int32_t kv_dtype, int32_t num_pages, int32_t Hkv,
                                            int32_t D, int32_t page_size,
-                                           const int32_t* block_table, int32_t table_width,
+                                           const int32_t* block_table,
+                                           const int32_t* logical_table, int32_t table_width,
                                            int32_t G, const int32_t* lens, int32_t B, int32_t Hq,
                                            void* out, float* lse, kap_stream stream);
 

@@ -158,7 +158,7 @@ def _attn(lib, fn, **kw):
     if fn == "decode":
         return lib.kap_decode_attn(a["q"], a["q_dtype"], a["pos"], a["theta"], a["scale"], a["k"],
                                    a["v"], a["kv_dtype"], a["num_pages"], a["Hkv"], a["D"],
-                                   a["page_size"], a["table"], a["width"], a["G"], a["lens"],
+                                   a["page_size"], a["table"], None, a["width"], a["G"], a["lens"],
                                    a["B"], a["Hq"], a["out"], a["lse"], a["ws"], a["ws_bytes"],
                                    None)
     return lib.kap_verify_attn(a["q"], a["q_dtype"], a["pos"], a["q_len"], a["theta"], a["scale"],
@@ -247,8 +247,8 @@ def test_noalloc_decode_rejects_oversize_before_any_hip_call(lib):
     cap = int(m.group(1)) << int(m.group(2))
     B, Hq, Hkv, D = 512, 128, 8, 128
     assert kap.attn_workspace_bytes(B, 1, Hq, Hkv, D) > cap
-    st = lib.kap_decode_attn_noalloc(NP, 1, NP, 1e4, 0.088, NP, NP, 1, 100, Hkv, D, 16, NP, 64, 1,
-                                     NP, B, Hq, NP, None, None)
+    st = lib.kap_decode_attn_noalloc(NP, 1, NP, 1e4, 0.088, NP, NP, 1, 100, Hkv, D, 16, NP, None,
+                                     64, 1, NP, B, Hq, NP, None, None)
     assert st == WORKSPACE
     assert b"scratch" in lib.kap_last_error()
     assert kap.attn_workspace_bytes(4, 1, 64, 8, 128) <= cap   # the 128K, B = 4 decode fits

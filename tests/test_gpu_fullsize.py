@@ -176,7 +176,8 @@ def _attention(big, sel_ref, cnt_ref, cv, samples):
     ws = torch.empty(kap.attn_workspace_bytes(w.B, w.q_len, w.Hq, w.Hkv, w.D), dtype=torch.uint8,
                      device="cuda")
     lse = torch.empty((w.B, w.Hq), dtype=torch.float32, device="cuda")
-    out = kap.decode_attn(big.q, big.pos, big.K, big.V, cbt, clen, G=G, lse=lse, workspace=ws)
+    out = kap.decode_attn(big.q, big.pos, big.K, big.V, cbt, clen, G=G, lse=lse, workspace=ws,
+                          logical=clog)
     torch.cuda.synchronize()
     keys_sel = oracle.keys_selected(sel_ref, cnt_ref, b["seq_lens"])
     e1 = _check_rows(big, out, lse, samples,

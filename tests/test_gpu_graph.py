@@ -52,7 +52,7 @@ class Cycle:
                         sel=self.sel, cnt=self.cnt)
         kap.compact_view(self.sel, self.cnt, c.bt, c.L, c.pos, 1, out=self.cv)
         kap.decode_attn(self.q, c.pos, c.K, c.V, self.cv[0], self.cv[2], out=self.out,
-                        lse=self.lse, workspace=self.ws)
+                        lse=self.lse, workspace=self.ws, logical=self.cv[1])
         kap.verify_attn(self.qv, c.pos, c.K, c.V, c.bt, c.L, out=self.vout, lse=self.vlse,
                         workspace=self.ws)
 

@@ -33,7 +33,7 @@ def test_host_routed_decode_matches_oracle():
     np.testing.assert_array_equal(cnt, cnt_ref)
     # upload the indices; the GPU compacts and decodes with the real query
     cbt, clog, clen, _ = kap.compact_view(t(sel), t(cnt), c.bt, c.L, c.pos, 1)
-    out = kap.decode_attn(c.q, c.pos, c.K, c.V, cbt, clen, G=w.Hkv)
+    out = kap.decode_attn(c.q, c.pos, c.K, c.V, cbt, clen, G=w.Hkv, logical=clog)
     torch.cuda.synchronize()
     keys = oracle.keys_selected(sel_ref, cnt_ref, b["seq_lens"])
     ref, _ = oracle.attend(b["q"][:, None], b["positions"], c.Kl, c.Vl, c.btl, keys, w.Hkv, w.Hkv)

@@ -76,8 +76,8 @@ def test_decode_over_workspace_is_bit_identical(name):
     k_ws, v_ws, tab = kap.materialize_view(c.K, c.V, cbt)
     lse1 = torch.empty((w.B, w.Hq), dtype=torch.float32, device="cuda")
     lse2 = torch.empty_like(lse1)
-    o_pool = kap.decode_attn(c.q, c.pos, c.K, c.V, cbt, clen, G=G, lse=lse1)
-    o_ws = kap.decode_attn(c.q, c.pos, k_ws, v_ws, tab, clen, G=G, lse=lse2)
+    o_pool = kap.decode_attn(c.q, c.pos, c.K, c.V, cbt, clen, G=G, lse=lse1, logical=clog)
+    o_ws = kap.decode_attn(c.q, c.pos, k_ws, v_ws, tab, clen, G=G, lse=lse2, logical=clog)
     torch.cuda.synchronize()
     assert torch.equal(o_pool, o_ws) and torch.equal(lse1, lse2)
     # and both are the oracle's selected-KV decode
@@ -99,7 +99,7 @@ def test_workspace_reuse_across_plans():
     sel2 = np.where(np.arange(sel.shape[2])[None, None, :] < half[:, :, None], sel, -1).astype(np.int32)
     cv2 = kap.compact_view(t(sel2), t(half), c.bt, c.L, c.pos, 1)
     k_ws, v_ws, tab2 = kap.materialize_view(c.K, c.V, cv2[0], k_ws, v_ws)
-    o_pool = kap.decode_attn(c.q, c.pos, c.K, c.V, cv2[0], cv2[2])
-    o_ws = kap.decode_attn(c.q, c.pos, k_ws, v_ws, tab2, cv2[2])
+    o_pool = kap.decode_attn(c.q, c.pos, c.K, c.V, cv2[0], cv2[2], logical=cv2[1])
+    o_ws = kap.decode_attn(c.q, c.pos, k_ws, v_ws, tab2, cv2[2], logical=cv2[1])
     torch.cuda.synchronize()
     assert torch.equal(o_pool, o_ws)

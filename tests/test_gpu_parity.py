@@ -175,12 +175,43 @@ def test_selected_decode_parity(name):
     cbt, clog, clen, slot = kap.compact_view(t(sel_ref), t(cnt_ref), c.bt, c.L, c.pos, 1)
     G = w.Hkv if w.per_head else 1
     lse = torch.empty((w.B, w.Hq), dtype=torch.float32, device="cuda")
-    out = kap.decode_attn(c.q, c.pos, c.K, c.V, cbt, clen, G=G, lse=lse)
+    out = kap.decode_attn(c.q, c.pos, c.K, c.V, cbt, clen, G=G, lse=lse, logical=clog)
     torch.cuda.synchronize()
     keys = oracle.keys_selected(sel_ref, cnt_ref, c.b["seq_lens"])
     ref, lref = oracle.attend(c.b["q"][:, None], c.b["positions"], c.Kl, c.Vl, c.btl, keys, G, w.Hkv)
     err = _check_attn(c, out, lse, ref[:, 0], lref[:, 0])
     print(f"[{name}] selected decode max rel err {err:.2e}", flush=True)
+
+
+@pytest.mark.parametrize("name,per_head", [("tiny", False), ("llama", False), ("llama", True),
+                                           ("qwen", False), ("mixed", False)])
+def test_selected_decode_position_inside_context(name, per_head):
+    """The decode's causal rule is on logical positions (the compact view keeps
+    them): with the query placed inside the context, selected pages past it
+    (the recent pages, the later middle picks) must be hidden exactly as the
+    oracle hides them over the selected keys, although their compact indices
+    are below the query position.  The rotation is at the same position."""
+    c = get_case(name)
+    w = c.w
+    b = c.b
+    cap = c.budget() + 3
+    s_ref = oracle.score(b["q"], b["positions"], c.summ_l, c.btl, b["seq_lens"], w.Hkv)
+    sel_ref, cnt_ref = oracle.select(s_ref.astype(np.float32), b["seq_lens"], b["anchor"],
+                                     b["recent"], c.k_mid_h, cap, per_head=per_head)
+    cbt, clog, clen, _ = kap.compact_view(t(sel_ref), t(cnt_ref), c.bt, c.L, c.pos, 1)
+    G = w.Hkv if per_head else 1
+    pin = np.maximum(b["seq_lens"].astype(np.int64) * 2 // 3 - 3, 1).astype(np.int32)
+    keys = oracle.keys_selected(sel_ref, cnt_ref, b["seq_lens"])
+    hidden = [int((k > pin[i // G]).sum()) for i, k in enumerate(keys)]
+    shown = [int((k <= pin[i // G]).sum()) for i, k in enumerate(keys)]
+    assert min(hidden) > 0 and min(shown) > 0, (hidden, shown)
+    lse = torch.empty((w.B, w.Hq), dtype=torch.float32, device="cuda")
+    out = kap.decode_attn(c.q, t(pin), c.K, c.V, cbt, clen, G=G, lse=lse, logical=clog)
+    torch.cuda.synchronize()
+    ref, lref = oracle.attend(b["q"][:, None], pin, c.Kl, c.Vl, c.btl, keys, G, w.Hkv)
+    err = _check_attn(c, out, lse, ref[:, 0], lref[:, 0])
+    print(f"[{name}, per_head={per_head}] decode inside the context: hidden keys per row "
+          f"{min(hidden)}..{max(hidden)}, max rel err {err:.2e}", flush=True)
 
 
 @pytest.mark.parametrize("name", list(CASES))
@@ -221,7 +252,7 @@ def test_gpu_chain_end_to_end(name):
     _, sel_ref, cnt_ref = _oracle_chain(c, cap)
     _, sel, cnt = _gpu_chain(c, cap)
     cbt, clog, clen, slot = kap.compact_view(sel, cnt, c.bt, c.L, c.pos, 1)
-    out = kap.decode_attn(c.q, c.pos, c.K, c.V, cbt, clen, G=1)
+    out = kap.decode_attn(c.q, c.pos, c.K, c.V, cbt, clen, G=1, logical=clog)
     torch.cuda.synchronize()
     keys = oracle.keys_selected(sel_ref, cnt_ref, c.b["seq_lens"])
     ref, _ = oracle.attend(c.b["q"][:, None], c.b["positions"], c.Kl, c.Vl, c.btl, keys, 1, w.Hkv)
@@ -289,6 +320,20 @@ def test_long_ragged_items(q_len, D):
                                     oracle.keys_full(c.b["seq_lens"]), 1, w.Hkv)
         err1 = _check_attn(c, out1, lse1, ref1[:, 0], lref1[:, 0])
         print(f"[long items] full decode max rel err {err1:.2e}", flush=True)
+        # the long-item discipline with a logical table (here the identity, so
+        # bit-identical to no table) and the query inside the context
+        width = c.b["bt"].shape[1]
+        ident = t(np.tile(np.arange(width, dtype=np.int32), (w.B, 1)))
+        pin = (c.b["positions"].astype(np.int64) * 3 // 5 + 7).astype(np.int32)
+        lse2, lse3 = (torch.empty((w.B, w.Hq), dtype=torch.float32, device="cuda") for _ in range(2))
+        out2 = kap.decode_attn(c.q, t(pin), c.K, c.V, c.bt, c.L, G=1, lse=lse2, logical=ident)
+        out3 = kap.decode_attn(c.q, t(pin), c.K, c.V, c.bt, c.L, G=1, lse=lse3)
+        torch.cuda.synchronize()
+        assert torch.equal(out2, out3) and torch.equal(lse2, lse3)
+        ref2, lref2 = oracle.attend(c.b["q"][:, None], pin, c.Kl, c.Vl, c.btl,
+                                    oracle.keys_full(c.b["seq_lens"]), 1, w.Hkv)
+        err2 = _check_attn(c, out2, lse2, ref2[:, 0], lref2[:, 0])
+        print(f"[long items] decode inside the context max rel err {err2:.2e}", flush=True)
     _long_cache.clear()
 
 
@@ -323,9 +368,9 @@ def test_head_layouts(Hq, Hkv, D, dtype):
                                      c.b["recent"], c.k_mid_h, cap)
     sel, cnt = kap.select_topk(t(s_ref.astype(np.float32)), c.L, c.anchor, c.recent, c.k_mid, cap,
                                cap)
-    cbt, _, clen, _ = kap.compact_view(sel, cnt, c.bt, c.L, c.pos, 1)
+    cbt, clog, clen, _ = kap.compact_view(sel, cnt, c.bt, c.L, c.pos, 1)
     lse = torch.empty((w.B, w.Hq), dtype=torch.float32, device="cuda")
-    out = kap.decode_attn(c.q, c.pos, c.K, c.V, cbt, clen, lse=lse)
+    out = kap.decode_attn(c.q, c.pos, c.K, c.V, cbt, clen, lse=lse, logical=clog)
     start = np.maximum(c.b["positions"] - 9, 0).astype(np.int32)
     vlse = torch.empty((w.B, w.q_len, w.Hq), dtype=torch.float32, device="cuda")
     vout = kap.verify_attn(c.qv, t(start), c.K, c.V, c.bt, c.L, lse=vlse)
@@ -363,7 +408,7 @@ def test_full_selection_is_bit_identical_to_full_decode():
     sel, cnt = kap.select_topk(kap.score_blocks(c.q, c.pos, c.S, c.bt, c.L, w.Hkv), c.L, c.anchor,
                                c.recent, kall, cap, cap)
     cbt, clog, clen, _ = kap.compact_view(sel, cnt, c.bt, c.L, c.pos, 1)
-    o_sel = kap.decode_attn(c.q, c.pos, c.K, c.V, cbt, clen)
+    o_sel = kap.decode_attn(c.q, c.pos, c.K, c.V, cbt, clen, logical=clog)
     o_full = kap.decode_attn(c.q, c.pos, c.K, c.V, c.bt, c.L)
     torch.cuda.synchronize()
     assert np.array_equal(clen.cpu().numpy()[:, 0], c.b["seq_lens"])
@@ -480,7 +525,7 @@ def test_attention_at_the_row_limit():
     cap = c.budget()
     _, sel_ref, cnt_ref = _oracle_chain(c, cap)
     cbt, clog, clen, slot = kap.compact_view(t(sel_ref), t(cnt_ref), c.bt, c.L, c.pos, 1)
-    out = kap.decode_attn(c.q, c.pos, c.K, c.V, cbt, clen, G=w.Hkv, lse=lse)
+    out = kap.decode_attn(c.q, c.pos, c.K, c.V, cbt, clen, G=w.Hkv, lse=lse, logical=clog)
     torch.cuda.synchronize()
     keys = oracle.keys_selected(sel_ref, cnt_ref, b["seq_lens"])
     ref, lref = oracle.attend(b["q"][:, None], b["positions"], c.Kl, c.Vl, c.btl, keys, w.Hkv, w.Hkv)
@@ -606,7 +651,7 @@ def test_proxy_query_and_per_head_routing():
     torch.cuda.synchronize()
     np.testing.assert_array_equal(sel.cpu().numpy(), sel_ref)
     cbt, clog, clen, _ = kap.compact_view(sel, cnt, c.bt, c.L, c.pos, 1)
-    out = kap.decode_attn(c.q, c.pos, c.K, c.V, cbt, clen, G=w.Hkv)
+    out = kap.decode_attn(c.q, c.pos, c.K, c.V, cbt, clen, G=w.Hkv, logical=clog)
     torch.cuda.synchronize()
     keys = oracle.keys_selected(sel_ref, cnt_ref, c.b["seq_lens"])
     ref, _ = oracle.attend(c.b["q"][:, None], c.b["positions"], c.Kl, c.Vl, c.btl, keys, w.Hkv,
