@@ -41,6 +41,8 @@ _SIGS = {
     "kap_select_compact": ([_P, _I32, _I32, _I32, _P, _I32, _I32, _P, _P, _P, _I32, _I32, _P, _P,
                             _I32, _P, _P, _P, _P, _P, _P], _I32),
     "kap_budget_from_ratio": ([_I32, _I64, _I64, _I32, _I32], _I32),
+    "kap_choose_plan": ([ctypes.c_double, ctypes.c_double, ctypes.c_double, ctypes.c_double, _I32,
+                         _I32, _I32, _P, _P], _I32),
     "kap_compact_view": ([_P, _P, _I32, _I32, _I32, _P, _I32, _P, _I32, _P, _I32, _P, _P, _P, _P,
                           _P], _I32),
     "kap_attn_workspace_bytes": ([_I32, _I32, _I32, _I32, _I32], _SZ),
@@ -128,6 +130,20 @@ def proxy_workspace_bytes(B, d_model, n_out) -> int:
 
 def budget_from_ratio(n_pages, s_num, s_den, anchor, recent) -> int:
     return int(load().kap_budget_from_ratio(n_pages, s_num, s_den, anchor, recent))
+
+
+PLAN_SELECTED, PLAN_FULL_CAPACITY, PLAN_FULL_MARGIN, PLAN_FULL_BOUNDARY = 0, 1, 2, 3
+
+
+def choose_plan(h, s, w_main_bytes, kv_bytes, k, budget_pages, capacity):
+    """kap_choose_plan -> (choice, modeled cycle speedup Cost_base / Cost_plan)."""
+    choice = ctypes.c_int32(-1)
+    speedup = ctypes.c_double(0.0)
+    st = load().kap_choose_plan(float(h), float(s), float(w_main_bytes), float(kv_bytes), int(k),
+                                int(budget_pages), int(capacity), ctypes.byref(choice),
+                                ctypes.byref(speedup))
+    _check(st, "kap_choose_plan")
+    return choice.value, speedup.value
 
 
 def score_blocks(q, positions, summary, block_table, seq_lens, Hkv, theta=1e4, scores=None,

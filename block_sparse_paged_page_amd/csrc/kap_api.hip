@@ -230,6 +230,29 @@ int32_t kap_budget_from_ratio(int32_t n_pages, int64_t s_num, int64_t s_den, int
   return (int32_t)budget;
 }
 
+kap_status kap_choose_plan(double h, double s, double w_main_bytes, double kv_bytes, int32_t k,
+                           int32_t budget_pages, int32_t capacity, int32_t* choice,
+                           double* speedup) {
+  g_err[0] = 0;
+  // written so that NaN fails every range test
+  if (!(h >= 0.0 && h <= 1.0) || !(s >= 0.0 && s <= 1.0))
+    return fail(KAP_ERR_INVALID_ARG, "h=%g s=%g (both in [0, 1])", h, s);
+  if (!(w_main_bytes >= 0.0) || !(kv_bytes >= 0.0) || w_main_bytes + kv_bytes == INFINITY)
+    return fail(KAP_ERR_INVALID_ARG, "byte counts W_main=%g KV=%g (finite, >= 0)", w_main_bytes,
+                kv_bytes);
+  if (k < 1 || budget_pages < 0 || capacity < 0)
+    return fail(KAP_ERR_INVALID_ARG, "k=%d budget=%d capacity=%d", k, budget_pages, capacity);
+  if (!choice) return fail(KAP_ERR_INVALID_ARG, "null pointer");
+  const double base = (1.0 + k * h) * (w_main_bytes + kv_bytes);
+  const double plan = k * (w_main_bytes + s * kv_bytes) + (w_main_bytes + kv_bytes);
+  if (speedup) *speedup = plan > 0.0 ? base / plan : 1.0;
+  if (budget_pages > capacity) *choice = KAP_PLAN_FULL_CAPACITY;
+  else if (!(h > s)) *choice = KAP_PLAN_FULL_MARGIN;
+  else if (!((h - s) * kv_bytes > (1.0 - h) * w_main_bytes)) *choice = KAP_PLAN_FULL_BOUNDARY;
+  else *choice = KAP_PLAN_SELECTED;
+  return KAP_OK;
+}
+
 kap_status kap_select_compact(const float* scores, int32_t B, int32_t Hkv, int32_t max_pages,
                               const int32_t* seq_lens, int32_t page_size, int32_t per_head,
                               const int32_t* anchor, const int32_t* recent,

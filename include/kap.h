@@ -170,6 +170,40 @@ KAP_API kap_status kap_select_topk(const float* scores, int32_t B, int32_t Hkv, 
                            int32_t max_budget, int32_t capacity, int32_t* sel_pages,
                            int32_t* sel_count, kap_stream stream);
 
+/*
+ * Host helper: keep the selected-KV plan or fall back to full-context decoding.
+ * [KAP] stability/fallback paragraph: the plan falls back to full context when
+ * it exceeds the compact workspace, or when the retained ratio s is high or the
+ * acceptance h low; [KAP-T] (the tutorial's phase-boundary section) makes the
+ * second condition exact under the memory-bound cost model of one cycle of k
+ * proposal steps and one verification:
+ *   Cost_base = (1 + k h) (W_main + KV),  Cost_plan = k (W_main + s KV) + (W_main + KV)
+ * (proposal weights = main weights), and Cost_plan < Cost_base  <=>
+ *   (h - s) KV > (1 - h) W_main.
+ *   h             acceptance rate of proposed tokens, in [0, 1]
+ *   s             retained ratio: bytes a proposal step reads / bytes a
+ *                 full-context step reads, in [0, 1]
+ *   w_main_bytes  per-step weight (and other non-KV) bytes of the main model, >= 0
+ *   kv_bytes      per-step full-context KV bytes, >= 0
+ *   k             proposal steps per cycle, >= 1
+ *   budget_pages  largest selection budget of the batch (a + r + k pages);
+ *   capacity      compact capacity in pages
+ *   choice        out: KAP_PLAN_SELECTED, or the first fallback reason in the
+ *                 order capacity, margin (h <= s), boundary
+ *   speedup       out (may be NULL): Cost_base / Cost_plan of the cycle (> 1
+ *                 exactly when the boundary holds); computed for every choice
+ * Returns KAP_ERR_INVALID_ARG for values outside these ranges (NaN included).
+ */
+typedef enum {
+  KAP_PLAN_SELECTED = 0,       /* keep the selected-KV plan                       */
+  KAP_PLAN_FULL_CAPACITY = 1,  /* budget_pages > capacity                          */
+  KAP_PLAN_FULL_MARGIN = 2,    /* h <= s: the plan cannot pay off at any KV size   */
+  KAP_PLAN_FULL_BOUNDARY = 3   /* (h - s) KV <= (1 - h) W_main                     */
+} kap_plan_choice;
+KAP_API kap_status kap_choose_plan(double h, double s, double w_main_bytes, double kv_bytes,
+                                   int32_t k, int32_t budget_pages, int32_t capacity,
+                                   int32_t* choice, double* speedup);
+
 /* Host helper: page budget for retention s = s_num/s_den over n_pages pages,
  * ceil(n_pages * s) in integers, raised to anchor + recent, capped at n_pages.
  * The middle count is budget - anchor - recent.  Returns -1 on bad input. */
