@@ -48,6 +48,8 @@ def parse():
     ap.add_argument("--batch", type=int, default=4)
     ap.add_argument("--layers", type=int, default=0, help="layer copies (0: auto)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-extras", action="store_true",
+                    help="skip the Llama-shaped 32K, mixed-serving and retention-fit legs of the default line")
     ap.add_argument("--graph", action="store_true",
                     help="replay each call of the cycle from its own HIP graph (default: launch "
                          "from Python; on this stack a graph launch adds ~7 us per call)")
@@ -195,13 +197,68 @@ def _upload(b, dev):
     return to
 
 
+def needle_recall(b, sel_h, cnt_h, k_mid):
+    """Needle pages (aimed at the rotated query, drawn from the middle region)
+    that the GPU selection picked, over what the middle budget k_mid allows:
+    hits / min(needles, k_mid) per request, [min, mean] over the requests whose
+    budget allows any."""
+    r = []
+    for bi, pages in enumerate(b["needle_pages"]):
+        room = min(len(pages), int(k_mid[bi]))
+        if room == 0:
+            continue
+        chosen = set(sel_h[bi, :cnt_h[bi]].tolist())
+        r.append(sum(int(p) in chosen for p in pages) / room)
+    return {"min": round(min(r), 4), "mean": round(float(np.mean(r)), 4),
+            "requests": len(r)} if r else None
+
+
+def retention_sweep(q, pos, bt, L, anchor, recent, scores, Ks, Vs, ws, out, N, B, kv_tok, steps,
+                    st):
+    """Selected decode over retention s in {1, 2, 5.5, 10, 25, 50, 100} % (A1R2,
+    pooled top-K on `scores`), each call on the next layer copy, plus the
+    full-table decode; a linear fit T(s) = T0 + s T_full."""
+    R = len(Ks)
+    cnt_l = {"i": 0}
+
+    def lay():
+        cnt_l["i"] += 1
+        return cnt_l["i"] % R
+
+    sweep = []
+    for num, den in ((1, 100), (2, 100), (55, 1000), (10, 100), (25, 100), (50, 100), (1, 1)):
+        bud = kap.budget_from_ratio(N, num, den, 1, 2)
+        km = torch.full((B,), bud - 3, dtype=torch.int32, device=q.device)
+        sl, ct = kap.select_topk(scores, L, anchor, recent, km, bud, bud)
+        cb = kap.compact_view(sl, ct, bt, L, pos, 1)
+        us = time_call(lambda: kap.decode_attn(q, pos, Ks[lay()], Vs[lay()], cb[0], cb[2], out=out,
+                                               workspace=ws, logical=cb[1]), steps, st)
+        nbytes = B * bud * 16 * kv_tok
+        sweep.append({"s": round(num / den, 4), "pages": bud, "us": round(us, 2),
+                      "GBps": round(nbytes / (us * 1e-6) / 1e9, 1)})
+    full_us = time_call(lambda: kap.decode_attn(q, pos, Ks[lay()], Vs[lay()], bt, L, out=out,
+                                                workspace=ws), steps, st)
+    xs = np.array([d["pages"] / N for d in sweep])
+    ys = np.array([d["us"] for d in sweep])
+    A = np.stack([np.ones_like(xs), xs], axis=1)
+    coef, *_ = np.linalg.lstsq(A, ys, rcond=None)
+    pred = A @ coef
+    r2 = 1 - ((ys - pred) ** 2).sum() / ((ys - ys.mean()) ** 2).sum()
+    fit = {"T0_us": round(float(coef[0]), 2), "T_full_us": round(float(coef[1]), 2),
+           "r2": round(float(r2), 5), "T(100%)/T(full table)": round(float(ys[-1] / full_us), 4)}
+    return sweep, full_us, fit
+
+
 def run_llama_sweep(args, dev):
     """Llama-3-8B-shaped attention at 32K, batch 8: every routing call, the
     selected (s = 113/2048) and full decodes, and decode time across retention
     s in {1, 2, 5.5, 10, 25, 50, 100} % with a linear fit T(s) = T0 + s T1."""
     w = W.spec("llama8b_32k")
-    _sweep(args, dev, w, "llama8b_32k: B=8, Hq=32, Hkv=8, D=128, 32768-token context, "
-           "s=113/2048 (A1R2K110 pooled)")
+    print(json.dumps(_sweep(args, dev, w, LLAMA_LABEL)), flush=True)
+
+
+LLAMA_LABEL = ("llama8b_32k: B=8, Hq=32, Hkv=8, D=128, 32768-token context, s=113/2048 "
+               "(A1R2K110 pooled), needles aimed at the rotated query")
 
 
 def run_qwen_sweep(args, dev):
@@ -209,14 +266,16 @@ def run_qwen_sweep(args, dev):
     (s = 451/8192) and full decodes, and the same retention sweep and fit."""
     for B in (1, 2, 4):
         w = W.spec("qwen32b_128k", B=B)
-        _sweep(args, dev, w, f"qwen32b_128k: B={B}, Hq=64, Hkv=8, D=128, 131072-token context, "
-               "s=451/8192 (A1R2K448 pooled)")
+        print(json.dumps(_sweep(args, dev, w, f"qwen32b_128k: B={B}, Hq=64, Hkv=8, D=128, "
+                                "131072-token context, s=451/8192 (A1R2K448 pooled)")), flush=True)
         torch.cuda.empty_cache()
 
 
 def _sweep(args, dev, w, label):
+    """Routing calls, the selected and full decodes, and the retention sweep of
+    one uniform-length workload; returns the result line as a dict."""
     B, Hq, Hkv, D = w.B, w.Hq, w.Hkv, w.D
-    b = W.make_device(w, dev)
+    b = W.make_device(w, dev, needle_dir=W.aimed_dirs(w))
     to = _upload(b, dev)
     bt, L, pos = to(b["bt"]), to(b["seq_lens"]), to(b["positions"])
     anchor, recent = to(b["anchor"]), to(b["recent"])
@@ -264,37 +323,21 @@ def _sweep(args, dev, w, label):
         lambda: kap.select_compact(pooled, L, anchor, recent, kmid, budget, budget, bt, pos, 1,
                                    cnt=cnt, out=cv), args.steps, st)
     kv_tok = Hkv * 2 * D * EB
-    sweep = []
-    for num, den in ((1, 100), (2, 100), (55, 1000), (10, 100), (25, 100), (50, 100), (1, 1)):
-        bud = kap.budget_from_ratio(N, num, den, 1, 2)
-        km = torch.full((B,), bud - 3, dtype=torch.int32, device=dev)
-        sl, ct = kap.select_topk(scores, L, anchor, recent, km, bud, bud)
-        cb = kap.compact_view(sl, ct, bt, L, pos, 1)
-        us = time_call(lambda: kap.decode_attn(q, pos, Ks[lay()], Vs[lay()], cb[0], cb[2], out=out,
-                                               workspace=ws, logical=cb[1]), args.steps, st)
-        nbytes = B * bud * 16 * kv_tok
-        sweep.append({"s": round(num / den, 4), "pages": bud, "us": round(us, 2),
-                      "GBps": round(nbytes / (us * 1e-6) / 1e9, 1)})
-    full_us = time_call(lambda: kap.decode_attn(q, pos, Ks[lay()], Vs[lay()], bt, L, out=out,
-                                                workspace=ws), args.steps, st)
-    xs = np.array([d["pages"] / N for d in sweep])
-    ys = np.array([d["us"] for d in sweep])
-    A = np.stack([np.ones_like(xs), xs], axis=1)
-    coef, *_ = np.linalg.lstsq(A, ys, rcond=None)
-    pred = A @ coef
-    r2 = 1 - ((ys - pred) ** 2).sum() / ((ys - ys.mean()) ** 2).sum()
-    sel_us = [d for d in sweep if d["pages"] == budget][0]["us"]
-    print(json.dumps({
+    recall = needle_recall(b, cv[1].cpu().numpy()[:, 0], cnt.cpu().numpy()[:, 0], b["k_mid"])
+    sweep, full_us, fit = retention_sweep(q, pos, bt, L, anchor, recent, scores, Ks, Vs, ws, out,
+                                          N, B, kv_tok, args.steps, st)
+    sel = [d for d in sweep if d["pages"] == budget][0]
+    return {
         "metric": METRIC, "workload": label, "unit": "tokens/s",
-        "value": round(B / (sel_us * 1e-6), 1), "dtype": "bf16", "data": "synthetic",
+        "value": round(B / (sel["us"] * 1e-6), 1), "dtype": "bf16", "data": "synthetic",
         "layer_copies": R, "kernels": {k: round(v, 2) for k, v in res.items()},
-        "decode_selected_us": sel_us, "decode_full_us": round(full_us, 2),
+        "decode_selected_us": sel["us"], "decode_selected_GBps": sel["GBps"],
+        "decode_full_us": round(full_us, 2),
         "decode_full_GBps": round(B * int(w.seq_lens[0]) * kv_tok / (full_us * 1e-6) / 1e9, 1),
-        "selected_vs_full_decode_speedup": round(full_us / sel_us, 3),
-        "s_sweep": sweep,
-        "fit": {"T0_us": round(float(coef[0]), 2), "T_full_us": round(float(coef[1]), 2),
-                "r2": round(float(r2), 5), "T(100%)/T(full table)": round(ys[-1] / full_us, 4)},
-    }), flush=True)
+        "selected_vs_full_decode_speedup": round(full_us / sel["us"], 3),
+        "needle_recall": recall,
+        "s_sweep": sweep, "fit": fit,
+    }
 
 
 def run_early_route(args, dev):
@@ -561,9 +604,13 @@ def run_mixed(args, dev):
     """Mixed serving batch: 64 ragged requests (4K-128K, log-uniform) with
     per-request retention {1, 5.5, 25, 100} % and A1R2/A4R4 splits, pages
     scattered over a 1,525,878-page (100 GB) pool: one ragged decode launch."""
+    print(json.dumps(_mixed(args, dev)), flush=True)
+
+
+def _mixed(args, dev):
     w = W.spec("mixed_serving")
     B, Hq, Hkv, D = w.B, w.Hq, w.Hkv, w.D
-    b = W.make_device(w, dev)
+    b = W.make_device(w, dev, needle_dir=W.aimed_dirs(w))
     to = _upload(b, dev)
     bt, L, pos = to(b["bt"]), to(b["seq_lens"]), to(b["positions"])
     anchor, recent = to(b["anchor"]), to(b["recent"])
@@ -602,9 +649,13 @@ def run_mixed(args, dev):
     sel_bytes = int(clen.sum()) * kv_tok
     full_bytes = int(b["seq_lens"].astype(np.int64).sum()) * kv_tok
     pages = (clen + 15) // 16
-    print(json.dumps({
+    recall = needle_recall(b, cv[1].cpu().numpy()[:, 0], cnt.cpu().numpy()[:, 0],
+                           budgets - b["anchor"] - b["recent"])
+    return {
         "metric": METRIC, "workload": "mixed_serving: B=64, Hq=32, Hkv=8, D=128, contexts "
-        "log-uniform 4K-128K, s in {1, 5.5, 25, 100} %, A1R2/A4R4, 100 GB pool",
+        "log-uniform 4K-128K, s in {1, 5.5, 25, 100} %, A1R2/A4R4, 100 GB pool, needles aimed "
+        "at the rotated query",
+        "needle_recall": recall,
         "unit": "tokens/s", "value": round(B / (t_sel * 1e-6), 1), "dtype": "bf16",
         "data": "synthetic",
         "route_us": round(t_route, 2),
@@ -621,7 +672,7 @@ def run_mixed(args, dev):
         "ragged_over_full_GBps": round((sel_bytes / t_sel) / (full_bytes / t_full), 3),
         "context_tokens": {"min": int(b["seq_lens"].min()), "mean": round(float(b["seq_lens"].mean()), 1),
                            "max": int(b["seq_lens"].max())},
-    }), flush=True)
+    }
 
 
 def run_commit(args, dev):
@@ -803,7 +854,7 @@ def main():
     w = W.spec("qwen32b_128k", B=args.batch)
     B, Hq, Hkv, D = w.B, w.Hq, w.Hkv, w.D
     t0 = time.time()
-    b = W.make_device(w, dev)
+    b = W.make_device(w, dev, needle_dir=W.aimed_dirs(w))
     torch.cuda.synchronize()
     log(f"generated {w.name} B={B} on device in {time.time() - t0:.1f}s", q)
 
@@ -920,6 +971,7 @@ def main():
     cnt_h = cnt.cpu().numpy()[:, 0]
     sel_pages = [sel_h[i, :cnt_h[i]] for i in range(B)]
     nbytes = algorithmic_bytes(w, b, sel_pages)
+    recall = needle_recall(b, sel_h, cnt_h, b["k_mid"])
 
     # full-context decode over the same pool (comparison)
     for _ in range(3):
@@ -949,8 +1001,21 @@ def main():
     ceiling_gbs = probe.numel() / (ceil_ms * 1e-3) / 1e9
     del probe
 
+    # retention sweep and fit on the same layer copies (pooled top-K on the
+    # per-head scores of the routing query)
+    fit128 = None
+    if not args.no_extras:
+        scores = kap.score_blocks(q_route, pos, S0, bt, L, Hkv)
+        sweep128, _, fit128 = retention_sweep(
+            q_prop[0], pos, bt, L, anchor, recent, scores, [ly.K for ly in layers],
+            [ly.V for ly in layers], ws, dec_out, int(w.n_pages[0]), B, Hkv * 2 * D * EB,
+            args.steps, stream)
+        fit128 = dict(fit128, s_sweep=sweep128)
+        del scores
+
     gbs = lambda nb, ms: nb / (ms * 1e-3) / 1e9  # noqa: E731
     ver_gbs = gbs(nbytes["verify"], ver_ms)
+    sel_gbs = gbs(nbytes["decode_selected"], dec_ms)
     traffic = read_traffic("verify")
     # the verify's dense contraction: QK and PV, 2 D flops each per (query row, visible key)
     ver_flops = 4 * D * Hq * w.q_len * int(b["seq_lens"].astype(np.int64).sum())
@@ -962,7 +1027,16 @@ def main():
                 "frac_of_measured_ceiling": round(ver_gbs / ceiling_gbs, 4),
                 "bytes_per_launch": nbytes["verify"], "avg_launch_us": round(ver_ms * 1e3, 2),
                 "mfma": {"flops_per_launch": ver_flops, "tflops": round(ver_tflops, 1),
-                         "frac_of_bf16_dense_peak": round(ver_tflops / 2500.0, 4)}}
+                         "frac_of_bf16_dense_peak": round(ver_tflops / 2500.0, 4)},
+                # the headline metric's own kernel, beside the dominant one
+                "selected_decode": {
+                    "kernel": "kap_decode_attn over the compact view (partial + merge, 2 launches)",
+                    "achieved": round(sel_gbs, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                    "frac": round(sel_gbs / HBM_PEAK_GBS, 4),
+                    "frac_of_measured_ceiling": round(sel_gbs / ceiling_gbs, 4),
+                    "bytes_per_launch": nbytes["decode_selected"],
+                    "avg_launch_us": round(dec_ms * 1e3, 2),
+                    "traffic": read_traffic("decode_selected")}}
     s_meas = nbytes["decode_selected"] / nbytes["decode_full"]
     # the same ratio with the route's summary reads charged to the proposal step
     summ_bytes = int(((b["seq_lens"].astype(np.int64) + 15) // 16).sum()) * Hkv * D * EB
@@ -992,7 +1066,7 @@ def main():
         "kernels": {
             "route_us": round(route_ms * 1e3, 2),
             "decode_selected_us": round(dec_ms * 1e3, 2),
-            "decode_selected_GBps": round(gbs(nbytes["decode_selected"], dec_ms), 1),
+            "decode_selected_GBps": round(sel_gbs, 1),
             "decode_full_us": round(full_ms * 1e3, 2),
             "decode_full_GBps": round(gbs(nbytes["decode_full"], full_ms), 1),
             "verify_us": round(ver_ms * 1e3, 2),
@@ -1008,7 +1082,30 @@ def main():
             "phase_boundary_break_even_W_over_KV_with_summary_reads":
                 round((h - s_meas_route) / (1 - h), 3),
         },
+        "needle_recall": recall,
     }
+    if fit128 is not None:
+        result["retention_fit"] = fit128
+    if not args.no_extras:
+        # the other configurations of the pages' workloads, each on its own
+        # inputs (the 128K pool stays resident for the CPU baseline)
+        extras = {}
+        r = _sweep(args, dev, W.spec("llama8b_32k"), LLAMA_LABEL)
+        extras["llama8b_32k"] = {k: r[k] for k in (
+            "workload", "decode_selected_us", "decode_selected_GBps", "decode_full_us",
+            "decode_full_GBps", "selected_vs_full_decode_speedup", "needle_recall", "fit")}
+        extras["llama8b_32k"]["route_us"] = round(
+            r["kernels"]["score_pool_us"] + r["kernels"]["select_compact_pooled_us"], 2)
+        torch.cuda.empty_cache()
+        log("llama8b_32k leg done", q)
+        r = _mixed(args, dev)
+        extras["mixed_serving"] = {k: r[k] for k in (
+            "workload", "route_us", "decode_selected_us", "decode_selected_GBps",
+            "decode_full_us", "decode_full_GBps", "s_meas_bytes", "needle_recall",
+            "request_imbalance_max_over_mean", "ragged_over_full_GBps")}
+        torch.cuda.empty_cache()
+        log("mixed_serving leg done", q)
+        result["extras"] = extras
     if not args.no_cpu_baseline:
         result["cpu_baseline"] = cpu_baseline(w, b, b["K"], b["V"], cap, q)
     else:

@@ -497,3 +497,22 @@ def test_table5_break_even():
         assert cm.cost_plan(6, s, w, w, kv) == pytest.approx(cm.cost_base(6, h, w, kv), rel=1e-12)
         assert cm.kv_crit(h, s, w) == pytest.approx(kv, rel=1e-12)
     assert cm.kv_crit(0.3, 0.4, 1.0) == float("inf")
+
+
+# ----------------------------------------------------------------------------- stored inputs
+def test_stored_needle_directions_match_the_oracle():
+    """workloads/aim/*.npz (the benchmark's needle directions) are the unit
+    vectors of the group-summed rotated query, as tests/golden/make_needle_dirs.py
+    computes them with the oracle's RoPE, for the current query draws."""
+    import importlib.util
+    import workloads as W
+    path = os.path.join(os.path.dirname(os.path.abspath(__file__)), "golden", "make_needle_dirs.py")
+    spec = importlib.util.spec_from_file_location("make_needle_dirs", path)
+    mod = importlib.util.module_from_spec(spec)
+    spec.loader.exec_module(mod)
+    for name, B in mod.WORKLOADS.items():
+        dirs, keys = mod.aimed(name, B)
+        w = W.spec(name, B=B) if name != "mixed_serving" else W.spec(name)
+        stored = W.aimed_dirs(w)
+        np.testing.assert_allclose(stored, dirs, rtol=0, atol=1e-6)
+        np.testing.assert_allclose(np.linalg.norm(stored, axis=-1), 1.0, atol=1e-6)

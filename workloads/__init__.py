@@ -5,4 +5,5 @@ method's arithmetic (no rotation, no scoring, no selection, no attention, no
 page summaries).  Both the oracle side (tests, cpu baseline) and the GPU side
 (tests, bench) take their inputs from here.
 """
-from .gen import SPECS, Workload, dense_pool, draft_kv, make, make_device, spec  # noqa: F401
+from .gen import (SPECS, Workload, aimed_dirs, dense_pool, draft_kv, make, make_device,  # noqa: F401
+                  request_key, spec)

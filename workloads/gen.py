@@ -336,3 +336,30 @@ def make_device(w: Workload, device, needle_dir: Optional[np.ndarray] = None) ->
         del kb, vb
     b["K"], b["V"] = K, V
     return b
+
+
+def request_key(q: np.ndarray, position: int) -> str:
+    """Identity of one request's decode query and its position (hash of the bits)."""
+    import hashlib
+    return hashlib.sha256(np.ascontiguousarray(q).tobytes() + int(position).to_bytes(8, "little")).hexdigest()[:16]
+
+
+def aimed_dirs(w: Workload) -> np.ndarray:
+    """Stored needle directions of a benchmark workload ([B][Hkv][D] float32),
+    written by workloads/aim/make_aim.py (which aims them at the rotated,
+    group-summed query).  Raises if the file is missing or was made from other
+    query draws or positions."""
+    import os
+    path = os.path.join(os.path.dirname(os.path.abspath(__file__)), "aim", f"{w.name}.npz")
+    if not os.path.exists(path):
+        raise FileNotFoundError(f"{path}: run tests/golden/make_needle_dirs.py")
+    z = np.load(path, allow_pickle=False)
+    dirs, keys = z["dirs"], z["keys"]
+    if dirs.shape[0] < w.B or dirs.shape[1:] != (w.Hkv, w.D):
+        raise ValueError(f"{path} holds {dirs.shape}, need [{w.B}][{w.Hkv}][{w.D}]")
+    b = make(w, with_kv=False)
+    for bi in range(w.B):
+        if request_key(b["q"][bi], int(b["positions"][bi])) != str(keys[bi]):
+            raise ValueError(f"{path}: request {bi} was aimed for other query draws or another "
+                             "position; rerun tests/golden/make_needle_dirs.py")
+    return dirs[:w.B]
