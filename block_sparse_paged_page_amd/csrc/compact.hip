@@ -1,7 +1,7 @@
-// Compact view over a page selection (KAP paper, selected-KV view: block
-// tables resolve plan-visible logical blocks to compact physical pages in
-// access order, logical positions are preserved, and slot mappings place the
-// newly scheduled tokens into their physical KV slots).
+// Compact view over a page selection (KAP paper, selected-KV view): a compact
+// table lists the physical page of every chosen logical page, in ascending
+// logical order, beside the logical page itself (positions stay logical), and
+// the slot mapping gives each new token its physical page and offset.
 //
 // One 256-thread block per selection row: gather the physical page of every
 // selected logical page, count the row's valid tokens (block reduction) and,

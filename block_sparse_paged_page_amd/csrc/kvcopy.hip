@@ -1,7 +1,7 @@
 // KV copies on the path, both bit for bit:
-//  * append through a slot mapping ([KAP] verifier: verification advances the
-//    committed full-context KV state; [KAP] selected-KV view: slot mappings
-//    place newly scheduled tokens into their physical KV slots);
+//  * append through a slot mapping ([KAP] verifier: a verify pass moves the
+//    committed full-context KV forward; [KAP] selected-KV view: the slot
+//    mapping gives each new token its physical page and offset);
 //  * compact workspace materialization ([KAP] selected-KV view: the executor
 //    materializes a compact physical view; shape stabilization: a reusable
 //    compact KV workspace).

@@ -211,10 +211,9 @@ KAP_API int32_t kap_budget_from_ratio(int32_t n_pages, int64_t s_num, int64_t s_
                               int32_t recent);
 
 /*
- * Compact view over a selection ([KAP] selected-KV view: block tables resolve
- * plan-visible logical blocks to compact physical pages in access order while
- * logical positions are preserved; slot mappings place newly scheduled tokens
- * into their physical KV slots).  For row (b, gr):
+ * Compact view over a selection ([KAP] selected-KV view: a compact table of
+ * the chosen pages' physical ids in ascending logical order, the logical pages
+ * kept beside it, and a slot for each new token).  For row (b, gr):
  *   compact_bt[j]      = block_table[b][sel_pages[j]]   (j < sel_count, else -1)
  *   compact_logical[j] = sel_pages[j]                   (j < sel_count, else -1)
  *   compact_len        = total valid tokens of the selected pages (the last
@@ -402,9 +401,9 @@ KAP_API kap_status kap_materialize_view(const void* k_pool, const void* v_pool, 
                                         int32_t ws_pages, int32_t* ws_table, kap_stream stream);
 
 /*
- * KV append through a slot mapping ([KAP] verifier: verification advances the
- * committed full-context KV state; [KAP] selected-KV view: slot mappings place
- * newly scheduled tokens into their physical KV slots).  Token i of request b
+ * KV append through a slot mapping ([KAP] verifier: a verify pass moves the
+ * committed full-context KV forward; [KAP] selected-KV view: the slot mapping
+ * gives each new token its physical page and offset).  Token i of request b
  * goes to slot s = slot_mapping[b][i] = page * 16 + offset: its K row for KV
  * head g becomes k_pool[page][g][offset][:] and its V values become
  * v_pool[page][g][:][offset].  Rows are copied bit for bit (K as the cache

@@ -256,9 +256,9 @@ int kor_budget_from_ratio(int N, int64_t s_num, int64_t s_den, int a, int r) {
 }
 
 /*
- * O5. Compact view ([KAP] selected-KV view: block tables resolve plan-visible
- * logical blocks to physical pages, compacted in access order; slot mappings
- * place newly scheduled tokens into their physical KV slots).
+ * O5. Compact view ([KAP] selected-KV view: the chosen logical pages, in
+ * ascending order, with their physical pages; the slot mapping gives each new
+ * token its physical page and offset).
  *   cbt[j]  = bt[sel[j]]           clog[j] = sel[j]        (j < cnt; -1 after)
  *   clen    = sum over j of the valid tokens of logical page sel[j]
  *   slot[i] = bt[(P+i)/ps]*ps + (P+i)%ps for the new token at P+i, or -1 when
@@ -376,9 +376,9 @@ void kor_attend(const void* q, int q_dt, int q_len, const int32_t* pos0, double 
 
 /*
  * O2'. KV append through a slot mapping: write one token's K row and V column
- * per KV head into the slot slot[b][i] (skipped when -1).  [KAP] verifier: the
- * verify transition advances the committed full-context KV state; slot mappings
- * place newly scheduled tokens into their physical KV slots.
+ * per KV head into the slot slot[b][i] (skipped when -1).  [KAP] verifier: a
+ * verify pass moves the committed full-context KV forward; [KAP] selected-KV
+ * view: the slot mapping gives each new token its physical page and offset.
  * k_new/v_new are [B][q_new][Hkv][D]; K and V are updated in place (same dtype).
  */
 void kor_append_kv(const void* k_new, const void* v_new, int kv_dt, const int64_t* slot, int B,

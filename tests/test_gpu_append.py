@@ -1,8 +1,8 @@
 """Committed-state advance: the verify window's K/V appended through the slot
 mapping, the touched pages' summaries recomputed, and the k+1-token verify
-attending causally to the appended tokens ([KAP] verifier: verification is
-scored against the full KV and advances the committed state; [KAP] selected-KV
-view: slot mappings place new tokens into their physical KV slots).
+attending causally to the appended tokens ([KAP] verifier: the verify window
+is scored against the full KV and moves the committed state forward; [KAP]
+selected-KV view: the slot mapping gives each new token its page and offset).
 
 The oracle side appends on its own host copies (local page order) with the
 oracle's slot mapping; nothing the GPU writes is read back into the oracle.

@@ -62,6 +62,19 @@ class Big:
         btl = np.arange(len(ph), dtype=np.int32)[None]
         return Kh, Vh, btl
 
+    def host_selected(self, bi, g, lpages):
+        """K/V of KV head g on request bi's logical pages `lpages` only, with a
+        full-width local table whose entry for each of those pages points at
+        its local copy (the other entries are never read: the key list holds
+        only tokens of those pages)."""
+        allp = self.pages(bi)
+        ph = torch.from_numpy(allp[lpages].astype(np.int64)).cuda()
+        Kh = _u16(self.K[ph][:, g:g + 1])
+        Vh = _u16(self.V[ph][:, g:g + 1])
+        btl = np.zeros((1, len(allp)), dtype=np.int32)
+        btl[0, lpages] = np.arange(len(lpages), dtype=np.int32)
+        return Kh, Vh, btl
+
     def host_summary(self, bi):
         """oracle summary of request bi (all heads), rounded to bf16, local page order."""
         ph = torch.from_numpy(self.pages(bi).astype(np.int64)).cuda()
@@ -149,15 +162,15 @@ def _routing(big):
     return sel_ref, cnt_ref, cv
 
 
-def _check_rows(big, out, lse, samples, keys_for, qsrc, q_len, start):
-    """Oracle on sampled (request, KV group) pairs: every query row of that group."""
+def _check_rows(big, out, lse, samples, keys_for, qsrc, q_len, start, host_for=None):
+    """Oracle on the given (request, KV group) pairs: every query row of each."""
     w, b = big.w, big.b
     grp = w.Hq // w.Hkv
     o = out.view(torch.int16).cpu().numpy().view(np.uint16)
     lg = lse.cpu().numpy()
     worst = 0.0
     for bi, g in samples:
-        Kh, Vh, btl = big.host_group(bi, g)
+        Kh, Vh, btl = host_for(bi, g) if host_for else big.host_group(bi, g)
         qsub = qsrc[bi:bi + 1, :, g * grp:(g + 1) * grp]
         ref, lref = oracle.attend(qsub, start[bi:bi + 1], Kh, Vh, btl, [keys_for(bi, g)], 1, 1)
         got = oracle.widen(o.reshape(w.B, q_len, w.Hq, w.D)[bi, :, g * grp:(g + 1) * grp])
@@ -169,9 +182,17 @@ def _check_rows(big, out, lse, samples, keys_for, qsrc, q_len, start):
     return worst
 
 
-def _attention(big, sel_ref, cnt_ref, cv, samples):
+def _attention(big, sel_ref, cnt_ref, cv, sel_requests=None, samples=()):
+    """Selected decode on every KV group of the requests `sel_requests` (all
+    requests by default; only their selected pages go to the host); full decode
+    and verify on every KV group of request 0 and every request of KV group 0,
+    plus `samples`."""
     w, b = big.w, big.b
     G = w.Hkv if w.per_head else 1
+    sel_requests = range(w.B) if sel_requests is None else sel_requests
+    sel_rows = [(bi, g) for bi in sel_requests for g in range(w.Hkv)]
+    samples = sorted(set([(0, g) for g in range(w.Hkv)] + [(bi, 0) for bi in range(w.B)] +
+                         list(samples)))
     cbt, clog, clen, _ = cv
     ws = torch.empty(kap.attn_workspace_bytes(w.B, w.q_len, w.Hq, w.Hkv, w.D), dtype=torch.uint8,
                      device="cuda")
@@ -180,9 +201,11 @@ def _attention(big, sel_ref, cnt_ref, cv, samples):
                           logical=clog)
     torch.cuda.synchronize()
     keys_sel = oracle.keys_selected(sel_ref, cnt_ref, b["seq_lens"])
-    e1 = _check_rows(big, out, lse, samples,
-                     lambda bi, g: keys_sel[bi * G + (g if G > 1 else 0)],
-                     b["q"][:, None], 1, b["positions"])
+    row = lambda bi, g: bi * G + (g if G > 1 else 0)  # noqa: E731
+    e1 = _check_rows(big, out, lse, sel_rows, lambda bi, g: keys_sel[row(bi, g)],
+                     b["q"][:, None], 1, b["positions"],
+                     host_for=lambda bi, g: big.host_selected(
+                         bi, g, sel_ref[bi, row(bi, g) % G, :cnt_ref[bi, row(bi, g) % G]]))
     out = kap.decode_attn(big.q, big.pos, big.K, big.V, big.bt, big.L, G=1, lse=lse, workspace=ws)
     torch.cuda.synchronize()
     e2 = _check_rows(big, out, lse, samples,
@@ -196,8 +219,8 @@ def _attention(big, sel_ref, cnt_ref, cv, samples):
         e3 = _check_rows(big, vout, vl, samples,
                          lambda bi, g: np.arange(int(b["seq_lens"][bi]), dtype=np.int32),
                          b["qv"], w.q_len, b["positions"])
-    print(f"[{w.name}] sampled max rel err: selected {e1:.2e} full {e2:.2e} verify {e3:.2e}",
-          flush=True)
+    print(f"[{w.name}] max rel err: selected {e1:.2e} ({len(sel_rows)} rows), full {e2:.2e} and "
+          f"verify {e3:.2e} ({len(samples)} rows)", flush=True)
 
 
 def test_qwen32b_128k_b4_full_size():
@@ -205,14 +228,14 @@ def test_qwen32b_128k_b4_full_size():
     big = Big(W.spec("qwen32b_128k", B=4))
     sel_ref, cnt_ref, cv = _routing(big)
     assert np.all(cnt_ref == 451)
-    _attention(big, sel_ref, cnt_ref, cv, samples=[(0, 0), (1, 3), (2, 7), (3, 5)])
+    _attention(big, sel_ref, cnt_ref, cv, samples=[(1, 3), (2, 7), (3, 5)])
 
 
 def test_llama8b_32k_b8_full_size():
     big = Big(W.spec("llama8b_32k"))
     sel_ref, cnt_ref, cv = _routing(big)
     assert np.all(cnt_ref == 113)
-    _attention(big, sel_ref, cnt_ref, cv, samples=[(0, 0), (3, 4), (7, 7)])
+    _attention(big, sel_ref, cnt_ref, cv, samples=[(3, 4), (7, 7)])
 
 
 def test_mixed_serving_b64_full_size():
@@ -221,8 +244,11 @@ def test_mixed_serving_b64_full_size():
     sel_ref, cnt_ref, cv = _routing(big)
     L = big.b["seq_lens"]
     order = np.argsort(L)
+    # every KV group of 8 requests across the length range for the selected
+    # decode; request 0 and KV group 0 in full for the full decode
+    span = [int(order[i]) for i in np.linspace(0, len(order) - 1, 8).round().astype(int)]
     samples = [(int(order[0]), 0), (int(order[len(order) // 2]), 5), (int(order[-1]), 7)]
-    _attention(big, sel_ref, cnt_ref, cv, samples=samples)
+    _attention(big, sel_ref, cnt_ref, cv, sel_requests=span, samples=samples)
     del big
     torch.cuda.empty_cache()
 
@@ -240,7 +266,7 @@ def test_early_route_40k_b8_full_size():
     assert e.max() <= 1e-5
     sel_ref, cnt_ref, cv = _routing(big)
     assert np.all(cnt_ref == 8)
-    _attention(big, sel_ref, cnt_ref, cv, samples=[(0, 0), (5, 6)])
+    _attention(big, sel_ref, cnt_ref, cv, samples=[(5, 6)])
 
 
 def test_qwen32b_128k_b4_append_and_causal_verify():
