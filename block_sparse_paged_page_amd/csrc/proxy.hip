@@ -2,120 +2,87 @@
 // side flow projects a preceding hidden state through the query projection to
 // obtain the routing query).  q_out = hidden @ W_q, bf16 inputs, fp32 sums.
 //
-// HBM-bound GEMV (B <= 16 rows share each W_q byte).  A block (4 waves) owns a
-// tile of 256 output columns x kProxyRows rows of W_q; every wave-wide load
-// reads 512 B of one W_q row contiguously (lane l: columns 4l .. 4l+3), and a
-// wave keeps all 32 of its rows in flight.  Each lane accumulates B x 4
-// columns over its rows; the four waves are added in wave order through LDS and each row split
-// writes its partial sums; a second kernel adds the splits in split order
+// HBM-bound GEMV (B <= 16 rows share each W_q byte) in two launches: each row
+// split of kProxyRows rows of W_q writes its partial sums (on the matrix
+// cores, below), and a second kernel adds the splits in split order
 // (deterministic).
 #include "kap_internal.h"
 
 namespace kap {
 
-constexpr int kProxyCols = 256;  // columns per block: 64 lanes x 4
-constexpr int kProxyRows = 128;  // W_q rows per block (32 per wave)
+constexpr int kProxyRows = 128;  // W_q rows per split
 
-template <int BM>
-__global__ __launch_bounds__(256) void proxy_partial_kernel(const uint16_t* hidden,
-                                                            const uint16_t* wq, int B, int dm,
-                                                            int n_out, float* partial) {
-  const int n0 = blockIdx.x * kProxyCols;
+// Partial sums on the matrix cores.  hidden [B][dm] @ W_q [dm][n]
+// is a dense contraction with M = B <= 16 (padded to 16), so it runs as
+// v_mfma_f32_16x16x32_bf16 with A = the hidden rows and B = W_q.  One wave
+// owns 128 output columns x kProxyRows rows of W_q (one row split).  Lane
+// (i, j) = (lane % 16, lane / 16) loads, for each 32-row k-step, rows
+// 8j .. 8j+7 of the step at columns 8i .. 8i+7 (eight 16-byte loads; each
+// load instruction covers four 256-byte row segments), so it holds an 8 x 8
+// tile of W_q.  The MFMA wants, per lane, 8 consecutive k of one column; MFMA
+// t (t = 0..7) takes column 8i + t from lane i, so each lane only transposes
+// its own tile (byte permutes, no exchange between lanes), and the eight
+// MFMAs of a step cover the 128 columns with column 8i + t in lane i of
+// instance t.  Products of bf16 are exact in fp32 and the matrix cores add in
+// fp32 (a different order than the lane loop: results agree to fp32 rounding).
+// All four k-steps' loads go out before the first MFMA (W_q is read once per
+// call: streaming loads), with the hidden slices first.  The B x 8 outputs a
+// lane holds (rows 4j .. 4j+3 of each MFMA) go to the split's partial sums.
+constexpr int kProxyMfmaCols = 128;
+__global__ __launch_bounds__(64) void proxy_mfma_kernel(const uint16_t* hidden,
+                                                        const uint16_t* wq, int B, int dm,
+                                                        int n_out, float* partial) {
+  const int n0 = blockIdx.x * kProxyMfmaCols;
   const int split = blockIdx.y;
   const int c0 = split * kProxyRows;
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  constexpr int RPW = kProxyRows / 4;  // rows per wave
-  // rows in flight at once: all of the wave's rows, or 16 when the batch is 16
-  constexpr int INFL = BM >= 16 ? 16 : RPW;
-  const uint16_t* wbase = wq + (int64_t)(c0 + wave * RPW) * n_out + n0 + lane * 4;
-  // The hidden-state slice is requested first and the W_q rows right after.
-  // Loads complete in issue order, so staging the slice in LDS waits only for
-  // its own few loads, and the row loop below waits for one W_q row at a time:
-  // each row's FMAs run while the later rows are still in flight.  (Issued the
-  // other way round, staging the slice waited for every W_q row, and all of
-  // the arithmetic ran after the whole burst had arrived.)  W_q is read once
-  // per call: streaming loads.
-  __shared__ float sh[BM][kProxyRows];
-  constexpr int PER = BM * kProxyRows / 256 > 0 ? BM * kProxyRows / 256 : 1;  // values per thread
-  uint16_t hraw[PER];
+  const int lane = threadIdx.x, i = lane & 15, j = lane >> 4;
+  constexpr int KSTEPS = kProxyRows / 32;
+  // hidden rows (A operand): lane (i, j) holds hidden[i][k + 8j .. + 7]; rows
+  // past B load row B - 1 and are masked to zero (straight-line loads)
+  uint4 hf[KSTEPS];
+  const uint16_t* hrow = hidden + (int64_t)min(i, B - 1) * dm + c0 + 8 * j;
+  const uint32_t keep = i < B ? 0xffffffffu : 0u;
 #pragma unroll
-  for (int k = 0; k < PER; ++k) {
-    const int e = k * 256 + tid;
-    const int b = e / kProxyRows, c = e % kProxyRows;
-    hraw[k] = hidden[(int64_t)min(b, B - 1) * dm + c0 + c];
+  for (int s = 0; s < KSTEPS; ++s) {
+    const uint4 x = *(const uint4*)(hrow + 32 * s);
+    hf[s] = make_uint4(x.x & keep, x.y & keep, x.z & keep, x.w & keep);
   }
-  __builtin_amdgcn_sched_barrier(0);  // keep the slice's loads ahead of the rows
-  uint2 wrow[INFL];
+  // W_q tiles: w[s][r] = row c0 + 32 s + 8 j + r, columns n0 + 8 i .. + 7
+  uint4 w[KSTEPS][8];
+  const uint16_t* wbase = wq + (int64_t)(c0 + 8 * j) * n_out + n0 + 8 * i;
 #pragma unroll
-  for (int r = 0; r < INFL; ++r) wrow[r] = ld_stream8(wbase + (int64_t)r * n_out);
-  __builtin_amdgcn_sched_barrier(0);
+  for (int s = 0; s < KSTEPS; ++s)
 #pragma unroll
-  for (int k = 0; k < PER; ++k) {
-    const int e = k * 256 + tid;
-    const int b = e / kProxyRows, c = e % kProxyRows;
-    if (e < BM * kProxyRows) sh[b][c] = b < B ? bf16_to_f32(hraw[k]) : 0.f;
-  }
-  lds_barrier();
-  float acc[BM][4];
+    for (int r = 0; r < 8; ++r) w[s][r] = ld_stream16(wbase + (int64_t)(32 * s + r) * n_out);
+  floatx4 acc[8];
 #pragma unroll
-  for (int b = 0; b < BM; ++b)
+  for (int t = 0; t < 8; ++t) acc[t] = floatx4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-    for (int e = 0; e < 4; ++e) acc[b][e] = 0.f;
+  for (int s = 0; s < KSTEPS; ++s) {
+    const bf16x8 a = __builtin_bit_cast(bf16x8, hf[s]);
 #pragma unroll
-  for (int r0 = 0; r0 < RPW; r0 += INFL) {
-    if (r0 > 0) {
+    for (int t = 0; t < 8; ++t) {
+      // column t of the tile, 8 rows: dword m = (row 2m, row 2m + 1)
+      const uint32_t sel = (t & 1) ? 0x07060302u : 0x05040100u;
+      uint32_t d[4];
 #pragma unroll
-      for (int r = 0; r < INFL; ++r)
-        wrow[r] = ld_stream8(wbase + (int64_t)(r0 + r) * n_out);
-    }
-#pragma unroll
-    for (int rr = 0; rr < INFL; ++rr) {
-      const int r = r0 + rr;
-      const uint32_t ww[2] = {wrow[rr].x, wrow[rr].y};
-      float wf[4];
-#pragma unroll
-      for (int e = 0; e < 2; ++e) {
-        wf[2 * e] = __uint_as_float(ww[e] << 16);
-        wf[2 * e + 1] = __uint_as_float(ww[e] & 0xffff0000u);
+      for (int m = 0; m < 4; ++m) {
+        const uint32_t lo = (&w[s][2 * m].x)[t >> 1], hi = (&w[s][2 * m + 1].x)[t >> 1];
+        d[m] = __builtin_amdgcn_perm(hi, lo, sel);
       }
-#pragma unroll
-      for (int b = 0; b < BM; ++b) {
-        const float h = sh[b][wave * RPW + r];
-#pragma unroll
-        for (int e = 0; e < 4; ++e) acc[b][e] += h * wf[e];
-      }
+      const bf16x8 bv = __builtin_bit_cast(bf16x8, make_uint4(d[0], d[1], d[2], d[3]));
+      acc[t] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, bv, acc[t], 0, 0, 0);
     }
   }
-  // waves 1..3 hand their sums to wave 0 through LDS, added in wave order,
-  // eight batch rows at a time
-  constexpr int BC = BM < 8 ? BM : 8;
-  __shared__ float red[3][BC][kProxyCols];
+  // lane (i, j) holds batch rows 4j .. 4j+3 of columns n0 + 8i + t
 #pragma unroll
-  for (int b0 = 0; b0 < BM; b0 += BC) {
-    if (wave > 0) {
-#pragma unroll
-      for (int bb = 0; bb < BC; ++bb)
-#pragma unroll
-        for (int e = 0; e < 4; ++e) red[wave - 1][bb][lane * 4 + e] = acc[b0 + bb][e];
+  for (int e = 0; e < 4; ++e) {
+    const int b = 4 * j + e;
+    if (b < B) {
+      float* dst = partial + ((int64_t)split * B + b) * n_out + n0 + 8 * i;
+      *(floatx4*)dst = floatx4{acc[0][e], acc[1][e], acc[2][e], acc[3][e]};
+      *(floatx4*)(dst + 4) = floatx4{acc[4][e], acc[5][e], acc[6][e], acc[7][e]};
     }
-    lds_barrier();
-    if (wave == 0) {
-#pragma unroll
-      for (int bb = 0; bb < BC; ++bb) {
-        const int b = b0 + bb;
-        if (b < B) {
-          float* dst = partial + ((int64_t)split * B + b) * n_out + n0 + lane * 4;
-          floatx4 o;
-#pragma unroll
-          for (int e = 0; e < 4; ++e) {
-            const int col = lane * 4 + e;
-            o[e] = ((acc[b][e] + red[0][bb][col]) + red[1][bb][col]) + red[2][bb][col];
-          }
-          *(floatx4*)dst = o;
-        }
-      }
-    }
-    lds_barrier();
   }
 }
 
@@ -144,16 +111,8 @@ int proxy_splits(int d_model) { return d_model / kProxyRows; }
 kap_status launch_proxy(const uint16_t* hidden, const uint16_t* wq, int32_t B, int32_t dm,
                         int32_t n_out, float* q_out, float* partial, int32_t splits,
                         hipStream_t stream) {
-  dim3 grid(n_out / kProxyCols, splits);
-#define KAP_PROXY(BM) \
-  hipLaunchKernelGGL((proxy_partial_kernel<BM>), grid, dim3(256), 0, stream, hidden, wq, B, dm, \
-                     n_out, partial)
-  if (B <= 1) KAP_PROXY(1);
-  else if (B <= 2) KAP_PROXY(2);
-  else if (B <= 4) KAP_PROXY(4);
-  else if (B <= 8) KAP_PROXY(8);
-  else KAP_PROXY(16);
-#undef KAP_PROXY
+  hipLaunchKernelGGL(proxy_mfma_kernel, dim3(n_out / kProxyMfmaCols, splits), dim3(64), 0, stream,
+                     hidden, wq, B, dm, n_out, partial);
   kap_status st = check_launch("proxy partial");
   if (st != KAP_OK) return st;
   const int total = B * n_out;

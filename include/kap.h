@@ -130,8 +130,8 @@ KAP_API kap_status kap_score_pool_blocks(const void* q, int32_t q_dtype, const i
  * Proxy query for early routing.  [ESKV] Interpretation: the side flow builds
  * a proxy query from a preceding hidden state through the query projection,
  * then scores and selects over the K-summary cache before the target layer.
- *   q_out[b][n] = sum_c hidden[b][c] * w_q[c][n]     (bf16 inputs, fp32 accumulation,
- *                 row splits of 128 added in split order: deterministic)
+ *   q_out[b][n] = sum_c hidden[b][c] * w_q[c][n]     (bf16 inputs, fp32 accumulation on
+ *                 the matrix cores, row splits of 128 added in split order: deterministic)
  *   hidden device [B][d_model] bf16; w_q device [d_model][n_out] bf16 (row-major)
  *   q_out  device out [B][n_out] float -- feed to kap_score_blocks as KAP_F32
  *          with n_out = Hq * D.
