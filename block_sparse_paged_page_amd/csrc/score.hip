@@ -133,11 +133,16 @@ __global__ __launch_bounds__(256) void score_kernel(ScoreArgs a) {
 // reads its head's 64 summary rows exactly as score_kernel does (same access
 // pattern and arithmetic, so the per-head scores are the same), and the waves
 // of a block read the same 64 pages, so each page's contiguous run of head
-// rows is fetched together.  The request's query heads are staged in LDS by
-// the whole block while the rows are in flight.  The run's scores are then
-// folded over the heads in head order, in fp32 with round-to-nearest adds and
-// one rounded division: the same mean the top-K forms for pooled selection,
-// so the top-K then reads one key row per request instead of Hkv.
+// rows is fetched together.  The run's scores are then folded over the heads
+// in head order, in fp32 with round-to-nearest adds and one rounded division:
+// the same mean the top-K forms for pooled selection, so the top-K then reads
+// one key row per request instead of Hkv.
+// Order of a wave's work: the table entries and the group's query heads are
+// requested at once (clamped indices, no wait for the request's length), the
+// rotation angles are computed from the position while they are in flight,
+// the summary rows are requested as soon as the table entries land, and the
+// group query is rotated and summed in the wave's own LDS region while the
+// rows are in flight.  Only the fold over heads needs the whole block.
 // Pages per block: 16 row loads in flight per wave, at most 64 pages (one
 // page-table entry per lane).
 template <int D, typename ST>
@@ -147,6 +152,24 @@ constexpr int pool_pages_per_block() {
 }
 constexpr int kPoolMaxHeads = 16;
 constexpr size_t kPoolMaxQueryLds = 64 * 1024;
+
+// Bytes of LDS a wave stages its group's query heads in: whole 1 KiB blocks
+// (one 16-byte load per lane each), so a block's last load may run past the
+// group's rows into padding.
+template <typename QT>
+__host__ __device__ constexpr int pool_query_region(int grp, int D) {
+  return (grp * D * (int)sizeof(QT) + 1023) / 1024 * 1024;
+}
+
+// Dynamic LDS of score_pool_kernel: one query region per wave.
+inline size_t pool_query_lds(kap_dtype q_dt, int Hq, int Hkv, int D) {
+  const int grp = Hq / Hkv;
+  return (size_t)Hkv * (q_dt == KAP_BF16 ? pool_query_region<uint16_t>(grp, D)
+                                         : pool_query_region<float>(grp, D));
+}
+
+typedef __attribute__((address_space(1))) const void* gptr_t;
+typedef __attribute__((address_space(3))) void* lptr_t;
 
 template <int D, typename ST, typename QT>
 __global__ __launch_bounds__(1024) void score_pool_kernel(ScoreArgs a) {
@@ -159,50 +182,61 @@ __global__ __launch_bounds__(1024) void score_pool_kernel(ScoreArgs a) {
   constexpr int PPB = pool_pages_per_block<D, ST>();  // pages per block (<= 64)
   constexpr int U = PPB / RPL;
   constexpr int half = D / 2;
-  constexpr int QC = D * (int)sizeof(QT) / 64;  // 16-byte query chunks per thread (grp <= 16)
+  constexpr int QC = D * (int)sizeof(QT) / 64;  // 1 KiB query blocks per wave at most (grp <= 16)
   const int part = lane % LPR, sub = lane / LPR;
-  const int N = (a.seq_lens[b] + kPage - 1) / kPage;
   const int w0 = blockIdx.y * PPB;
   const int w1 = min(w0 + PPB, a.max_pages);
-  const int nv = max(0, min(w1, N) - w0);  // pages of the run that hold keys
   const ST* summ = (const ST*)a.summ;
   extern __shared__ __align__(16) unsigned char smem[];
-  QT* sq = (QT*)smem;  // the request's query heads [Hq][D] (dynamic)
+  // wave g's region: its group's query heads, then padding (written and read
+  // by that wave only, so staging needs no block barrier)
+  const int qreg = pool_query_region<QT>(a.grp, D);
+  unsigned char* sqg = smem + (size_t)g * qreg;
   __shared__ float su[kPoolMaxHeads][D];
   __shared__ float sc[kPoolMaxHeads][PPB];
+  __shared__ int sbt[kPoolMaxHeads][64];
+
+  // The group's query heads and the run's table entries go straight to LDS
+  // (global_load_lds: no registers, and the compiler keeps them where they
+  // stand), all issued before the request's length is known; the length and
+  // position come by scalar loads beside them.  Clamped sources: lanes past
+  // the group's rows fill the region's padding.
+  const int L = a.seq_lens[b], P = a.pos[b];  // scalar loads, ahead of the LDS writes
+  const int nchunk = a.grp * D * (int)sizeof(QT) / 16;
+  const uint4* qsrc = (const uint4*)((const QT*)a.q + ((int64_t)b * a.Hq + (int64_t)g * a.grp) * D);
+#pragma unroll
+  for (int k = 0; k < QC; ++k)
+    if (k * 1024 < qreg)  // uniform
+      __builtin_amdgcn_global_load_lds((gptr_t)(qsrc + min(k * 64 + lane, nchunk - 1)),
+                                       (lptr_t)(sqg + k * 1024), 16, 0, 0);
+  __builtin_amdgcn_global_load_lds(
+      (gptr_t)(a.bt + (int64_t)b * a.max_pages + min(w0 + lane, a.max_pages - 1)),
+      (lptr_t)&sbt[g][0], 4, 0, 0);
+  const int N = (L + kPage - 1) / kPage;
+  double sn = 0.0, cs = 1.0;  // lane = rotation pair; the angle needs only the position
+  if (lane < half) rope_sincos((double)P, lane, D, a.log2_theta, &sn, &cs);
+  const int nv = max(0, min(w1, N) - w0);  // pages of the run that hold keys
 
   if (nv > 0) {  // uniform over the block
-    // Straight-line loads at clamped indices (a load under a branch makes the
-    // compiler wait for it, and for every older load, at once): the query
-    // heads, then the run's page-table entries, then the head's rows.
-    const int nchunk = a.Hq * D * (int)sizeof(QT) / 16;
-    const uint4* qsrc = (const uint4*)((const QT*)a.q + (int64_t)b * a.Hq * D);
-    uint4 qc[QC];
-#pragma unroll
-    for (int k = 0; k < QC; ++k) qc[k] = qsrc[min(k * nt + tid, nchunk - 1)];
-    const int tr0 = a.bt[(int64_t)b * a.max_pages + min(w0 + lane, a.max_pages - 1)];
-    const int tr = lane < nv ? tr0 : 0;
-    // the query chunks arrived with the table entries (loads complete in order)
-#pragma unroll
-    for (int k = 0; k < QC; ++k)  // clamped like the loads: repeats store the same chunk
-      ((uint4*)sq)[min(k * nt + tid, nchunk - 1)] = qc[k];
+    // every load above has landed (loads complete in order; the table
+    // entries were issued last)
+    __builtin_amdgcn_s_waitcnt(0x0f70);  // vmcnt(0)
+    // rows past the run's keys re-read its first page (masked below), so
+    // every lane issues the same straight-line loads
     int phys[U];
-#pragma unroll
-    for (int u = 0; u < U; ++u) phys[u] = __shfl(tr, u * RPL + sub);
-    uint4 v[U];
 #pragma unroll
     for (int u = 0; u < U; ++u) {
       const int j = u * RPL + sub;
-      v[u] = make_uint4(0, 0, 0, 0);
-      if (j < nv) v[u] = ld_stream16(summ + ((int64_t)phys[u] * a.Hkv + g) * D + part * EPL);
+      phys[u] = sbt[g][j < nv ? j : 0];
     }
-    lds_barrier();
-    // u_g = sum over the group of RoPE(q_h, pos); lane = rotation pair
+    uint4 v[U];
+#pragma unroll
+    for (int u = 0; u < U; ++u)
+      v[u] = ld_stream16(summ + ((int64_t)phys[u] * a.Hkv + g) * D + part * EPL);
+    // u_g = sum over the group of RoPE(q_h, pos), while the rows are in flight
+    const QT* qg = (const QT*)sqg;
     if (lane < half) {
-      double sn, cs;
-      rope_sincos((double)a.pos[b], lane, D, a.log2_theta, &sn, &cs);
       double ux = 0.0, uy = 0.0;
-      const QT* qg = sq + (size_t)g * a.grp * D;
       for (int hh = 0; hh < a.grp; ++hh) {
         const double x = load_as_f32<QT>(qg, hh * D + lane);
         const double y = load_as_f32<QT>(qg, hh * D + lane + half);
@@ -212,7 +246,9 @@ __global__ __launch_bounds__(1024) void score_pool_kernel(ScoreArgs a) {
       su[g][lane] = (float)ux;
       su[g][lane + half] = (float)uy;
     }
-    lds_barrier();
+    // LDS operations of one wave complete in order: the reads below see
+    // every lane's writes without a barrier (this keeps the compiler's order)
+    __builtin_amdgcn_wave_barrier();
     float ur[EPL];
 #pragma unroll
     for (int e = 0; e < EPL; ++e) ur[e] = su[g][part * EPL + e];
@@ -266,7 +302,7 @@ kap_status launch_score(const void* q, kap_dtype q_dt, const int32_t* pos, float
   // Up to 16 KV heads the all-heads kernel computes the same per-head scores
   // (same loads and arithmetic per head) and reads each page's head rows
   // together, which measured faster; this kernel serves the other shapes.
-  if (Hkv <= kPoolMaxHeads && (size_t)Hq * D * (q_dt == KAP_BF16 ? 2 : 4) <= kPoolMaxQueryLds)
+  if (Hkv <= kPoolMaxHeads && pool_query_lds(q_dt, Hq, Hkv, D) <= kPoolMaxQueryLds)
     return launch_score_pool(q, q_dt, pos, theta, summ, s_dt, bt, max_pages, seq_lens, B, Hq, Hkv,
                              D, scores, nullptr, stream);
   ScoreArgs a{q, pos, log2((double)theta), summ, bt, max_pages, seq_lens, Hq, Hkv, Hq / Hkv,
@@ -299,7 +335,7 @@ kap_status launch_score_pool(const void* q, kap_dtype q_dt, const int32_t* pos, 
     return fail(KAP_ERR_UNSUPPORTED, "pooled scoring with Hkv=%d > %d", Hkv, kPoolMaxHeads);
   ScoreArgs a{q, pos, log2((double)theta), summ, bt, max_pages, seq_lens, Hq, Hkv, Hq / Hkv,
               scores, pooled};
-  const size_t lds = (size_t)Hq * D * (q_dt == KAP_BF16 ? 2 : 4);
+  const size_t lds = pool_query_lds(q_dt, Hq, Hkv, D);
   if (lds > kPoolMaxQueryLds)
     return fail(KAP_ERR_UNSUPPORTED, "pooled scoring stages %zu query bytes (> %zu)", lds,
                 kPoolMaxQueryLds);

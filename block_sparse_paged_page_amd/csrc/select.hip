@@ -69,20 +69,53 @@ __global__ __launch_bounds__(1024) void select_kernel(SelArgs a) {
   const int gr = blockIdx.x, b = blockIdx.y;
   const int G = a.per_head ? a.Hkv : 1;
   const int tid = threadIdx.x;
-  __shared__ int s_hist[2][4096];  // radix histograms, alternating by pass
+  __shared__ __align__(16) int s_hist[2][4096];  // radix histograms, alternating by pass
   __shared__ int s_suf[8];  // [4] keys above the chosen bin, [5] keys in it
   __shared__ int s_wave[5][33];  // one region per block scan (three passes, ties, output)
   __shared__ uint32_t s_digit;
   __shared__ int s_last;  // the row's last logical page is in its list
-  if (a.cbt) {  // uniform
-    if (tid == 0) s_last = 0;
-    __syncthreads();
+  if (a.cbt && tid == 0) s_last = 0;  // published by the staging barrier below
+  if constexpr (!STAGED) {
+    if (a.cbt) __syncthreads();  // uniform
+  }
+  const int nh = a.per_head ? 1 : a.Hkv;
+  const float* base = a.scores + ((int64_t)b * a.Hkv + (a.per_head ? gr : 0)) * a.max_pages;
+  const int32_t* btrow = a.bt ? a.bt + (int64_t)b * a.max_pages : nullptr;
+  extern __shared__ float s_dyn[];  // STAGED: keys [max_pages], then (compact) the table row
+  int32_t* s_bt = (int32_t*)(s_dyn + a.max_pages);
+  bool bt_lds = false;  // compact view: the table row is in s_bt (block-uniform)
+  if constexpr (STAGED) {
+    float* s_key = s_dyn;
+    if (nh == 1) {  // uniform (arguments only)
+      // one score row (per-head selection, or keys pooled beforehand) and,
+      // for a compact view, the request's table row for the output gather:
+      // both staged whole, with straight-line loads at clamped indices that
+      // wait for nothing (the row's length and split are not needed here;
+      // pages outside the middle are never candidates)
+      const int32_t* bsrc = btrow ? btrow : (const int32_t*)base;  // valid memory either way
+      float kv[KPT];
+      int btv[KPT];
+#pragma unroll
+      for (int u = 0; u < KPT; ++u) kv[u] = base[min(u * 1024 + tid, a.max_pages - 1)];
+#pragma unroll
+      for (int u = 0; u < KPT; ++u) btv[u] = bsrc[min(u * 1024 + tid, a.max_pages - 1)];
+      const float sc = (float)a.Hkv;
+#pragma unroll
+      for (int u = 0; u < KPT; ++u)
+        if (u * 1024 + tid < a.max_pages)
+          s_key[u * 1024 + tid] = a.per_head ? kv[u] : __fdiv_rn(kv[u], sc);
+      if (a.cbt) {
+#pragma unroll
+        for (int u = 0; u < KPT; ++u)
+          if (u * 1024 + tid < a.max_pages) s_bt[u * 1024 + tid] = btv[u];
+        bt_lds = true;
+      }
+    }
   }
   const int L = a.seq_lens[b];
   const int N = min((max(L, 0) + kPage - 1) / kPage, a.max_pages);
   const int na = max(a.anchor[b], 0), nr = max(a.recent[b], 0), nk = a.k_mid[b];
   int32_t* out = a.sel + ((int64_t)b * G + gr) * a.cap;
-  const int32_t* btrow = a.bt ? a.bt + (int64_t)b * a.max_pages : nullptr;
   // slot mapping of the new tokens through the full table (first row of a request)
   auto write_slots = [&](const int32_t* tab) {
     if (gr != 0 || !a.slot) return;
@@ -107,47 +140,11 @@ __global__ __launch_bounds__(1024) void select_kernel(SelArgs a) {
   // row); all heads of a page are folded by one thread in head order.
   // Otherwise (very long tables) each thread reads its own pages directly.
   const int pbase = tid * KPT;
-  const int nh = a.per_head ? 1 : a.Hkv;
-  const float* base = a.scores + ((int64_t)b * a.Hkv + (a.per_head ? gr : 0)) * a.max_pages;
   uint32_t key[KPT];
   uint64_t cand = 0;  // bit j: page t*KPT+j is a middle candidate
-  extern __shared__ float s_dyn[];  // STAGED: keys [max_pages], then (compact) the table row
-  int32_t* s_bt = (int32_t*)(s_dyn + a.max_pages);
-  bool bt_lds = false;  // compact view: the table row is in s_bt (block-uniform)
   if constexpr (STAGED) {
     float* s_key = s_dyn;
-    if (!all && nh == 1) {
-      // compact view: the request's table row goes to LDS for the output
-      // gather; its loads go first, so they have landed with the keys
-      int btv[KPT];
-      if (a.cbt) {
-#pragma unroll
-        for (int u = 0; u < KPT; ++u) btv[u] = btrow[min(u * 1024 + tid, a.max_pages - 1)];
-      }
-      // one score row (per-head selection, or keys pooled beforehand): 8
-      // pages of loads in flight per thread, one round up to 8192 pages
-      constexpr int SU1 = 8;
-      const float sc = (float)a.Hkv;
-      for (int p0 = mid_lo; p0 < mid_hi; p0 += 1024 * SU1) {
-        float v[SU1];
-#pragma unroll
-        for (int u = 0; u < SU1; ++u) {
-          const int p = p0 + u * 1024 + tid;
-          v[u] = p < mid_hi ? base[p] : 0.f;
-        }
-#pragma unroll
-        for (int u = 0; u < SU1; ++u) {
-          const int p = p0 + u * 1024 + tid;
-          if (p < mid_hi) s_key[p] = a.per_head ? v[u] : __fdiv_rn(v[u], sc);
-        }
-      }
-      if (a.cbt) {
-#pragma unroll
-        for (int u = 0; u < KPT; ++u)
-          if (u * 1024 + tid < a.max_pages) s_bt[u * 1024 + tid] = btv[u];
-        bt_lds = true;
-      }
-    } else if (!all) {
+    if (nh != 1 && !all) {
       // up to 8 heads x 4 pages of loads in flight per thread (more would not
       // fit the 128 registers of a 1024-thread block), folded in head order
       constexpr int SU = 4, SG = 8;
@@ -297,27 +294,25 @@ __global__ __launch_bounds__(1024) void select_kernel(SelArgs a) {
     eq_rank = block_exclusive_scan(n_eq, s_wave[3], &tot);
   }
 
-  uint64_t chosen = 0;
+  // chosen mask, branch-free (nested branches per key cost more than the
+  // arithmetic): pages outside the middle are taken whole; a middle page is
+  // taken when its key is above T, or equal to T while ties remain
+  const bool cands = take > 0;
+  using mask_t = typename std::conditional<(KPT > 32), uint64_t, uint32_t>::type;
+  mask_t chosen = 0;
 #pragma unroll
   for (int j = 0; j < KPT; ++j) {
     const int p = pbase + j;
-    bool c = false;
-    if (p < N) {
-      if (all || p < mid_lo || p >= mid_hi) {
-        c = true;
-      } else if (take > 0 && ((cand >> j) & 1ull)) {
-        const uint32_t km = key[j] & pmask;
-        if (km > T) c = true;
-        else if (km == T) {
-          c = eq_rank < remaining;
-          ++eq_rank;
-        }
-      }
-    }
-    if (c) chosen |= 1ull << j;
+    const bool mid = !all && p >= mid_lo && p < mid_hi;
+    const bool isc = cands && ((cand >> j) & 1ull);  // implies mid
+    const uint32_t km = key[j] & pmask;
+    const bool eq = isc && km == T;
+    const bool c = p < N && (!mid || (isc && (km > T || (eq && eq_rank < remaining))));
+    eq_rank += eq ? 1 : 0;
+    chosen |= (mask_t)(c ? 1u : 0u) << j;
   }
-  const int n_ch = __popcll(chosen);
-  if (N > 0 && (N - 1) / KPT == tid && ((chosen >> ((N - 1) % KPT)) & 1ull)) s_last = 1;
+  const int n_ch = KPT > 32 ? __popcll((uint64_t)chosen) : __popc((uint32_t)chosen);
+  if (N > 0 && (N - 1) / KPT == tid && ((chosen >> ((N - 1) % KPT)) & 1u)) s_last = 1;
   int total;
   int pos = block_exclusive_scan(n_ch, s_wave[4], &total);  // (its barriers publish s_last)
   const int64_t row = (int64_t)b * G + gr;
@@ -328,7 +323,7 @@ __global__ __launch_bounds__(1024) void select_kernel(SelArgs a) {
   }
 #pragma unroll
   for (int j = 0; j < KPT; ++j) {
-    if ((chosen >> j) & 1ull) {
+    if ((chosen >> j) & 1u) {
       if (pos < a.cap) {
         out[pos] = pbase + j;
         if (a.cbt) a.cbt[row * a.cap + pos] = bt_lds ? s_bt[pbase + j] : gb[j];
@@ -375,6 +370,7 @@ kap_status launch_select(const float* scores, int32_t B, int32_t Hkv, int32_t ma
   else if (kpt <= 2) KAP_SEL(2);
   else if (kpt <= 4) KAP_SEL(4);
   else if (kpt <= 8) KAP_SEL(8);
+  else if (kpt <= 9) KAP_SEL(9);  // a power-of-two table plus a few pages
   else if (kpt <= 12) KAP_SEL(12);
   else if (kpt <= 16) KAP_SEL(16);
   else if (kpt <= 24) KAP_SEL(24);
