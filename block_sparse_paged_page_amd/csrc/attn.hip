@@ -321,7 +321,7 @@ struct PageFrag {
 enum { kThrottled = 0, kPairs = 1, kStaggered = 2 };
 
 template <int D, int NT, int MODE>
-__global__ __launch_bounds__(64) void attn_partial_bf16(PartArgs a) {
+__global__ __launch_bounds__(64, NT == 1 ? 2 : 1) void attn_partial_bf16(PartArgs a) {
   const PlanIn pin{a.lens, a.B, a.Hkv, a.G, a.width, a.target};
   const bool publish = blockIdx.x == 0 && blockIdx.y == 0;
   const int lane = threadIdx.x;
@@ -435,6 +435,8 @@ __global__ __launch_bounds__(64) void attn_partial_bf16(PartArgs a) {
   const int b = __builtin_amdgcn_readfirstlane(it.b), g = __builtin_amdgcn_readfirstlane(it.g);
   const int p0 = __builtin_amdgcn_readfirstlane(it.p0), p1 = __builtin_amdgcn_readfirstlane(it.p1);
   const int len = __builtin_amdgcn_readfirstlane(it.len);
+  // pair loop: a multiple of four pages (one row tile) runs with two pairs in flight
+  const bool two_pairs = MODE == kPairs && NT == 1 && p1 - p0 >= 4 && ((p1 - p0) & 3) == 0;
   if (!(sp.valid && sb == b && sg == g && sp0 == p0 && sp1 == p1)) {
     // no guess, or rows shorter than the table (wave-uniform)
     load_q(b, g);
@@ -502,6 +504,15 @@ __global__ __launch_bounds__(64) void attn_partial_bf16(PartArgs a) {
     // staggered loop requests the next page itself before consuming it)
     load_at(__builtin_amdgcn_readfirstlane(e0), lg0, buf0);
     load_at(__builtin_amdgcn_readfirstlane(e1), lg1, buf1);
+    // the pair loop over a multiple of four pages keeps two pairs in flight,
+    // so with one row tile the second pair goes out here too.  Unconditionally
+    // (clamped into the item): the compiler counts the loads in flight at the
+    // loop the same way on every path only when every path issues the same
+    // loads; the other items do not consume it (at most one pair per item).
+    if constexpr (MODE == kPairs && NT == 1) {
+      load_page(min(p0 + 2, p1 - 1), buf2);
+      load_page(min(p0 + 3, p1 - 1), buf3);
+    }
   } else {
     // the first four pages go out together (straight-line, past the item
     // clamped to its last page: never consumed unmasked; their table entries
@@ -699,15 +710,35 @@ __global__ __launch_bounds__(64) void attn_partial_bf16(PartArgs a) {
       load_page(min(p + 5, p1 - 1), buf1);
     }
   } else if constexpr (MODE == kPairs) {
-    // the last pair is consumed after the loop, so no pages past the item are
-    // requested (clamped copies would be fetched again: V streams)
-    int p = p0;
-    for (; p + 2 < p1; p += 2) {
+    if (two_pairs) {
+      // Two pairs in flight: while one pair is consumed the other is in
+      // flight, and each buffer pair is refilled right after it is consumed.
+      // Every load is unconditional inside the loop and the last two pairs
+      // are consumed after it, so the compiler waits for exactly the pair
+      // about to be consumed and no page past the item is requested (clamped
+      // copies would be fetched again: V streams).
+      int p = p0;
+      for (; p + 4 < p1; p += 4) {
+        consume2(p, buf0, buf1, true);
+        load_page(p + 4, buf0);
+        load_page(p + 5, buf1);
+        consume2(p + 2, buf2, buf3, true);
+        load_page(p + 6, buf2);
+        load_page(p + 7, buf3);
+      }
       consume2(p, buf0, buf1, true);
-      load_page(p + 2, buf0);
-      load_page(min(p + 3, p1 - 1), buf1);
+      consume2(p + 2, buf2, buf3, true);
+    } else {
+      // one pair in flight; the last pair is consumed after the loop, so no
+      // pages past the item are requested
+      int p = p0;
+      for (; p + 2 < p1; p += 2) {
+        consume2(p, buf0, buf1, true);
+        load_page(p + 2, buf0);
+        load_page(min(p + 3, p1 - 1), buf1);
+      }
+      consume2(p, buf0, buf1, p + 1 < p1);
     }
-    consume2(p, buf0, buf1, p + 1 < p1);
   } else {
     for (int p = p0; p < p1; p += 4) {
       consume2(p, buf0, buf1, p + 1 < p1);
