@@ -290,7 +290,8 @@ struct PartArgs {
 //    the single wave per SIMD computes.
 //  * pairs (short items of a selected view, and 48/64-row tiles at any
 //    length): straight-line loads of one pair at a time, requested as soon as
-//    the previous pair is consumed.
+//    the previous pair is consumed; with one row tile and items of at least
+//    eight pages, two pairs in flight (one consumed while the other arrives).
 // The straight-line disciplines read page-table entries through scalar loads
 // and make every page load unconditional, so the compiler waits for exactly
 // the loads about to be consumed: the staggered loop clamps pages past the
@@ -318,7 +319,8 @@ struct PageFrag {
   int lp;  // logical page (the causal mask compares logical positions)
 };
 
-enum { kThrottled = 0, kPairs = 1, kStaggered = 2 };
+// kPairs2: the pair loop with two pairs in flight (one row tile, items of at least eight pages)
+enum { kThrottled = 0, kPairs = 1, kStaggered = 2, kPairs2 = 3 };
 
 template <int D, int NT, int MODE>
 __global__ __launch_bounds__(64, NT == 1 ? 2 : 1) void attn_partial_bf16(PartArgs a) {
@@ -330,6 +332,8 @@ __global__ __launch_bounds__(64, NT == 1 ? 2 : 1) void attn_partial_bf16(PartArg
   constexpr int KS = D / 32;  // QK k-steps
   constexpr int NC = D / 16;  // PV dim tiles
   constexpr bool STRAIGHT = MODE != kThrottled;  // straight-line loads, scalar table reads
+  constexpr bool PAIRS = MODE == kPairs || MODE == kPairs2;
+  static_assert(MODE != kPairs2 || NT == 1, "two pairs in flight only with one row tile");
   constexpr int SR = 16 * NT;   // rows per slice
   constexpr int CPR = D / 8;    // 16-byte chunks per row
   constexpr int QPL = SR * CPR / 64;  // chunks per lane
@@ -412,7 +416,7 @@ __global__ __launch_bounds__(64, NT == 1 ? 2 : 1) void attn_partial_bf16(PartArg
   // plan-first order, which measured 0.4 us faster there: a burst of start-up
   // loads from every wave at once returns later than the same loads issued
   // after the plan.
-  constexpr bool SPECULATE = MODE != kPairs;
+  constexpr bool SPECULATE = !PAIRS;
   PlanItem sp{0, 0, 0, 0, 0, false};
   if constexpr (SPECULATE) sp = plan_guess(pin, blockIdx.x);
   const int sb = sp.valid ? sp.b : 0, sg = sp.valid ? sp.g : 0;
@@ -435,8 +439,6 @@ __global__ __launch_bounds__(64, NT == 1 ? 2 : 1) void attn_partial_bf16(PartArg
   const int b = __builtin_amdgcn_readfirstlane(it.b), g = __builtin_amdgcn_readfirstlane(it.g);
   const int p0 = __builtin_amdgcn_readfirstlane(it.p0), p1 = __builtin_amdgcn_readfirstlane(it.p1);
   const int len = __builtin_amdgcn_readfirstlane(it.len);
-  // pair loop: a multiple of four pages (one row tile) runs with two pairs in flight
-  const bool two_pairs = MODE == kPairs && NT == 1 && p1 - p0 >= 4 && ((p1 - p0) & 3) == 0;
   if (!(sp.valid && sb == b && sg == g && sp0 == p0 && sp1 == p1)) {
     // no guess, or rows shorter than the table (wave-uniform)
     load_q(b, g);
@@ -504,12 +506,10 @@ __global__ __launch_bounds__(64, NT == 1 ? 2 : 1) void attn_partial_bf16(PartArg
     // staggered loop requests the next page itself before consuming it)
     load_at(__builtin_amdgcn_readfirstlane(e0), lg0, buf0);
     load_at(__builtin_amdgcn_readfirstlane(e1), lg1, buf1);
-    // the pair loop over a multiple of four pages keeps two pairs in flight,
-    // so with one row tile the second pair goes out here too.  Unconditionally
-    // (clamped into the item): the compiler counts the loads in flight at the
-    // loop the same way on every path only when every path issues the same
-    // loads; the other items do not consume it (at most one pair per item).
-    if constexpr (MODE == kPairs && NT == 1) {
+    // two pairs in flight: the second pair goes out here too (clamped into
+    // the item, which has at least eight pages on this path's calls; a
+    // shorter one reads its last page again)
+    if constexpr (MODE == kPairs2) {
       load_page(min(p0 + 2, p1 - 1), buf2);
       load_page(min(p0 + 3, p1 - 1), buf3);
     }
@@ -709,16 +709,18 @@ __global__ __launch_bounds__(64, NT == 1 ? 2 : 1) void attn_partial_bf16(PartArg
       consume2(p + 2, buf2, buf3, p + 3 < p1);
       load_page(min(p + 5, p1 - 1), buf1);
     }
-  } else if constexpr (MODE == kPairs) {
-    if (two_pairs) {
-      // Two pairs in flight: while one pair is consumed the other is in
-      // flight, and each buffer pair is refilled right after it is consumed.
-      // Every load is unconditional inside the loop and the last two pairs
-      // are consumed after it, so the compiler waits for exactly the pair
-      // about to be consumed and no page past the item is requested (clamped
+  } else if constexpr (PAIRS) {
+    if constexpr (MODE == kPairs2) {
+      // Two pairs in flight: A = (p, p + 1) and B = (p + 2, p + 3) went out
+      // in the prologue (clamped into the item); while one pair is consumed
+      // the other is in flight, and each is refilled right after it is
+      // consumed.  Inside the loop every load is unconditional, so the
+      // compiler waits for exactly the pair about to be consumed; the last
+      // one to seven pages are consumed after it, the pages past the first
+      // four a pair at a time, so no page past the item is requested (clamped
       // copies would be fetched again: V streams).
       int p = p0;
-      for (; p + 4 < p1; p += 4) {
+      for (; p + 8 <= p1; p += 4) {
         consume2(p, buf0, buf1, true);
         load_page(p + 4, buf0);
         load_page(p + 5, buf1);
@@ -726,8 +728,15 @@ __global__ __launch_bounds__(64, NT == 1 ? 2 : 1) void attn_partial_bf16(PartArg
         load_page(p + 6, buf2);
         load_page(p + 7, buf3);
       }
-      consume2(p, buf0, buf1, true);
-      consume2(p + 2, buf2, buf3, true);
+      // pages left: 1..7 (uniform); A and B hold the next four (clamped)
+      const int r = p1 - p;
+      consume2(p, buf0, buf1, r >= 2);
+      if (r >= 3) consume2(p + 2, buf2, buf3, r >= 4);
+      for (int q = p + 4; q < p1; q += 2) {  // at most two more pairs, one at a time
+        load_page(q, buf0);
+        load_page(min(q + 1, p1 - 1), buf1);
+        consume2(q, buf0, buf1, q + 1 < p1);
+      }
     } else {
       // one pair in flight; the last pair is consumed after the loop, so no
       // pages past the item are requested
@@ -999,10 +1008,12 @@ kap_status launch_attention(const AttnCall& c) {
 #define KAP_PARTIALS(D, M)                                                            \
   {(const void*)attn_partial_bf16<D, 1, M>, (const void*)attn_partial_bf16<D, 2, M>,      \
    (const void*)attn_partial_bf16<D, 3, M>, (const void*)attn_partial_bf16<D, 4, M>}
-    static const void* const fns[3][2][4] = {
+    static const void* const fns[4][2][4] = {
         {KAP_PARTIALS(64, kThrottled), KAP_PARTIALS(128, kThrottled)},
         {KAP_PARTIALS(64, kPairs), KAP_PARTIALS(128, kPairs)},
-        {KAP_PARTIALS(64, kStaggered), KAP_PARTIALS(128, kStaggered)}};
+        {KAP_PARTIALS(64, kStaggered), KAP_PARTIALS(128, kStaggered)},
+        {{(const void*)attn_partial_bf16<64, 1, kPairs2>, nullptr, nullptr, nullptr},
+         {(const void*)attn_partial_bf16<128, 1, kPairs2>, nullptr, nullptr, nullptr}}};
 #undef KAP_PARTIALS
     const int di = c.D == 128 ? 1 : 0;
     // Short work items (a selected view) are latency-bound, and the 48/64-row
@@ -1016,7 +1027,12 @@ kap_status launch_attention(const AttnCall& c) {
     const int t0 = max(1, min(kTargetItems, resident_blocks(fns[0][di][nt - 1], 64) / slices));
     const int aim = max(t0 - rows, max(t0 / 2, 1));
     const long long chunk = max(((long long)c.width * rows + aim - 1) / aim, (long long)kMinChunk);
-    const int mode = (chunk <= kShortItemPages || nt >= 3) ? kPairs : nt == 1 ? kThrottled : kStaggered;
+    // (items of at least eight pages with one row tile keep two pairs in
+    // flight: 12-page items of a 451-page view 32.9-33.1 -> 32.2-32.5 us;
+    // 6-page items measured slower that way, 20.7-20.9 -> 21.6 us)
+    const int mode = (chunk <= kShortItemPages || nt >= 3)
+                         ? (nt == 1 && chunk >= 8 ? kPairs2 : kPairs)
+                         : nt == 1 ? kThrottled : kStaggered;
     fn = fns[mode][di][nt - 1];
   } else {
     slices = (R + 31) / 32;
