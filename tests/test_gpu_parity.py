@@ -337,6 +337,41 @@ def test_long_ragged_items(q_len, D):
     _long_cache.clear()
 
 
+@pytest.mark.parametrize("counts,D", [([700, 613, 651, 590], 128), ([587, 598, 609, 602], 128),
+                                      ([700, 613, 651, 590], 64)])
+def test_two_pairs_in_flight_tails(counts, D):
+    """The pair loop with two pairs in flight (views with one row tile whose
+    items have at least eight pages): 4 requests with compact views of the
+    given page counts (ragged) under GQA 8:1 with 4 KV heads make 16 rows.  On
+    MI355X the plan splits them into items of 9 pages (first and last sets) or
+    8 pages (second set), and every row ends in a shorter item, so the tails
+    after the unrolled loop take every length from one to seven pages (9-page
+    items: 5 after one pass; last items 7, 1, 3, 5 and 3, 6, 1, 2).  The query
+    sits at the sequence end and inside the context (the causal rule on the
+    compact view's logical pages)."""
+    w = W.spec("qwen32b_128k", B=4, seq_lens=[23000, 20011, 30000, 25555], Hq=32, Hkv=4, D=D)
+    c = Case(w)
+    N = w.n_pages
+    counts = np.array(counts, np.int32)
+    rng = np.random.default_rng(77)
+    cap = int(counts.max())
+    sel = np.full((w.B, 1, cap), -1, np.int32)
+    for bi in range(w.B):
+        pages = rng.choice(int(N[bi]), size=int(counts[bi]), replace=False)
+        sel[bi, 0, :counts[bi]] = np.sort(pages).astype(np.int32)
+    cnt = counts.reshape(w.B, 1)
+    cbt, clog, clen, _ = kap.compact_view(t(sel), t(cnt), c.bt, c.L, c.pos, 1)
+    keys = oracle.keys_selected(sel, cnt, c.b["seq_lens"])
+    inside = (c.b["positions"].astype(np.int64) * 2 // 3).astype(np.int32)
+    for pos in (c.b["positions"], inside):
+        lse = torch.empty((w.B, w.Hq), dtype=torch.float32, device="cuda")
+        out = kap.decode_attn(c.q, t(pos), c.K, c.V, cbt, clen, G=1, lse=lse, logical=clog)
+        torch.cuda.synchronize()
+        ref, lref = oracle.attend(c.b["q"][:, None], pos, c.Kl, c.Vl, c.btl, keys, 1, w.Hkv)
+        err = _check_attn(c, out, lse, ref[:, 0], lref[:, 0])
+        print(f"[two pairs, counts {counts.tolist()}, D {D}] max rel err {err:.2e}", flush=True)
+
+
 @pytest.mark.parametrize("Hq,Hkv,D,dtype", [
     (8, 8, 128, "bf16"),     # MHA: one query row per KV head
     (16, 1, 64, "bf16"),     # MQA, head_dim 64
