@@ -4,8 +4,8 @@ The library's host routing source (CPU-offloaded routing) and the C oracle are
 built with -fsanitize=address,undefined into one test executable
 (tests/sanitize/route_check.cpp) that runs both on small seeded inputs and
 their degenerate cases; any invalid access, leak or undefined operation aborts
-it.  The GPU sources are not part of this build: their device code cannot be
-sanitized on this hardware.
+it.  The HIP sources are left out: their device code is not instrumented by
+these sanitizers.
 """
 import os
 import shutil
