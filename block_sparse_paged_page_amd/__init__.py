@@ -18,3 +18,4 @@ from ._lib import (  # noqa: F401
     proxy_workspace_bytes, score_blocks, score_pool_blocks, select_compact, select_topk,
     update_summary, verify_attn, version,
 )
+from .tags import format_split_tag, middle_count, parse_split_tag  # noqa: F401,E402
