@@ -550,20 +550,30 @@ __global__ __launch_bounds__(64, NT == 1 ? 2 : 1) void attn_partial_bf16(PartArg
              (dim & 7);
     };
     // Rows r of query i = r / grp share one angle: one fp64 sincos per
-    // distinct position of the slice, then the rows of that position.  Rows
-    // past R hold zeros and go with the last position (they stay zero).
-    const int i_lo = row0 / a.grp, i_hi = (min(row0 + SR, a.R) - 1) / a.grp;
+    // distinct position of the slice, then the rows of that position.  The
+    // fragment offset of (row rr, dim) is frag_at(0, dim) plus a row term, so
+    // each lane's two offsets are computed once; both halves are rounded by
+    // one conversion instruction.  Rows past R are written as zeros.
+    const int fx = frag_at(0, pr), fy = frag_at(0, pr + HALF);
+    auto row_term = [](int rr) { return (rr >> 4) * (KS * 512) + (rr & 15) * 8; };
+    const int rq = min(SR, a.R - row0);  // rows of this slice that hold queries
+    const int i_lo = row0 / a.grp, i_hi = (row0 + rq - 1) / a.grp;
     for (int i = i_lo; i <= i_hi; ++i) {
       double sn, cs;
       rope_sincos((double)pos_b + (double)i, pr, D, a.log2_theta, &sn, &cs);
       const int ra = max(i * a.grp - row0, 0);
-      const int rb = (i == i_hi) ? SR : min((i + 1) * a.grp - row0, SR);
+      const int rb = min((i + 1) * a.grp - row0, rq);
 #pragma unroll 4
       for (int rr = ra + rsub; rr < rb; rr += LPP) {
         const float2 v = rope_pair(bf16_to_f32(sraw[rr][pr]), bf16_to_f32(sraw[rr][pr + HALF]), sn, cs);
-        sqh[frag_at(rr, pr)] = f32_to_bf16(v.x);
-        sqh[frag_at(rr, pr + HALF)] = f32_to_bf16(v.y);
+        const uint32_t h = pack_bf16x2(v.x, v.y);
+        sqh[fx + row_term(rr)] = (uint16_t)h;
+        sqh[fy + row_term(rr)] = (uint16_t)(h >> 16);
       }
+    }
+    for (int rr = rq + rsub; rr < SR; rr += LPP) {
+      sqh[fx + row_term(rr)] = 0;
+      sqh[fy + row_term(rr)] = 0;
     }
 #pragma unroll
     for (int t = 0; t < NT; ++t) {
