@@ -16,7 +16,9 @@ value = B * k proposal tokens per cycle / cycle time (tokens/s), timed by wall
 clock around K uninstrumented cycles.  Per-call durations come from HIP events
 on the launch stream in a second timed pass of the same K cycles, one event
 after every call (each event costs ~3.5 us of GPU time, which is why the
-headline pass has none; that pass's cycle time is reported too).
+headline pass has none; that pass's cycle time is reported too).  The 4
+decodes of a cycle sit between two events, so the decode time is a quarter of
+that interval.
 The full-context decode (the same kernel over the whole table) is timed
 separately for the comparison.  The CPU baseline times the oracle on request 0
 of the same batch.
@@ -893,7 +895,7 @@ def main():
     dec_out = torch.empty((B, Hq, D), dtype=torch.bfloat16, device=dev)
     ver_out = torch.empty((B, w.q_len, Hq, D), dtype=torch.bfloat16, device=dev)
     stream = torch.cuda.current_stream()
-    n_ev = 3 + K_PROPOSE
+    n_ev = 4
     state = {"layer": 0}
 
     def next_layer():
@@ -951,16 +953,25 @@ def main():
                     r()
         torch.cuda.synchronize()
 
+    # Instrumented step: events before the route, after it, after the 4th
+    # decode and after the verify.  The 4 decodes run back to back between two
+    # events, so each decode's time carries a quarter of an event's overhead
+    # instead of a whole one.
     def step(i, ev):
+        calls = runs[i % period]
         ev[0].record(stream)
-        for c, fn in enumerate(runs[i % period]):
+        calls[0]()
+        ev[1].record(stream)
+        for fn in calls[1:1 + K_PROPOSE]:
             fn()
-            ev[c + 1].record(stream)
+        ev[2].record(stream)
+        calls[1 + K_PROPOSE]()
+        ev[3].record(stream)
 
     # The headline: K steps with nothing between the calls.  A timing event
     # recorded on the stream costs ~3.5 us of GPU time here, so the per-call
-    # durations come from a second pass of the same K steps with an event
-    # after every call (its own wall time is reported beside the headline).
+    # durations come from a second pass of the same K steps with events
+    # around the calls (its own wall time is reported beside the headline).
     torch.cuda.synchronize()
     t_start = time.perf_counter()
     for i in range(args.steps):
@@ -978,8 +989,8 @@ def main():
     torch.cuda.synchronize()
     ms_step_events = 1e3 * (time.perf_counter() - t_ev) / args.steps
     route_ms = np.mean([e[0].elapsed_time(e[1]) for e in evs])
-    dec_ms = np.mean([e[1 + j].elapsed_time(e[2 + j]) for e in evs for j in range(K_PROPOSE)])
-    ver_ms = np.mean([e[1 + K_PROPOSE].elapsed_time(e[2 + K_PROPOSE]) for e in evs])
+    dec_ms = np.mean([e[1].elapsed_time(e[2]) for e in evs]) / K_PROPOSE
+    ver_ms = np.mean([e[2].elapsed_time(e[3]) for e in evs])
 
     # Router-style selection (a K-summary router picks pages for every
     # proposal step with that step's own query): the same cycle with the route
