@@ -441,8 +441,14 @@ __global__ __launch_bounds__(64, NT == 1 ? 2 : 1) void attn_partial_bf16(PartArg
   const int len = __builtin_amdgcn_readfirstlane(it.len);
   if (!(sp.valid && sb == b && sg == g && sp0 == p0 && sp1 == p1)) {
     // no guess, or rows shorter than the table (wave-uniform)
+    // The position comes through the constant space like the table entries:
+    // as a plain load the compiler makes it a vector load (the kernel's own
+    // stores keep it from proving the array read-only), and moving it to a
+    // scalar register then waits for every vector load before it (the query
+    // rows), which held the table entries, and so the first pages, back by
+    // one round trip (selected decode at 128K: 29.8-29.9 -> 29.0-29.1 us).
     load_q(b, g);
-    pos_b = SPECULATE ? ld_uniform(a.pos + b) : a.pos[b];
+    pos_b = SPECULATE ? ld_uniform(a.pos + b) : as_const(a.pos)[b];
     load_entries(b, g, p0, p1, false);
   }
   pos_b = __builtin_amdgcn_readfirstlane(pos_b);
