@@ -1017,6 +1017,7 @@ kap_status launch_attention(const AttnCall& c) {
   a.log2_theta = log2((double)c.theta);
   const void* fn;
   int slices;
+  int item_cap = kTargetItems;
   if (c.dtype == KAP_BF16) {
     // one row slice whenever the rows fit in 64, so each page is read once per (b, g)
     const int nt = R <= 16 ? 1 : R <= 32 ? 2 : R <= 48 ? 3 : 4;
@@ -1046,16 +1047,26 @@ kap_status launch_attention(const AttnCall& c) {
     // (items of at least eight pages with one row tile keep two pairs in
     // flight: 12-page items of a 451-page view 32.9-33.1 -> 32.2-32.5 us;
     // 6-page items measured slower that way, 20.7-20.9 -> 21.6 us)
-    const int mode = (chunk <= kShortItemPages || nt >= 3)
-                         ? (nt == 1 && chunk >= 8 ? kPairs2 : kPairs)
-                         : nt == 1 ? kThrottled : kStaggered;
+    int mode = (chunk <= kShortItemPages || nt >= 3)
+                   ? (nt == 1 && chunk >= kPairs2MinPages ? kPairs2 : kPairs)
+                   : nt == 1 ? kThrottled : kStaggered;
+    // Items of four to seven pages are made eight long instead (fewer items,
+    // capped so that a row of the table's width splits into eight-page
+    // items) and run with two pairs in flight: two round trips per item
+    // instead of three or four.  113-page views of 64 rows (Llama-shaped
+    // 32K, B = 8): 1216 items of 6 pages 20.2 us -> 960 items of 8 pages
+    // 19.8 us; views of 1 to 3 pages per item keep their many short items.
+    if (mode == kPairs && nt == 1 && chunk >= 4 && c.width >= kPairs2MinPages) {
+      item_cap = rows * ((c.width + kPairs2MinPages - 1) / kPairs2MinPages);
+      mode = kPairs2;
+    }
     fn = fns[mode][di][nt - 1];
   } else {
     slices = (R + 31) / 32;
     fn = c.D == 128 ? (const void*)attn_partial_f32<128> : (const void*)attn_partial_f32<64>;
   }
   // one round of resident waves, shared among the row slices
-  a.target = max(1, min(kTargetItems, resident_blocks(fn, 64) / slices));
+  a.target = max(1, min(item_cap, resident_blocks(fn, 64) / slices));
   void* args[] = {&a};
   const int max_items = a.target + c.B * c.Hkv;  // the plan never makes more
   const hipError_t e = hipLaunchKernel(fn, dim3(max_items, slices), dim3(64), args, 0, c.stream);

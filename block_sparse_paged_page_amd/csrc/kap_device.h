@@ -14,6 +14,7 @@ constexpr int kPage = 16;            // tokens per KV page
 constexpr int kTargetItems = 1280;   // split-K work items aimed at per call (measured best at 128K, B = 4)
 constexpr int kMinChunk = 2;         // minimum pages per work item
 constexpr int kShortItemPages = 32;  // items up to this many pages run the pair loop
+constexpr int kPairs2MinPages = 8;   // one-tile items this long keep two pairs in flight
 constexpr int kMaxSelectPages = 65536;
 constexpr int kMaxPlanRows = 4096;      // batch x KV heads per attention call
 
