@@ -189,7 +189,9 @@ def test_workspace_sizes_are_monotone(lib):
     b = kap.attn_workspace_bytes(4, 4, 64, 8, 128)
     assert 0 < a < b
     assert kap.attn_workspace_bytes(0, 1, 8, 2, 64) == 0
-    assert kap.proxy_workspace_bytes(8, 4096, 4096) == (4096 // 128) * 8 * 4096 * 4
+    # one partial per group of four 128-row splits of W_q
+    assert kap.proxy_workspace_bytes(8, 4096, 4096) == (4096 // 128 // 4) * 8 * 4096 * 4
+    assert kap.proxy_workspace_bytes(3, 640, 512) == 2 * 3 * 512 * 4
 
 
 def test_proxy_validation(lib):

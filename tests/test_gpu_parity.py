@@ -695,10 +695,11 @@ def test_proxy_query_and_per_head_routing():
 
 
 @pytest.mark.parametrize("B,dm,n_out", [(1, 4096, 4096), (3, 256, 512), (8, 4096, 4096),
-                                        (16, 1024, 1536)])
+                                        (16, 1024, 1536), (5, 640, 1024)])
 def test_proxy_query_shapes(B, dm, n_out):
     """The proxy GEMV on the matrix cores: batch rows padded to 16 (B = 1, 3,
-    8, 16), row splits of 128, column tiles of 128; within 1e-5 |q| of the
+    5, 8, 16), row splits of 128 added in groups of four (d_model 256 and 640
+    end in a partial group), column tiles of 128; within 1e-5 |q| of the
     oracle's fp64 sum of exact bf16 products, per batch row."""
     rng = np.random.default_rng(1000 + B)
     hidden = W.gen._to_bf16_bits(rng.standard_normal((B, dm)).astype(np.float32))
