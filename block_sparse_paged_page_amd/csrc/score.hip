@@ -129,10 +129,10 @@ __global__ __launch_bounds__(256) void score_kernel(ScoreArgs a) {
 }
 
 // All KV heads of a run of pages in one block, with the head-pooled key.
-// Grid (B, runs of 64 pages); one wave per KV head (Hkv <= 16).  Each wave
-// reads its head's 64 summary rows exactly as score_kernel does (same access
+// Grid (B, runs of 32 pages); one wave per KV head (Hkv <= 16).  Each wave
+// reads its head's 32 summary rows exactly as score_kernel does (same access
 // pattern and arithmetic, so the per-head scores are the same), and the waves
-// of a block read the same 64 pages, so each page's contiguous run of head
+// of a block read the same 32 pages, so each page's contiguous run of head
 // rows is fetched together.  The run's scores are then folded over the heads
 // in head order, in fp32 with round-to-nearest adds and one rounded division:
 // the same mean the top-K forms for pooled selection, so the top-K then reads
@@ -143,12 +143,16 @@ __global__ __launch_bounds__(256) void score_kernel(ScoreArgs a) {
 // the summary rows are requested as soon as the table entries land, and the
 // group query is rotated and summed in the wave's own LDS region while the
 // rows are in flight.  Only the fold over heads needs the whole block.
-// Pages per block: 16 row loads in flight per wave, at most 64 pages (one
-// page-table entry per lane).
+// Pages per block: at most 32 (eight 16-byte row loads in flight per lane at
+// D = 128 in bf16).  Runs of 64 pages gave 320 blocks for 8 requests of 40K
+// tokens, so a quarter of the CUs held two blocks and set the end: 32-page
+// runs took that scoring call from 12.4-13.0 to 10.1-10.4 us, and the 128K
+// pooled scoring from 15.3-15.7 to 13.7-15.4 us (runs of 16 pages: no better
+// at 40K, slower at 128K).
 template <int D, typename ST>
 constexpr int pool_pages_per_block() {
-  return 16 * (64 / (D / (16 / (int)sizeof(ST)))) < 64 ? 16 * (64 / (D / (16 / (int)sizeof(ST))))
-                                                        : 64;
+  return 16 * (64 / (D / (16 / (int)sizeof(ST)))) < 32 ? 16 * (64 / (D / (16 / (int)sizeof(ST))))
+                                                        : 32;
 }
 constexpr int kPoolMaxHeads = 16;
 constexpr size_t kPoolMaxQueryLds = 64 * 1024;
