@@ -147,8 +147,8 @@ __global__ __launch_bounds__(256) void score_kernel(ScoreArgs a) {
 // D = 128 in bf16).  Runs of 64 pages gave 320 blocks for 8 requests of 40K
 // tokens, so a quarter of the CUs held two blocks and set the end: 32-page
 // runs took that scoring call from 12.4-13.0 to 10.1-10.4 us, and the 128K
-// pooled scoring from 15.3-15.7 to 13.7-15.4 us (runs of 16 pages: no better
-// at 40K, slower at 128K).
+// pooled scoring from 15.3-15.7 to 13.7-15.4 us (runs of 16, 24 and 48
+// pages: no better at 40K, slower at 128K).
 template <int D, typename ST>
 constexpr int pool_pages_per_block() {
   return 16 * (64 / (D / (16 / (int)sizeof(ST)))) < 32 ? 16 * (64 / (D / (16 / (int)sizeof(ST))))
