@@ -69,6 +69,13 @@ __device__ __forceinline__ void rope_sincos(double pos, int pair, int D, double 
   sincos(r, s, c);
 }
 
+// sin and cos of one position step for pair `pair` (the angle rope_sincos
+// advances by per position), for angle-addition steps between positions.
+__device__ __forceinline__ void rope_step(int pair, int D, double log2_theta, double* s, double* c) {
+  const double inv_freq = exp2(-(2.0 * pair / D) * log2_theta);
+  sincos(inv_freq, s, c);
+}
+
 // Streaming loads with the non-temporal policy, which marks the lines for
 // early eviction instead of keeping them cached.  On MI355X it raises the
 // sustained read rate of a plain stream from about 6.3 to 7.2 TB/s, and of
