@@ -372,6 +372,76 @@ def test_two_pairs_in_flight_tails(counts, D):
         print(f"[two pairs, counts {counts.tolist()}, D {D}] max rel err {err:.2e}", flush=True)
 
 
+@pytest.mark.parametrize("D", [128, 64])
+def test_short_items_made_eight_pages(D):
+    """Views whose items would be four to seven pages run as eight-page items
+    with two pairs in flight: 2 requests x 8 KV heads (16 rows) with compact
+    views of 300 and 277 pages bound the item length at ceil(300 * 16 / 1264)
+    = 4 pages on the host, so the item cap drops to 16 * ceil(300 / 8) and the
+    device plan splits the ragged rows into items of 8 pages, each row ending
+    in a shorter one (4 and 5 pages).  The query sits at the sequence end and
+    inside the context."""
+    w = W.spec("qwen32b_128k", B=2, seq_lens=[9000, 7777], Hq=64, Hkv=8, D=D)
+    c = Case(w)
+    N = w.n_pages
+    counts = np.array([300, 277], np.int32)
+    rng = np.random.default_rng(78)
+    cap = int(counts.max())
+    sel = np.full((w.B, 1, cap), -1, np.int32)
+    for bi in range(w.B):
+        pages = rng.choice(int(N[bi]), size=int(counts[bi]), replace=False)
+        sel[bi, 0, :counts[bi]] = np.sort(pages).astype(np.int32)
+    cnt = counts.reshape(w.B, 1)
+    cbt, clog, clen, _ = kap.compact_view(t(sel), t(cnt), c.bt, c.L, c.pos, 1)
+    keys = oracle.keys_selected(sel, cnt, c.b["seq_lens"])
+    inside = (c.b["positions"].astype(np.int64) * 3 // 4).astype(np.int32)
+    for pos in (c.b["positions"], inside):
+        lse = torch.empty((w.B, w.Hq), dtype=torch.float32, device="cuda")
+        out = kap.decode_attn(c.q, t(pos), c.K, c.V, cbt, clen, G=1, lse=lse, logical=clog)
+        torch.cuda.synchronize()
+        ref, lref = oracle.attend(c.b["q"][:, None], pos, c.Kl, c.Vl, c.btl, keys, 1, w.Hkv)
+        err = _check_attn(c, out, lse, ref[:, 0], lref[:, 0])
+        print(f"[eight-page items, D {D}] max rel err {err:.2e}", flush=True)
+
+
+def test_values_beyond_the_fp16_range():
+    """The split partials are bf16 outputs normalized by their own sums, so
+    they keep the range of the KV values: with every V value scaled by 2^17
+    (up to about 1e5, past fp16's 65504, exact in bf16) the selected decode,
+    the full decode and a 4-token verify still match the oracle."""
+    w = W.spec("qwen32b_128k", B=2, seq_lens=[8192, 6001])
+    c = Case(w)
+    scale = np.float32(2.0 ** 17)
+    vl = (oracle.widen(c.Vl).astype(np.float32) * scale)
+    assert np.nanmax(np.abs(vl)) > 65504.0
+    vbits = W.gen._to_bf16_bits(vl)
+    assert np.array_equal(oracle.widen(vbits)[np.isfinite(vl)], vl[np.isfinite(vl)].astype(np.float64))
+    phys = torch.from_numpy(c.b["phys"].astype(np.int64)).cuda()
+    V = torch.zeros_like(c.V)
+    V[phys] = t(vbits)
+    cap = c.budget()
+    sel, cnt = oracle.select(oracle.score(c.b["q"], c.b["positions"], c.summ_l, c.btl,
+                                          c.b["seq_lens"], w.Hkv).astype(np.float32),
+                             c.b["seq_lens"], c.b["anchor"], c.b["recent"], c.k_mid_h, cap)
+    cbt, clog, clen, _ = kap.compact_view(t(sel), t(cnt), c.bt, c.L, c.pos, 1)
+    for name, keys, tab in (("selected", oracle.keys_selected(sel, cnt, c.b["seq_lens"]), (cbt, clen, clog)),
+                            ("full", oracle.keys_full(c.b["seq_lens"]), (c.bt, c.L, None))):
+        lse = torch.empty((w.B, w.Hq), dtype=torch.float32, device="cuda")
+        out = kap.decode_attn(c.q, c.pos, c.K, V, tab[0], tab[1], G=1, lse=lse, logical=tab[2])
+        torch.cuda.synchronize()
+        ref, lref = oracle.attend(c.b["q"][:, None], c.b["positions"], c.Kl, vbits, c.btl, keys, 1,
+                                  w.Hkv)
+        err = _check_attn(c, out, lse, ref[:, 0], lref[:, 0])
+        print(f"[V x 2^17, {name} decode] max rel err {err:.2e}", flush=True)
+    vl_ = torch.empty((w.B, w.q_len, w.Hq), dtype=torch.float32, device="cuda")
+    vout = kap.verify_attn(c.qv, c.pos, c.K, V, c.bt, c.L, lse=vl_)
+    torch.cuda.synchronize()
+    ref, lref = oracle.attend(c.b["qv"], c.b["positions"], c.Kl, vbits, c.btl,
+                              oracle.keys_full(c.b["seq_lens"]), 1, w.Hkv)
+    err = _check_attn(c, vout, vl_, ref, lref)
+    print(f"[V x 2^17, verify] max rel err {err:.2e}", flush=True)
+
+
 @pytest.mark.parametrize("Hq,Hkv,D,dtype", [
     (8, 8, 128, "bf16"),     # MHA: one query row per KV head
     (16, 1, 64, "bf16"),     # MQA, head_dim 64
