@@ -1117,7 +1117,7 @@ kap_status launch_attention(const AttnCall& c) {
   ma.grp = grp;
   ma.R = R;
   dim3 mgrid(c.B * c.Hkv, R);
-  const bool ph = c.dtype == KAP_BF16;  // the MFMA partials are fp16, the fp32 path's fp32
+  const bool ph = c.dtype == KAP_BF16;  // the MFMA partials are bf16, the fp32 path's fp32
   if (c.D == 128) {
     if (ph) hipLaunchKernelGGL((attn_merge_kernel<128, true>), mgrid, dim3(256), 0, c.stream, ma);
     else hipLaunchKernelGGL((attn_merge_kernel<128, false>), mgrid, dim3(256), 0, c.stream, ma);
