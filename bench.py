@@ -98,6 +98,22 @@ def algorithmic_bytes(w, b, sel_pages):
     return dict(decode_selected=dec_sel, decode_full=dec_full, verify=verify, score=score)
 
 
+def pools_alloc(pages, Hkv, D, dtype, device):
+    """Zeroed K and V pools of one layer in one allocation, placed as
+    kap_kv_pool_layout advises."""
+    return kap.alloc_kv_pools(pages, Hkv, D, dtype, device, zero=True)
+
+
+def layer_pools(b, n):
+    """The batch's K and V pools and n - 1 copies (one per further layer)."""
+    Ks, Vs = [b["K"]], [b["V"]]
+    for _ in range(n - 1):
+        k, v = kap.copy_kv_pools(b["K"], b["V"])
+        Ks.append(k)
+        Vs.append(v)
+    return Ks, Vs
+
+
 def kernel_source_hash():
     """Hash of the attention kernel's code (attn.hip and the device-side header
     it shares) with comments and blank lines removed, so that only code changes
@@ -280,7 +296,7 @@ def _sweep(args, dev, w, label):
     """Routing calls, the selected and full decodes, and the retention sweep of
     one uniform-length workload; returns the result line as a dict."""
     B, Hq, Hkv, D = w.B, w.Hq, w.Hkv, w.D
-    b = W.make_device(w, dev, needle_dir=W.aimed_dirs(w))
+    b = W.make_device(w, dev, needle_dir=W.aimed_dirs(w), alloc_pools=pools_alloc)
     to = _upload(b, dev)
     bt, L, pos = to(b["bt"]), to(b["seq_lens"]), to(b["positions"])
     anchor, recent = to(b["anchor"]), to(b["recent"])
@@ -289,8 +305,7 @@ def _sweep(args, dev, w, label):
     kap.build_summary(b["K"], bt, L, S)
     layer_bytes = 2 * b["K"].numel() * EB
     R = max(4, int(math.ceil(8 * 2**30 / layer_bytes)))
-    Ks = [b["K"]] + [b["K"].clone() for _ in range(R - 1)]
-    Vs = [b["V"]] + [b["V"].clone() for _ in range(R - 1)]
+    Ks, Vs = layer_pools(b, R)
     Ss = [S] + [S.clone() for _ in range(R - 1)]
     torch.cuda.synchronize()
     st = torch.cuda.current_stream()
@@ -353,7 +368,7 @@ def run_early_route(args, dev):
     w = W.spec("early_route_40k", B=args.batch if args.batch != 4 else 8)
     B, Hq, Hkv, D = w.B, w.Hq, w.Hkv, w.D
     layers = 32
-    b = W.make_device(w, dev)
+    b = W.make_device(w, dev, alloc_pools=pools_alloc)
     to = _upload(b, dev)
     bt, L, pos = to(b["bt"]), to(b["seq_lens"]), to(b["positions"])
     anchor, recent, kmid = to(b["anchor"]), to(b["recent"]), to(b["k_mid"])
@@ -361,8 +376,7 @@ def run_early_route(args, dev):
     kap.build_summary(b["K"], bt, L, S)
     g = torch.Generator(device=dev)
     g.manual_seed(int(w.seed) * 7919)
-    Ks = [b["K"]] + [b["K"].clone() for _ in range(layers - 1)]
-    Vs = [b["V"]] + [b["V"].clone() for _ in range(layers - 1)]
+    Ks, Vs = layer_pools(b, layers)
     Ss = [S] + [S.clone() for _ in range(layers - 1)]
     Wq = [(torch.randn((w.hidden_dim, Hq * D), generator=g, device=dev) / 64.0).bfloat16()
           for _ in range(layers)]
@@ -499,15 +513,14 @@ def run_early_route_cpu(args, dev):
     w = W.spec("early_route_40k", B=args.batch if args.batch != 4 else 8)
     B, Hq, Hkv, D = w.B, w.Hq, w.Hkv, w.D
     layers = 32
-    b = W.make_device(w, dev)
+    b = W.make_device(w, dev, alloc_pools=pools_alloc)
     to = _upload(b, dev)
     bt, L, pos = to(b["bt"]), to(b["seq_lens"]), to(b["positions"])
     S = torch.zeros((b["pool_pages"], Hkv, D), dtype=torch.bfloat16, device=dev)
     kap.build_summary(b["K"], bt, L, S)
     g = torch.Generator(device=dev)
     g.manual_seed(int(w.seed) * 7919)
-    Ks = [b["K"]] + [b["K"].clone() for _ in range(layers - 1)]
-    Vs = [b["V"]] + [b["V"].clone() for _ in range(layers - 1)]
+    Ks, Vs = layer_pools(b, layers)
     Wq = [(torch.randn((w.hidden_dim, Hq * D), generator=g, device=dev) / 64.0).bfloat16()
           for _ in range(layers)]
     hid = [torch.randn((B, w.hidden_dim), generator=g, device=dev).bfloat16() for _ in range(layers)]
@@ -615,7 +628,7 @@ def run_mixed(args, dev):
 def _mixed(args, dev):
     w = W.spec("mixed_serving")
     B, Hq, Hkv, D = w.B, w.Hq, w.Hkv, w.D
-    b = W.make_device(w, dev, needle_dir=W.aimed_dirs(w))
+    b = W.make_device(w, dev, needle_dir=W.aimed_dirs(w), alloc_pools=pools_alloc)
     to = _upload(b, dev)
     bt, L, pos = to(b["bt"]), to(b["seq_lens"]), to(b["positions"])
     anchor, recent = to(b["anchor"]), to(b["recent"])
@@ -687,7 +700,7 @@ def run_commit(args, dev):
     Every call rotates over layer copies like the headline step."""
     w = W.spec("qwen32b_128k", B=args.batch, q_len=K_PROPOSE + 1)
     B, Hq, Hkv, D = w.B, w.Hq, w.Hkv, w.D
-    b = W.make_device(w, dev)
+    b = W.make_device(w, dev, alloc_pools=pools_alloc)
     to = _upload(b, dev)
     bt, L, pos = to(b["bt"]), to(b["seq_lens"]), to(b["positions"])
     L2 = to((b["seq_lens"] + w.q_len).astype(np.int32))
@@ -705,7 +718,7 @@ def run_commit(args, dev):
     R = args.layers or 8
     layers = [Layer(b["K"], b["V"], S0)]
     for _ in range(R - 1):
-        layers.append(Layer(b["K"].clone(), b["V"].clone(), S0.clone()))
+        layers.append(Layer(*kap.copy_kv_pools(b["K"], b["V"]), S0.clone()))
     ws = torch.empty(kap.attn_workspace_bytes(B, w.q_len, Hq, Hkv, D), dtype=torch.uint8, device=dev)
     pooled = torch.empty((B, 1, bt.shape[1]), dtype=torch.float32, device=dev)
     sel = torch.empty((B, 1, cap), dtype=torch.int32, device=dev)
@@ -781,7 +794,7 @@ def run_workspace(args, dev):
     the one-time copy and both decode rates, each over 8 rotating layer copies."""
     w = W.spec("qwen32b_128k", B=args.batch)
     B, Hq, Hkv, D = w.B, w.Hq, w.Hkv, w.D
-    b = W.make_device(w, dev)
+    b = W.make_device(w, dev, alloc_pools=pools_alloc)
     to = _upload(b, dev)
     bt, L, pos = to(b["bt"]), to(b["seq_lens"]), to(b["positions"])
     anchor, recent, k_mid = to(b["anchor"]), to(b["recent"]), to(b["k_mid"])
@@ -793,7 +806,7 @@ def run_workspace(args, dev):
     sel, cnt = kap.select_topk(scores, L, anchor, recent, k_mid, cap, cap)
     cbt, clog, clen, _ = kap.compact_view(sel, cnt, bt, L, pos, 1)
     R = args.layers or 8
-    pools = [(b["K"], b["V"])] + [(b["K"].clone(), b["V"].clone()) for _ in range(R - 1)]
+    pools = list(zip(*layer_pools(b, R)))
     wss = [kap.materialize_view(K, V, cbt) for K, V in pools]
     ws = torch.empty(kap.attn_workspace_bytes(B, 1, Hq, Hkv, D), dtype=torch.uint8, device=dev)
     out = torch.empty((B, Hq, D), dtype=torch.bfloat16, device=dev)
@@ -859,7 +872,7 @@ def main():
     w = W.spec("qwen32b_128k", B=args.batch)
     B, Hq, Hkv, D = w.B, w.Hq, w.Hkv, w.D
     t0 = time.time()
-    b = W.make_device(w, dev, needle_dir=W.aimed_dirs(w))
+    b = W.make_device(w, dev, needle_dir=W.aimed_dirs(w), alloc_pools=pools_alloc)
     torch.cuda.synchronize()
     log(f"generated {w.name} B={B} on device in {time.time() - t0:.1f}s", q)
 
@@ -879,7 +892,7 @@ def main():
     R = args.layers or max(8, int(math.ceil(16 * 2**30 / layer_bytes)))
     layers = [Layer(b["K"], b["V"], S0)]
     for _ in range(R - 1):
-        layers.append(Layer(b["K"].clone(), b["V"].clone(), S0.clone()))
+        layers.append(Layer(*kap.copy_kv_pools(b["K"], b["V"]), S0.clone()))
     torch.cuda.synchronize()
     log(f"{R} layer copies, {R * layer_bytes / 2**30:.1f} GiB", q)
 

@@ -12,9 +12,10 @@ holding bf16 bit patterns; fp32 data are torch.float32; index tensors int32
 """
 from ._lib import (  # noqa: F401
     BF16, F32, PLAN_FULL_BOUNDARY, PLAN_FULL_CAPACITY, PLAN_FULL_MARGIN, PLAN_SELECTED, KapError,
-    KapLibraryMissing, append_kv, attn_workspace_bytes, budget_from_ratio, choose_plan,
-    build_summary, compact_view, decode_attn, decode_attn_noalloc, diag_stream_read, host_proxy_query,
-    host_score_blocks, host_select_topk, lib_path, load, materialize_view, proxy_query,
+    KapLibraryMissing, alloc_kv_pools, append_kv, attn_workspace_bytes, budget_from_ratio,
+    choose_plan, build_summary, compact_view, copy_kv_pools, decode_attn, decode_attn_noalloc,
+    diag_stream_read, host_proxy_query, host_score_blocks, host_select_topk, kv_pool_layout,
+    lib_path, load, materialize_view, proxy_query,
     proxy_workspace_bytes, score_blocks, score_pool_blocks, select_compact, select_topk,
     update_summary, verify_attn, version,
 )

@@ -41,6 +41,7 @@ _SIGS = {
     "kap_select_compact": ([_P, _I32, _I32, _I32, _P, _I32, _I32, _P, _P, _P, _I32, _I32, _P, _P,
                             _I32, _P, _P, _P, _P, _P, _P], _I32),
     "kap_budget_from_ratio": ([_I32, _I64, _I64, _I32, _I32], _I32),
+    "kap_kv_pool_layout": ([_I64, _I32, _I32, _I32, _I32, _P, _P], _I32),
     "kap_choose_plan": ([ctypes.c_double, ctypes.c_double, ctypes.c_double, ctypes.c_double, _I32,
                          _I32, _I32, _P, _P], _I32),
     "kap_compact_view": ([_P, _P, _I32, _I32, _I32, _P, _I32, _P, _I32, _P, _I32, _P, _P, _P, _P,
@@ -130,6 +131,37 @@ def proxy_workspace_bytes(B, d_model, n_out) -> int:
 
 def budget_from_ratio(n_pages, s_num, s_den, anchor, recent) -> int:
     return int(load().kap_budget_from_ratio(n_pages, s_num, s_den, anchor, recent))
+
+
+def kv_pool_layout(num_pages, Hkv, D, elem_bytes=2, page_size=16):
+    """kap_kv_pool_layout -> (v_offset_bytes, total_bytes): one allocation holding
+    a layer's K pool at byte 0 and its V pool at v_offset_bytes."""
+    v_off, total = ctypes.c_int64(-1), ctypes.c_int64(-1)
+    st = load().kap_kv_pool_layout(num_pages, Hkv, D, page_size, elem_bytes, ctypes.byref(v_off),
+                                   ctypes.byref(total))
+    _check(st, "kap_kv_pool_layout")
+    return int(v_off.value), int(total.value)
+
+
+def alloc_kv_pools(num_pages, Hkv, D, dtype=torch.bfloat16, device="cuda", zero=False):
+    """A layer's K pool [num_pages][Hkv][16][D] and V pool [num_pages][Hkv][D][16]
+    as views of one allocation placed by kap_kv_pool_layout."""
+    eb = torch.empty((), dtype=dtype).element_size()
+    v_off, total = kv_pool_layout(num_pages, Hkv, D, eb)
+    buf = (torch.zeros if zero else torch.empty)(total, dtype=torch.uint8, device=device)
+    n = num_pages * Hkv * 16 * D * eb
+    k = buf[:n].view(dtype).view(num_pages, Hkv, 16, D)
+    v = buf[v_off:v_off + n].view(dtype).view(num_pages, Hkv, D, 16)
+    return k, v
+
+
+def copy_kv_pools(k_pool, v_pool):
+    """Copies of a layer's K and V pools in one allocation (kap_kv_pool_layout)."""
+    num_pages, Hkv, ps, D = k_pool.shape
+    k, v = alloc_kv_pools(num_pages, Hkv, D, k_pool.dtype, k_pool.device)
+    k.copy_(k_pool)
+    v.copy_(v_pool)
+    return k, v
 
 
 PLAN_SELECTED, PLAN_FULL_CAPACITY, PLAN_FULL_MARGIN, PLAN_FULL_BOUNDARY = 0, 1, 2, 3

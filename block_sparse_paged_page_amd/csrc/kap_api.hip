@@ -230,6 +230,37 @@ int32_t kap_budget_from_ratio(int32_t n_pages, int64_t s_num, int64_t s_den, int
   return (int32_t)budget;
 }
 
+// One layer's K and V pools in one allocation: K at byte 0, V at the K
+// pool's bytes rounded up to 16 KiB plus 4 KiB.  A wave reads the K tile and
+// the V tile of one (page, KV head) together; with a V offset that is a
+// multiple of 16 KiB (two separate 2 MiB-aligned allocations always are),
+// the two tiles share address bits 12-13 on every page.  Measured on MI355X
+// at 128K, B = 4: the full-context verify took 328.7-334 us with such
+// offsets (342 us at multiples of 4 MiB) against 323-326.5 us with offsets
+// 4, 8 or 12 KiB past a multiple of 16 KiB; the full decode 317-322 us
+// (330 us) against 317-318 us.
+constexpr int64_t kKvPoolPeriod = 16384, kKvPoolShift = 4096;
+
+kap_status kap_kv_pool_layout(int64_t num_pages, int32_t num_kv_heads, int32_t head_dim,
+                              int32_t page_size, int32_t elem_bytes, int64_t* v_offset_bytes,
+                              int64_t* total_bytes) {
+  g_err[0] = 0;
+  if (!v_offset_bytes || !total_bytes) return fail(KAP_ERR_INVALID_ARG, "null output");
+  if (num_pages < 0 || num_kv_heads <= 0 || (elem_bytes != 2 && elem_bytes != 4))
+    return fail(KAP_ERR_INVALID_ARG, "num_pages=%lld num_kv_heads=%d elem_bytes=%d",
+                (long long)num_pages, num_kv_heads, elem_bytes);
+  if (head_dim != 64 && head_dim != 128) return fail(KAP_ERR_UNSUPPORTED, "head_dim %d", head_dim);
+  if (page_size != kPage) return fail(KAP_ERR_UNSUPPORTED, "page_size %d (16)", page_size);
+  const int64_t page_bytes = (int64_t)num_kv_heads * head_dim * page_size * elem_bytes;
+  if (num_pages > (INT64_MAX / 4) / page_bytes)
+    return fail(KAP_ERR_INVALID_ARG, "pool of %lld pages too large", (long long)num_pages);
+  const int64_t pool = num_pages * page_bytes;
+  const int64_t v_off = (pool + kKvPoolPeriod - 1) / kKvPoolPeriod * kKvPoolPeriod + kKvPoolShift;
+  *v_offset_bytes = v_off;
+  *total_bytes = v_off + pool;
+  return KAP_OK;
+}
+
 kap_status kap_choose_plan(double h, double s, double w_main_bytes, double kv_bytes, int32_t k,
                            int32_t budget_pages, int32_t capacity, int32_t* choice,
                            double* speedup) {

@@ -18,7 +18,7 @@ struct AttnWorkspace {
   int32_t* n_items;     // [1]
   int32_t* row_off;     // [B*Hkv + 1] first work item of each (b, g)
   float2* part_ml;      // [max_items][R] (reference max in log2 units, sum)
-  float* part_o;        // [max_items][R][D]
+  float* part_o;        // [max_items][R][D] fp32 (bf16, normalized, for the MFMA kernel)
   int32_t max_items;
   size_t bytes;
 };

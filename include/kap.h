@@ -211,6 +211,27 @@ KAP_API int32_t kap_budget_from_ratio(int32_t n_pages, int64_t s_num, int64_t s_
                               int32_t recent);
 
 /*
+ * Host helper: where to place one attention layer's K pool and V pool (the
+ * paged pools every block table indexes, [KAP] selected-KV view) in a single
+ * device allocation.  Any placement gives the same results; this one reads
+ * fastest.  The K pool starts at byte 0 and the V pool at
+ *   v_offset = (K pool bytes rounded up to 16 KiB) + 4 KiB,
+ * so that the K tile and the V tile of one (page, KV head), which one wave
+ * requests together, never share address bits 12-13.  V pools at a multiple
+ * of 16 KiB from their K pool (two separate 2 MiB-aligned allocations always
+ * are) made the full-context verify at 128K 1.5-5 % slower on MI355X.
+ *   num_pages, num_kv_heads, head_dim (64 or 128), page_size (16),
+ *   elem_bytes (2: bf16, 4: f32)  the pools' shape, as the attention calls take it
+ *   v_offset_bytes  host out: byte offset of the V pool from the allocation
+ *   total_bytes     host out: bytes to allocate (K pool, gap, V pool)
+ * Returns KAP_ERR_INVALID_ARG for null outputs, negative or oversized pools,
+ * KAP_ERR_UNSUPPORTED for other head_dim or page_size values.
+ */
+KAP_API kap_status kap_kv_pool_layout(int64_t num_pages, int32_t num_kv_heads, int32_t head_dim,
+                                      int32_t page_size, int32_t elem_bytes,
+                                      int64_t* v_offset_bytes, int64_t* total_bytes);
+
+/*
  * Compact view over a selection ([KAP] selected-KV view: a compact table of
  * the chosen pages' physical ids in ascending logical order, the logical pages
  * kept beside it, and a slot for each new token).  For row (b, gr):
@@ -254,7 +275,8 @@ KAP_API kap_status kap_select_compact(const float* scores, int32_t B, int32_t Hk
 
 /*
  * Workspace for kap_decode_attn (q_len = 1) and kap_verify_attn: the split-K
- * work plan's per-row offsets and the split partials (m, l, o in fp32).
+ * work plan's per-row offsets and the split partials (m and l in fp32; o in
+ * bf16, normalized, for bf16 pools and unnormalized fp32 for f32 pools).
  * Caller-owned device memory of at least this many bytes; its contents need
  * no initialization and are overwritten by every call (so concurrent calls
  * need separate workspaces).

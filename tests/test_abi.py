@@ -54,6 +54,23 @@ def test_budget_helper_agrees_with_oracle(lib):
                 assert kap.budget_from_ratio(N, num, den, a, r) == oracle.budget_from_ratio(N, num, den, a, r)
 
 
+def test_kv_pool_layout(lib):
+    # K at byte 0, V at the K pool's bytes rounded up to 16 KiB plus 4 KiB
+    for pages, hkv, d, eb in ((32772, 8, 128, 2), (1, 1, 64, 4), (0, 8, 128, 2), (4096, 8, 128, 2),
+                              (12345, 4, 64, 2)):
+        kb = pages * hkv * d * 16 * eb
+        v_off, total = kap.kv_pool_layout(pages, hkv, d, eb)
+        assert v_off % 16384 == 4096 and kb <= v_off < kb + 16384 + 4096
+        assert total == v_off + kb
+    assert kap.kv_pool_layout(32772, 8, 128, 2) == (1073876992, 2147749888)
+    out = ctypes.c_int64(0)
+    for args, st in (((-1, 8, 128, 16, 2), INVALID), ((10, 0, 128, 16, 2), INVALID),
+                     ((10, 8, 128, 16, 3), INVALID), ((10, 8, 96, 16, 2), UNSUPPORTED),
+                     ((10, 8, 128, 8, 2), UNSUPPORTED), ((1 << 60, 8, 128, 16, 2), INVALID)):
+        assert lib.kap_kv_pool_layout(*args, ctypes.byref(out), ctypes.byref(out)) == st, args
+    assert lib.kap_kv_pool_layout(10, 8, 128, 16, 2, None, ctypes.byref(out)) == INVALID
+
+
 def _score(lib, **kw):
     args = dict(q=NP, q_dtype=1, positions=NP, theta=1e4, summary=NP, sum_dtype=1, num_pages=10,
                 bt=NP, max_pages=4, seq_lens=NP, B=1, Hq=8, Hkv=2, D=128, page_size=16,

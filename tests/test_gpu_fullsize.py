@@ -21,11 +21,15 @@ def _u16(x: torch.Tensor) -> np.ndarray:
     return x.contiguous().view(torch.int16).cpu().numpy().view(np.uint16)
 
 
+def _pools(pages, Hkv, D, dtype, device):
+    return kap.alloc_kv_pools(pages, Hkv, D, dtype, device, zero=True)
+
+
 class Big:
     def __init__(self, w):
         self.w = w
         dev = torch.device("cuda:0")
-        self.b = b = W.make_device(w, dev)
+        self.b = b = W.make_device(w, dev, alloc_pools=_pools)  # placed as bench.py places them
         to = lambda a: torch.from_numpy(np.ascontiguousarray(a)).to(dev)  # noqa: E731
         self.bt, self.L, self.pos = to(b["bt"]), to(b["seq_lens"]), to(b["positions"])
         self.anchor, self.recent = to(b["anchor"]), to(b["recent"])

@@ -521,7 +521,8 @@ def test_full_selection_is_bit_identical_to_full_decode():
 
 
 def test_placement_invariance_and_determinism():
-    """Moving pages in the pool (table moved with them) and re-running change no bit."""
+    """Moving pages in the pool (table moved with them), placing the K and V pools
+    in one allocation (kap_kv_pool_layout) and re-running change no bit."""
     c = get_case("qwen")
     pool = c.K.shape[0]
     g = torch.Generator().manual_seed(7)
@@ -534,8 +535,14 @@ def test_placement_invariance_and_determinism():
     o3 = kap.verify_attn(c.qv, c.pos, c.K, c.V, c.bt, c.L)
     d1 = kap.decode_attn(c.q, c.pos, c.K, c.V, c.bt, c.L)
     d2 = kap.decode_attn(c.q, c.pos, K2, V2, bt2, c.L)
+    K3, V3 = kap.copy_kv_pools(c.K, c.V)
+    v_off, _ = kap.kv_pool_layout(pool, c.w.Hkv, c.w.D, 2)
+    assert V3.data_ptr() - K3.data_ptr() == v_off
+    o4 = kap.verify_attn(c.qv, c.pos, K3, V3, c.bt, c.L)
+    d3 = kap.decode_attn(c.q, c.pos, K3, V3, c.bt, c.L)
     torch.cuda.synchronize()
     assert torch.equal(o1, o2) and torch.equal(o1, o3) and torch.equal(d1, d2)
+    assert torch.equal(o1, o4) and torch.equal(d1, d3)
 
 
 # ----------------------------------------------------------------------------- edge cases

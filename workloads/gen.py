@@ -277,7 +277,8 @@ def dense_pool(batch: dict):
     return K, V
 
 
-def make_device(w: Workload, device, needle_dir: Optional[np.ndarray] = None) -> dict:
+def make_device(w: Workload, device, needle_dir: Optional[np.ndarray] = None,
+                alloc_pools=None) -> dict:
     """Same recipe as make(), with the K/V pages drawn on the GPU.
 
     Queries, needle pages, placement and budgets come from the same numpy
@@ -286,6 +287,9 @@ def make_device(w: Workload, device, needle_dir: Optional[np.ndarray] = None) ->
     rounded to bf16 by torch (round-to-nearest-even).  Returns the make()
     dictionary without K_pages/V_pages, plus device tensors K, V (full pool,
     unallocated pages zero), and torch copies of the small arrays.
+    alloc_pools(pages, Hkv, D, dtype, device), if given, returns the zeroed
+    K and V pool tensors (a placement of the caller's choosing); by default
+    they are two separate allocations.
     """
     import torch
 
@@ -296,8 +300,12 @@ def make_device(w: Workload, device, needle_dir: Optional[np.ndarray] = None) ->
     NA = w.alloc_pages
     tdt = torch.bfloat16 if w.dtype == "bf16" else torch.float32
     pool = b["pool_pages"]
-    K = torch.zeros((pool, Hkv, ps, D), dtype=tdt, device=device)
-    V = torch.zeros((pool, Hkv, D, ps), dtype=tdt, device=device)
+    if alloc_pools is None:
+        K = torch.zeros((pool, Hkv, ps, D), dtype=tdt, device=device)
+        V = torch.zeros((pool, Hkv, D, ps), dtype=tdt, device=device)
+    else:
+        K, V = alloc_pools(pool, Hkv, D, tdt, device)
+        assert K.shape == (pool, Hkv, ps, D) and V.shape == (pool, Hkv, D, ps)
     alpha = w.needle_scale * w.sigma * math.sqrt(D)
     starts = np.concatenate([[0], np.cumsum(NA)[:-1]]).astype(np.int64)
     for bi in range(B):
