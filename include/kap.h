@@ -45,6 +45,8 @@
  *                                         values of one dim are contiguous)
  *     Summary pool [num_pages][Hkv][D].  Block table [B][max_pages] int32
  *     maps logical page p of request b to its physical page (-1: none).
+ *     The K and V pools may sit anywhere; kap_kv_pool_layout gives the
+ *     placement in one allocation that reads fastest.
  *   - Results are bit-identical from run to run and do not depend on where
  *     pages sit in the pool.
  */
