@@ -366,7 +366,8 @@ def run_early_route(args, dev):
     """Early routing over 32 layers (40K inputs, per-head top-8 pages): the side
     flow (proxy GEMV -> per-head scores -> top-8 -> compact) for layer l+1 runs on
     a second stream while the main flow decodes layer l; compared with the same
-    work serialized on one stream."""
+    work serialized on one stream.  The GEMV reads each layer's W_q in the
+    packed layout (packed once, outside the timed sequences)."""
     w = W.spec("early_route_40k", B=args.batch if args.batch != 4 else 8)
     B, Hq, Hkv, D = w.B, w.Hq, w.Hkv, w.D
     layers = 32
@@ -384,6 +385,8 @@ def run_early_route(args, dev):
           for _ in range(layers)]
     hid = [torch.randn((B, w.hidden_dim), generator=g, device=dev).bfloat16() for _ in range(layers)]
     qreal = [torch.randn((B, Hq, D), generator=g, device=dev).bfloat16() for _ in range(layers)]
+    # the projection weights are static: packed once for the one-launch GEMV
+    Wp = [kap.proxy_pack_weights(x) for x in Wq]
     torch.cuda.synchronize()
     cap = 8
     views = [(torch.empty((B, Hkv, cap), dtype=torch.int32, device=dev),
@@ -399,7 +402,7 @@ def run_early_route(args, dev):
 
     def route(l, s):
         src = hid[l - 1] if l > 0 else hid[0]
-        kap.proxy_query(src, Wq[l], q_out=qp, workspace=pws, stream=s)
+        kap.proxy_query_packed(src, Wp[l], Hq * D, q_out=qp, stream=s)
         kap.score_blocks(qp.view(B, Hq, D), pos, Ss[l], bt, L, Hkv, scores=scores, stream=s)
         kap.select_compact(scores, L, anchor, recent, kmid, cap, cap, bt, pos, 1, per_head=True,
                            cnt=cnt, out=views[l], stream=s)
@@ -462,7 +465,9 @@ def run_early_route(args, dev):
         return wall(lambda: [fn(l) for l in range(layers)], reps) / layers
 
     parts = {
-        "proxy_gemv": per_call(lambda l: kap.proxy_query(hid[l], Wq[l], q_out=qp, workspace=pws)),
+        "proxy_gemv": per_call(lambda l: kap.proxy_query_packed(hid[l], Wp[l], Hq * D, q_out=qp)),
+        "proxy_gemv_row_major": per_call(lambda l: kap.proxy_query(hid[l], Wq[l], q_out=qp,
+                                                                   workspace=pws)),
         "score": per_call(lambda l: kap.score_blocks(qp.view(B, Hq, D), pos, Ss[l], bt, L, Hkv,
                                                      scores=scores)),
         "select_compact": per_call(lambda l: kap.select_compact(
@@ -490,6 +495,9 @@ def run_early_route(args, dev):
         "per_layer_us": {"route_side_flow": round(t_route, 2), "decode_main_flow": round(t_dec, 2),
                          **{k: round(v, 2) for k, v in parts.items()}},
         "proxy_gemv_GBps": round(w_bytes / (parts["proxy_gemv"] * 1e-6) / 1e9, 1),
+        "proxy_gemv_note": "the side flow's GEMV is kap_proxy_query_packed (one launch over W_q "
+                           "packed once at load time); proxy_gemv_row_major times kap_proxy_query "
+                           "(row-major W_q, split sums added by a second launch) on the same inputs",
         "score_GBps": round(score_bytes / (parts["score"] * 1e-6) / 1e9, 1),
         "same_bytes_stream_read": {
             "w_q_us": round(t_rd_w, 2), "w_q_GBps": round(w_bytes / (t_rd_w * 1e-6) / 1e9, 1),

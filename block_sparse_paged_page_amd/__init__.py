@@ -15,7 +15,7 @@ from ._lib import (  # noqa: F401
     KapLibraryMissing, alloc_kv_pools, append_kv, attn_workspace_bytes, budget_from_ratio,
     choose_plan, build_summary, compact_view, copy_kv_pools, decode_attn, decode_attn_noalloc,
     diag_stream_read, host_proxy_query, host_score_blocks, host_select_topk, kv_pool_layout,
-    lib_path, load, materialize_view, proxy_query,
+    lib_path, load, materialize_view, proxy_pack_weights, proxy_query, proxy_query_packed,
     proxy_workspace_bytes, score_blocks, score_pool_blocks, select_compact, select_topk,
     update_summary, verify_attn, version,
 )

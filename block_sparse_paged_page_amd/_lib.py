@@ -36,6 +36,8 @@ _SIGS = {
                                _I32, _I32, _P, _P, _P], _I32),
     "kap_proxy_workspace_bytes": ([_I32, _I32, _I32], _SZ),
     "kap_proxy_query": ([_P, _P, _I32, _I32, _I32, _P, _P, _SZ, _P], _I32),
+    "kap_proxy_pack_weights": ([_P, _I32, _I32, _P, _P], _I32),
+    "kap_proxy_query_packed": ([_P, _P, _I32, _I32, _I32, _P, _P], _I32),
     "kap_select_topk": ([_P, _I32, _I32, _I32, _P, _I32, _I32, _P, _P, _P, _I32, _I32, _P, _P, _P],
                         _I32),
     "kap_select_compact": ([_P, _I32, _I32, _I32, _P, _I32, _I32, _P, _P, _P, _I32, _I32, _P, _P,
@@ -226,6 +228,35 @@ def proxy_query(hidden, w_q, q_out=None, workspace=None, stream=None):
     st = lib.kap_proxy_query(_p(hidden), _p(w_q), B, dm, n_out, _p(q_out), _p(workspace),
                              workspace.numel(), _stream(stream))
     _check(st, "kap_proxy_query")
+    return q_out
+
+
+def proxy_pack_weights(w_q, out=None, stream=None):
+    """kap_proxy_pack_weights: the packed copy of a row-major bf16 w_q [d_model][n_out]
+    (same element count, returned flat) for proxy_query_packed."""
+    lib = load()
+    dm, n_out = w_q.shape
+    if out is None:
+        out = torch.empty(dm * n_out, dtype=w_q.dtype, device=w_q.device)
+    if out.numel() != dm * n_out or out.element_size() != 2:
+        raise ValueError("packed output must hold d_model * n_out 16-bit values")
+    st = lib.kap_proxy_pack_weights(_p(w_q), dm, n_out, _p(out), _stream(stream))
+    _check(st, "kap_proxy_pack_weights")
+    return out
+
+
+def proxy_query_packed(hidden, w_packed, n_out, q_out=None, stream=None):
+    """kap_proxy_query_packed: hidden [B][d_model] bf16 @ W_q (packed by
+    proxy_pack_weights) -> fp32 [B][n_out], one launch."""
+    lib = load()
+    B, dm = hidden.shape
+    if w_packed.numel() != dm * n_out:
+        raise ValueError("packed weight size does not match d_model * n_out")
+    if q_out is None:
+        q_out = torch.empty((B, n_out), dtype=torch.float32, device=hidden.device)
+    st = lib.kap_proxy_query_packed(_p(hidden), _p(w_packed), B, dm, n_out, _p(q_out),
+                                    _stream(stream))
+    _check(st, "kap_proxy_query_packed")
     return q_out
 
 

@@ -198,6 +198,37 @@ kap_status kap_proxy_query(const void* hidden, const void* w_q, int32_t B, int32
                       (float*)workspace, proxy_splits(d_model), (hipStream_t)stream);
 }
 
+static kap_status check_packed_shape(int32_t d_model, int32_t n_out) {
+  if (d_model <= 0 || d_model % 32 != 0)
+    return fail(KAP_ERR_UNSUPPORTED, "d_model %d (multiple of 32)", d_model);
+  if (n_out <= 0 || n_out % 16 != 0)
+    return fail(KAP_ERR_UNSUPPORTED, "n_out %d (multiple of 16)", n_out);
+  return KAP_OK;
+}
+
+kap_status kap_proxy_pack_weights(const void* w_q, int32_t d_model, int32_t n_out, void* w_packed,
+                                  kap_stream stream) {
+  g_err[0] = 0;
+  kap_status st = check_packed_shape(d_model, n_out);
+  if (st != KAP_OK) return st;
+  if (!w_q || !w_packed) return fail(KAP_ERR_INVALID_ARG, "null pointer");
+  if (w_q == w_packed) return fail(KAP_ERR_INVALID_ARG, "packing needs a separate output buffer");
+  return launch_proxy_pack((const uint16_t*)w_q, (uint16_t*)w_packed, d_model, n_out,
+                           (hipStream_t)stream);
+}
+
+kap_status kap_proxy_query_packed(const void* hidden, const void* w_packed, int32_t B,
+                                  int32_t d_model, int32_t n_out, float* q_out,
+                                  kap_stream stream) {
+  g_err[0] = 0;
+  if (B <= 0 || B > 16) return fail(KAP_ERR_UNSUPPORTED, "proxy batch %d (1..16)", B);
+  kap_status st = check_packed_shape(d_model, n_out);
+  if (st != KAP_OK) return st;
+  if (!hidden || !w_packed || !q_out) return fail(KAP_ERR_INVALID_ARG, "null pointer");
+  return launch_proxy_packed((const uint16_t*)hidden, (const uint16_t*)w_packed, B, d_model, n_out,
+                             q_out, (hipStream_t)stream);
+}
+
 kap_status kap_select_topk(const float* scores, int32_t B, int32_t Hkv, int32_t max_pages,
                            const int32_t* seq_lens, int32_t page_size, int32_t per_head,
                            const int32_t* anchor, const int32_t* recent, const int32_t* k_mid,

@@ -81,6 +81,10 @@ kap_status launch_append(const void* k_new, const void* v_new, kap_dtype dt, con
                          int32_t B, int32_t q_new, int32_t Hkv, int32_t D, int64_t num_slots,
                          void* k, void* v, hipStream_t stream);
 int proxy_splits(int d_model);
+kap_status launch_proxy_pack(const uint16_t* wq, uint16_t* wp, int32_t dm, int32_t n_out,
+                             hipStream_t stream);
+kap_status launch_proxy_packed(const uint16_t* hidden, const uint16_t* wp, int32_t B, int32_t dm,
+                               int32_t n_out, float* q_out, hipStream_t stream);
 kap_status launch_diag_read(const void* buf, size_t bytes, uint32_t* sink, hipStream_t stream);
 kap_status launch_proxy(const uint16_t* hidden, const uint16_t* wq, int32_t B, int32_t dm,
                         int32_t n_out, float* q_out, float* partial, int32_t splits,

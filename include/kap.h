@@ -146,6 +146,32 @@ KAP_API kap_status kap_proxy_query(const void* hidden, const void* w_q, int32_t 
                            kap_stream stream);
 
 /*
+ * The same proxy query in one launch, over a query projection packed once
+ * for it ([ESKV] Interpretation: the side flow's projection of the preceding
+ * hidden state; W_q is a static weight, so its layout is ours to choose).
+ * kap_proxy_pack_weights writes the packed copy (same size, 2 * d_model *
+ * n_out bytes) of a row-major W_q: element (r, c) goes to
+ *   w_packed[((((c / 16) * (d_model / 32) + r / 32) * 4 + (r % 32) / 8) * 16 + c % 16) * 8 + r % 8]
+ * (each 16-column tile's whole d_model contiguous; 8 consecutive rows of one
+ * column per 16 bytes).  kap_proxy_query_packed then computes
+ *   q_out[b][n] = sum_c hidden[b][c] * w_q[c][n]
+ * with bf16 inputs and fp32 accumulation on the matrix cores: each of eight
+ * row shares of a 16-column tile is summed in row order, and the shares are
+ * added in order (deterministic; it agrees with kap_proxy_query to fp32
+ * rounding, not bit for bit).  No workspace.
+ *   w_q      device [d_model][n_out] bf16 (row-major); w_packed device out, a
+ *            separate buffer of the same size
+ *   hidden   device [B][d_model] bf16; q_out device out [B][n_out] float (as
+ *            kap_proxy_query writes it)
+ * 1 <= B <= 16; d_model a multiple of 32; n_out a multiple of 16.
+ */
+KAP_API kap_status kap_proxy_pack_weights(const void* w_q, int32_t d_model, int32_t n_out,
+                                          void* w_packed, kap_stream stream);
+KAP_API kap_status kap_proxy_query_packed(const void* hidden, const void* w_packed, int32_t B,
+                                          int32_t d_model, int32_t n_out, float* q_out,
+                                          kap_stream stream);
+
+/*
  * Top-K pages under the A<a>R<r>K<k> split ([KRI] A<a>R<r>K<k> tag section):
  * anchors = the first a logical pages, recents = the last r, plus the best
  * k_mid pages of the middle [a, N - r) by score (N = ceil(seq_lens[b]/16)).

@@ -218,6 +218,16 @@ def test_proxy_validation(lib):
     assert f(NP, NP, 1, 1000, 4096, NP, NP, 1 << 30, None) == UNSUPPORTED
     assert f(NP, NP, 1, 4096, 4000, NP, NP, 1 << 30, None) == UNSUPPORTED
     assert f(NP, NP, 1, 4096, 4096, NP, NP, 16, None) == WORKSPACE
+    pk, pq = lib.kap_proxy_pack_weights, lib.kap_proxy_query_packed
+    assert pk(NP, 4016, 4096, ctypes.c_void_p(0x2000), None) == UNSUPPORTED   # d_model % 32
+    assert pk(NP, 4096, 4088, ctypes.c_void_p(0x2000), None) == UNSUPPORTED   # n_out % 16
+    assert pk(None, 4096, 4096, NP, None) == INVALID
+    assert pk(NP, 4096, 4096, NP, None) == INVALID                            # in place
+    assert pq(NP, NP, 0, 4096, 4096, NP, None) == UNSUPPORTED
+    assert pq(NP, NP, 17, 4096, 4096, NP, None) == UNSUPPORTED
+    assert pq(NP, NP, 1, 48, 4096, NP, None) == UNSUPPORTED
+    assert pq(NP, NP, 1, 4096, 40, NP, None) == UNSUPPORTED
+    assert pq(NP, None, 1, 4096, 4096, NP, None) == INVALID
 
 
 def test_append_and_summary_update_validation(lib):
