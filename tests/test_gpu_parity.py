@@ -596,6 +596,49 @@ def test_select_radix_exits():
         np.testing.assert_array_equal(cnt.cpu().numpy(), cref)
 
 
+@pytest.mark.parametrize("P", [3000, 12000])
+def test_select_small_takes(P):
+    """Small middle counts (per-head early routing takes 8): takes 0..17 on
+    adversarial keys (ties, +-0, +-inf, NaN), normal draws and a threshold
+    inside a run of equal keys, one take per request, with tables staged in
+    LDS (3000 pages) and read directly (12000 pages).  Bit-exact against the
+    oracle, per head and pooled, and through the fused top-K with compact
+    view."""
+    rng = np.random.default_rng(31 + P)
+    palette = np.array([0.0, -0.0, 1.0, -1.0, 2.5, np.inf, -np.inf, np.nan, 1.0, 0.5], np.float32)
+    takes = np.array([1, 2, 3, 7, 8, 15, 16, 17, 8, 5, 16, 0], np.int32)
+    B, H = len(takes), 4
+    S = np.empty((B, H, P), np.float32)
+    for i in range(B):
+        fam = i % 3
+        if fam == 0:
+            S[i] = palette[rng.integers(0, len(palette), size=(H, P))]
+        elif fam == 1:
+            S[i] = rng.standard_normal((H, P)).astype(np.float32)
+        else:
+            S[i] = np.where(rng.random((H, P)) < 0.3, np.float32(1.5),
+                            rng.standard_normal((H, P)).astype(np.float32) - 3.0)
+    L = np.full(B, 16 * P, np.int32)
+    L[3] = 16 * (P - 7) + 5                    # a short row with a partial last page
+    a = np.array([1, 0, 2, 1, 0, 4, 1, 1, 0, 3, 1, 2], np.int32)
+    r = np.array([2, 0, 3, 2, 1, 4, 2, 2, 0, 3, 2, 2], np.int32)
+    cap = 64
+    for per_head in (True, False):
+        sel, cnt = kap.select_topk(t(S), t(L), t(a), t(r), t(takes), cap, cap, per_head=per_head)
+        torch.cuda.synchronize()
+        sref, cref = oracle.select(S, L, a, r, takes, cap, per_head=per_head)
+        np.testing.assert_array_equal(sel.cpu().numpy(), sref)
+        np.testing.assert_array_equal(cnt.cpu().numpy(), cref)
+    bt = np.stack([rng.permutation(4 * P)[:P] for _ in range(B)]).astype(np.int32)
+    pos = L.copy()
+    cnt2, cv = kap.select_compact(t(S), t(L), t(a), t(r), t(takes), cap, cap, t(bt), t(pos), 1,
+                                  per_head=True)
+    torch.cuda.synchronize()
+    sref, cref = oracle.select(S, L, a, r, takes, cap, per_head=True)
+    np.testing.assert_array_equal(cv[1].cpu().numpy(), sref)
+    np.testing.assert_array_equal(cnt2.cpu().numpy(), cref)
+
+
 def test_select_compact_matches_the_two_calls():
     """kap_select_compact writes exactly what kap_select_topk then kap_compact_view
     write, and what the oracle's selection then compaction give, on adversarial
