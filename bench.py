@@ -54,7 +54,7 @@ def parse():
     ap.add_argument("--layers", type=int, default=0, help="layer copies (0: auto)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-extras", action="store_true",
-                    help="skip the Llama-shaped 32K, mixed-serving and retention-fit legs of the default line")
+                    help="skip the Llama-shaped 32K, mixed-serving, early-routing and retention-fit legs of the default line")
     ap.add_argument("--graph", action="store_true",
                     help="replay each call of the cycle from its own HIP graph (default: launch "
                          "from Python; on this stack a graph launch adds ~7 us per call)")
@@ -363,6 +363,10 @@ def _sweep(args, dev, w, label):
 
 
 def run_early_route(args, dev):
+    print(json.dumps(_early_route(args, dev)), flush=True)
+
+
+def _early_route(args, dev):
     """Early routing over 32 layers (40K inputs, per-head top-8 pages): the side
     flow (proxy GEMV -> per-head scores -> top-8 -> compact) for layer l+1 runs on
     a second stream while the main flow decodes layer l; compared with the same
@@ -486,7 +490,7 @@ def run_early_route(args, dev):
     score_bytes = n_pages * (Hkv * D * 2 + 4) + B * Hkv * bt.shape[1] * 4 + B * Hq * D * 4
     s_bytes = Ss[0].numel() * Ss[0].element_size()
     hidden = (t_ser - t_ovl) / (layers * min(t_route, t_dec))
-    print(json.dumps({
+    return {
         "metric": METRIC, "workload": f"early_route_40k: B={B}, Hq=32, Hkv=8, D=128, 40000-token "
         "inputs, per-head top-8 pages (128 tokens), proxy query 4096x4096 bf16 W_q, 32 layers",
         "unit": "tokens/s", "value": round(B / (t_ovl * 1e-6), 1), "dtype": "bf16",
@@ -509,7 +513,7 @@ def run_early_route(args, dev):
                   "times from 32 calls (one per layer) replayed from a HIP graph",
         "overlap_efficiency": round(hidden, 3),
         "note": "efficiency = time saved / (layers x shorter flow per layer)",
-    }), flush=True)
+    }
 
 
 def run_early_route_cpu(args, dev):
@@ -1194,6 +1198,12 @@ def main():
             "request_imbalance_max_over_mean", "ragged_over_full_GBps")}
         torch.cuda.empty_cache()
         log("mixed_serving leg done", q)
+        r = _early_route(args, dev)
+        extras["early_route_40k"] = {k: r[k] for k in (
+            "workload", "wall_us_32_layers", "per_layer_us", "proxy_gemv_GBps", "score_GBps",
+            "overlap_efficiency", "timing")}
+        torch.cuda.empty_cache()
+        log("early_route_40k leg done", q)
         result["extras"] = extras
     if not args.no_cpu_baseline:
         result["cpu_baseline"] = cpu_baseline(w, b, b["K"], b["V"], cap, q)
