@@ -158,3 +158,70 @@ def test_commit_cycle_replays_from_a_graph():
         assert torch.equal(gx["cv"][3], ex["cv"][3])
         run(ex)                            # eager work between replays
         torch.cuda.synchronize()
+
+
+def test_early_route_side_flow_replays_from_a_graph():
+    """The early-routing side flow as the 32-layer line replays it: proxy query
+    over the packed W_q, per-head scores, per-head top-8 with the compact view,
+    and the decode over those views.  Each replay gets a new hidden state in the
+    captured buffer and must equal the eager flow bit for bit."""
+    w = W.spec("early_route_40k", B=2, seq_lens=[9000, 6123])
+    c = Case(w)
+    dev = c.q.device
+    Hq, Hkv, D, cap = w.Hq, w.Hkv, w.D, 8
+    wq = t(c.b["wq"])
+    wp = kap.proxy_pack_weights(wq)
+    n_out = Hq * D
+
+    def buffers():
+        return dict(hid=t(c.b["hidden"]).clone(),
+                    qp=torch.empty((w.B, n_out), dtype=torch.float32, device=dev),
+                    scores=torch.empty((w.B, Hkv, c.max_pages), dtype=torch.float32, device=dev),
+                    cnt=torch.empty((w.B, Hkv), dtype=torch.int32, device=dev),
+                    cv=(torch.empty((w.B, Hkv, cap), dtype=torch.int32, device=dev),
+                        torch.empty((w.B, Hkv, cap), dtype=torch.int32, device=dev),
+                        torch.empty((w.B, Hkv), dtype=torch.int32, device=dev),
+                        torch.empty((w.B, 1), dtype=torch.int64, device=dev)),
+                    ws=torch.empty(kap.attn_workspace_bytes(w.B, 1, Hq, Hkv, D), dtype=torch.uint8,
+                                   device=dev),
+                    out=torch.empty_like(c.q))
+
+    def run(x):
+        kap.proxy_query_packed(x["hid"], wp, n_out, q_out=x["qp"])
+        kap.score_blocks(x["qp"].view(w.B, Hq, D), c.pos, c.S, c.bt, c.L, Hkv, scores=x["scores"])
+        kap.select_compact(x["scores"], c.L, c.anchor, c.recent, c.k_mid, cap, cap, c.bt, c.pos, 1,
+                           per_head=True, cnt=x["cnt"], out=x["cv"])
+        kap.decode_attn(c.q, c.pos, c.K, c.V, x["cv"][0], x["cv"][2], G=Hkv, out=x["out"],
+                        workspace=x["ws"], logical=x["cv"][1])
+
+    gx, ex = buffers(), buffers()
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        run(gx)
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        run(gx)
+    torch.cuda.synchronize()
+    rng = np.random.default_rng(77)
+    first = None
+    for rep in range(4):
+        hid = t(oracle.round_to_bf16(rng.standard_normal(c.b["hidden"].shape))) if rep % 3 else t(c.b["hidden"])
+        gx["hid"].copy_(hid)
+        g.replay()
+        torch.cuda.synchronize()
+        ex["hid"].copy_(hid)
+        run(ex)                            # eager library work between replays
+        torch.cuda.synchronize()
+        for key in ("qp", "scores", "cnt", "out"):
+            assert torch.equal(gx[key], ex[key]), f"replay {rep}, {key}"
+        for i in range(3):
+            assert torch.equal(gx["cv"][i], ex["cv"][i]), f"replay {rep}, view {i}"
+        if rep == 0:
+            first = gx["qp"].clone()
+        elif rep % 3:
+            assert not torch.equal(gx["qp"], first)  # the replay followed the new hidden state
+        else:
+            assert torch.equal(gx["qp"], first)
