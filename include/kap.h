@@ -13,7 +13,8 @@
  * and around it: kap_append_kv writes the window's K/V through the slot
  * mapping (so the verify can attend causally to it), kap_update_summary /
  * kap_build_summary keep the block-mean K summaries current, kap_proxy_query
- * forms an early-routing query.
+ * (or kap_proxy_query_packed over a weight packed once) forms an early-routing
+ * query, and kap_kv_pool_layout says where to place a layer's K and V pools.
  *
  * Sources (web pages the method is described on):
  *   [KAP]  "KAP: Bridging the Knowledge Selection-Runtime Consumption Gap in
