@@ -5,6 +5,7 @@
 #include <string.h>
 
 #include <atomic>
+#include <initializer_list>
 
 #include "kap_internal.h"
 
@@ -131,6 +132,15 @@ const char* kap_last_error(void) { return g_err; }
 
 const char* kap_version(void) { return "kap 0.1 gfx950"; }
 
+// The kernels move bulk data (queries, K/V pages, summaries, weights,
+// outputs, workspaces) in 16-byte vectors, some straight into LDS: those
+// pointers must be 16-byte aligned (hipMalloc and torch allocations are).
+static bool misaligned(std::initializer_list<const void*> ptrs) {
+  for (const void* p : ptrs)
+    if (((uintptr_t)p & 15) != 0) return true;
+  return false;
+}
+
 kap_status kap_score_blocks(const void* q, int32_t q_dtype, const int32_t* positions,
                             float rope_theta, const void* summary, int32_t sum_dtype,
                             int32_t num_pages, const int32_t* block_table, int32_t max_pages,
@@ -148,6 +158,7 @@ kap_status kap_score_blocks(const void* q, int32_t q_dtype, const int32_t* posit
   if (B == 0 || max_pages == 0) return KAP_OK;
   if (!q || !positions || !summary || !block_table || !seq_lens || !scores)
     return fail(KAP_ERR_INVALID_ARG, "null pointer");
+  if (misaligned({q, summary})) return fail(KAP_ERR_INVALID_ARG, "q or summary not 16-byte aligned");
   return launch_score(q, (kap_dtype)q_dtype, positions, rope_theta, summary,
                       (kap_dtype)sum_dtype, block_table, max_pages, seq_lens, B, Hq, Hkv, D,
                       scores, (hipStream_t)stream);
@@ -171,6 +182,7 @@ kap_status kap_score_pool_blocks(const void* q, int32_t q_dtype, const int32_t* 
   if (B == 0 || max_pages == 0) return KAP_OK;
   if (!q || !positions || !summary || !block_table || !seq_lens || (!pooled && !scores))
     return fail(KAP_ERR_INVALID_ARG, "null pointer");
+  if (misaligned({q, summary})) return fail(KAP_ERR_INVALID_ARG, "q or summary not 16-byte aligned");
   return launch_score_pool(q, (kap_dtype)q_dtype, positions, rope_theta, summary,
                            (kap_dtype)sum_dtype, block_table, max_pages, seq_lens, B, Hq, Hkv,
                            D, scores, pooled, (hipStream_t)stream);
@@ -191,6 +203,8 @@ kap_status kap_proxy_query(const void* hidden, const void* w_q, int32_t B, int32
   if (n_out <= 0 || n_out % 512 != 0)
     return fail(KAP_ERR_UNSUPPORTED, "n_out %d (multiple of 512)", n_out);
   if (!hidden || !w_q || !q_out) return fail(KAP_ERR_INVALID_ARG, "null pointer");
+  if (misaligned({hidden, w_q, q_out, workspace}))
+    return fail(KAP_ERR_INVALID_ARG, "hidden, w_q, q_out or workspace not 16-byte aligned");
   const size_t need = kap_proxy_workspace_bytes(B, d_model, n_out);
   if (!workspace || workspace_bytes < need)
     return fail(KAP_ERR_WORKSPACE, "proxy workspace %zu < %zu bytes", workspace_bytes, need);
@@ -212,6 +226,7 @@ kap_status kap_proxy_pack_weights(const void* w_q, int32_t d_model, int32_t n_ou
   kap_status st = check_packed_shape(d_model, n_out);
   if (st != KAP_OK) return st;
   if (!w_q || !w_packed) return fail(KAP_ERR_INVALID_ARG, "null pointer");
+  if (misaligned({w_packed})) return fail(KAP_ERR_INVALID_ARG, "w_packed not 16-byte aligned");
   if (w_q == w_packed) return fail(KAP_ERR_INVALID_ARG, "packing needs a separate output buffer");
   return launch_proxy_pack((const uint16_t*)w_q, (uint16_t*)w_packed, d_model, n_out,
                            (hipStream_t)stream);
@@ -225,6 +240,8 @@ kap_status kap_proxy_query_packed(const void* hidden, const void* w_packed, int3
   kap_status st = check_packed_shape(d_model, n_out);
   if (st != KAP_OK) return st;
   if (!hidden || !w_packed || !q_out) return fail(KAP_ERR_INVALID_ARG, "null pointer");
+  if (misaligned({hidden, w_packed}))
+    return fail(KAP_ERR_INVALID_ARG, "hidden or w_packed not 16-byte aligned");
   return launch_proxy_packed((const uint16_t*)hidden, (const uint16_t*)w_packed, B, d_model, n_out,
                              q_out, (hipStream_t)stream);
 }
@@ -400,6 +417,8 @@ static kap_status attn_common(const void* q, int32_t q_dtype, const int32_t* pos
   if (B == 0) return KAP_OK;
   if (!q || !positions || !k_pool || !v_pool || !table || !lens || !out)
     return fail(KAP_ERR_INVALID_ARG, "null pointer");
+  if (misaligned({q, k_pool, v_pool, out, workspace}))
+    return fail(KAP_ERR_INVALID_ARG, "q, a pool, out or workspace not 16-byte aligned");
   const size_t need = kap_attn_workspace_bytes(B, q_len, Hq, Hkv, D);
   if (!workspace || workspace_bytes < need)
     return fail(KAP_ERR_WORKSPACE, "attention workspace %zu < %zu bytes", workspace_bytes, need);
@@ -503,6 +522,8 @@ kap_status kap_build_summary(const void* k_pool, int32_t kv_dtype, int32_t num_p
   if (B == 0 || max_pages == 0) return KAP_OK;
   if (!k_pool || !block_table || !seq_lens || !summary)
     return fail(KAP_ERR_INVALID_ARG, "null pointer");
+  if (misaligned({k_pool, summary}))
+    return fail(KAP_ERR_INVALID_ARG, "k_pool or summary not 16-byte aligned");
   return launch_summary(k_pool, (kap_dtype)kv_dtype, Hkv, D, block_table, max_pages, seq_lens,
                         nullptr, 0, B, summary, (kap_dtype)sum_dtype, (hipStream_t)stream);
 }
@@ -522,6 +543,8 @@ kap_status kap_update_summary(const void* k_pool, int32_t kv_dtype, int32_t num_
   if (B == 0 || max_pages == 0 || q_new == 0) return KAP_OK;
   if (!k_pool || !block_table || !seq_lens || !positions || !summary)
     return fail(KAP_ERR_INVALID_ARG, "null pointer");
+  if (misaligned({k_pool, summary}))
+    return fail(KAP_ERR_INVALID_ARG, "k_pool or summary not 16-byte aligned");
   return launch_summary(k_pool, (kap_dtype)kv_dtype, Hkv, D, block_table, max_pages, seq_lens,
                         positions, q_new, B, summary, (kap_dtype)sum_dtype, (hipStream_t)stream);
 }
@@ -545,6 +568,8 @@ kap_status kap_materialize_view(const void* k_pool, const void* v_pool, int32_t 
   if (capacity > 65535 || B > 65535) return fail(KAP_ERR_UNSUPPORTED, "grid too large");
   if (!k_pool || !v_pool || !compact_bt || !k_ws || !v_ws || !ws_table)
     return fail(KAP_ERR_INVALID_ARG, "null pointer");
+  if (misaligned({k_pool, v_pool, k_ws, v_ws}))
+    return fail(KAP_ERR_INVALID_ARG, "a pool or workspace not 16-byte aligned");
   return launch_materialize(k_pool, v_pool, (kap_dtype)kv_dtype, Hkv, D, compact_bt, B, G,
                             capacity, k_ws, v_ws, ws_table, (hipStream_t)stream);
 }
@@ -563,6 +588,8 @@ kap_status kap_append_kv(const void* k_new, const void* v_new, int32_t kv_dtype,
   if (B == 0 || q_new == 0) return KAP_OK;
   if (!k_new || !v_new || !slot_mapping || !k_pool || !v_pool)
     return fail(KAP_ERR_INVALID_ARG, "null pointer");
+  if (misaligned({k_new, v_new, k_pool, v_pool}))
+    return fail(KAP_ERR_INVALID_ARG, "new rows or a pool not 16-byte aligned");
   return launch_append(k_new, v_new, (kap_dtype)kv_dtype, slot_mapping, B, q_new, Hkv, D,
                        (int64_t)num_pages * kPage, k_pool, v_pool, (hipStream_t)stream);
 }
@@ -570,6 +597,7 @@ kap_status kap_append_kv(const void* k_new, const void* v_new, int32_t kv_dtype,
 kap_status kap_diag_stream_read(const void* buf, size_t bytes, uint32_t* sink, kap_stream stream) {
   g_err[0] = 0;
   if (!buf || !sink) return fail(KAP_ERR_INVALID_ARG, "null pointer");
+  if (misaligned({buf})) return fail(KAP_ERR_INVALID_ARG, "buffer not 16-byte aligned");
   if (bytes % 16 != 0) return fail(KAP_ERR_INVALID_ARG, "bytes %zu not a multiple of 16", bytes);
   return launch_diag_read(buf, bytes, sink, (hipStream_t)stream);
 }

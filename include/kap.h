@@ -35,7 +35,10 @@
  *     that proposal and verify replay as graphs).
  *   - All shape, dtype and size checks run on the host before any launch and
  *     return a status; kap_last_error() then holds a message for the calling
- *     thread.  Device-side data are trusted: page ids outside [0, num_pages)
+ *     thread.  Bulk-data pointers (queries, hidden states, weights, K/V pools,
+ *     summaries, attention outputs, workspaces) must be 16-byte aligned, as
+ *     hipMalloc and torch allocations are: the kernels move them in 16-byte
+ *     vectors.  A call with one that is not returns KAP_ERR_INVALID_ARG.  Device-side data are trusted: page ids outside [0, num_pages)
  *     or lengths beyond a table's width are undefined behaviour.
  *   - Element types: KAP_F32 (float) and KAP_BF16 (bfloat16 stored as 16-bit).
  *   - Page size is 16 tokens; head_dim is 64 or 128; Hq is a multiple of Hkv,

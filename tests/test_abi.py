@@ -199,6 +199,21 @@ def test_attention_validation(lib):
         assert _attn(lib, fn, B=513, Hkv=8, Hq=64) == UNSUPPORTED
         assert _attn(lib, fn, B=4097, Hkv=1, Hq=8) == UNSUPPORTED
     assert _attn(lib, "decode", G=3) == INVALID
+    odd = ctypes.c_void_p(0x1008)                              # 8-byte but not 16-byte aligned
+    for fn in ("decode", "verify"):
+        for arg in ("q", "k", "v", "out", "ws"):
+            assert _attn(lib, fn, **{arg: odd}) == INVALID, (fn, arg)
+
+
+def test_bulk_pointers_must_be_16_byte_aligned(lib):
+    odd = ctypes.c_void_p(0x1008)
+    assert _score(lib, q=odd) == INVALID
+    assert _score(lib, summary=odd) == INVALID
+    assert lib.kap_proxy_query(odd, NP, 1, 4096, 4096, NP, NP, 1 << 30, None) == INVALID
+    assert lib.kap_proxy_query(NP, NP, 1, 4096, 4096, NP, odd, 1 << 30, None) == INVALID
+    assert lib.kap_proxy_pack_weights(NP, 4096, 4096, odd, None) == INVALID
+    assert lib.kap_proxy_query_packed(NP, odd, 1, 4096, 4096, NP, None) == INVALID
+    assert lib.kap_diag_stream_read(odd, 1 << 20, NP, None) == INVALID
 
 
 def test_workspace_sizes_are_monotone(lib):
